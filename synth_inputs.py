@@ -160,6 +160,11 @@ def make_cache(cfg: LayerCfg, which: str, seed: int = 0) -> np.ndarray:
     return out
 
 
+def normal(seed: int, stream: int, shape, dtype: str, std: float = 1.0, mean: float = 0.0) -> np.ndarray:
+    """A seeded N(mean, std) tensor for kernel-level cases (stream ids >= 100 by convention)."""
+    return _draw(seed, stream, tuple(shape), std, mean, dtype)
+
+
 def scaled(cfg: LayerCfg, **kw) -> LayerCfg:
     """A copy of a config with some fields replaced (smaller parity cases of the same family)."""
     return dataclasses.replace(cfg, **kw)

@@ -1,0 +1,171 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the header declares,
+and rejects bad arguments with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import transformer_layer_forward_amd as L
+from transformer_layer_forward_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llama_layer.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "return")))
+
+
+def test_header_declares_the_six_layer_entry_points():
+    names = _declared_functions()
+    for n in ("llama_layer_forward", "rmsnorm", "rope_apply", "gqa_attn_prefill", "gqa_attn_decode", "swiglu_mlp"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    assert set(_lib.EXPORTED) == set(_declared_functions())
+
+
+def test_struct_layouts_match_header():
+    # ll_rope: 2 x int32 + 4 x double + int64; ll_layer_cfg: 5 x int64 + double + ll_rope + 2 x int32
+    assert ctypes.sizeof(_lib.LLRope) == 48
+    assert ctypes.sizeof(_lib.LLLayerCfg) == 104
+    assert ctypes.sizeof(_lib.LLLayerWeights) == 48
+
+
+def _cfg(**kw):
+    base = dict(hidden=64, n_heads=4, n_kv_heads=2, head_dim=16, intermediate=176, dtype=torch.float32)
+    base.update(kw)
+    return L.LayerConfig(**base).to_c()
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_heads", 5, _lib.LL_EINVAL),          # not a multiple of n_kv_heads
+    ("head_dim", 15, _lib.LL_EINVAL),        # odd
+    ("head_dim", 258, _lib.LL_EUNSUPPORTED),
+    ("hidden", 0, _lib.LL_EINVAL),
+    ("intermediate", -3, _lib.LL_EINVAL),
+    ("eps", -1.0, _lib.LL_EINVAL),
+    ("dtype", 7, _lib.LL_EINVAL),
+    ("reserved", 1, _lib.LL_EINVAL),
+])
+def test_layer_config_validation(field, value, status):
+    lib = L.load()
+    c = _cfg()
+    setattr(c, field, value)
+    w = _lib.LLLayerWeights(*([FAKE.value] * 6))
+    st = lib.llama_layer_forward(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, 1, 32, 32, None, None, 0, FAKE, FAKE,
+                                 1 << 30, None)
+    assert st == status, L.last_error()
+    assert L.last_error()
+    assert lib.llama_layer_workspace_bytes(ctypes.byref(c), 1, 32, 0) == 0
+
+
+def test_bf16_needs_multiples_of_8():
+    lib = L.load()
+    c = _cfg(dtype=torch.bfloat16, hidden=60)
+    w = _lib.LLLayerWeights(*([FAKE.value] * 6))
+    st = lib.llama_layer_forward(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, 1, 32, 32, None, None, 0, FAKE, FAKE,
+                                 1 << 30, None)
+    assert st == _lib.LL_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("rope_kw", [dict(type="llama3", low_freq_factor=4.0, high_freq_factor=1.0),
+                                     dict(type="linear", factor=0.0),
+                                     dict(theta=-1.0),
+                                     dict(type="dynamic_ntk", original_max_pos=0)])
+def test_rope_validation(rope_kw):
+    lib = L.load()
+    c = _cfg(rope=L.Rope(**rope_kw))
+    w = _lib.LLLayerWeights(*([FAKE.value] * 6))
+    st = lib.llama_layer_forward(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, 1, 32, 32, None, None, 0, FAKE, FAKE,
+                                 1 << 30, None)
+    assert st == _lib.LL_EINVAL
+
+
+def test_layer_argument_errors():
+    lib = L.load()
+    c = _cfg()
+    w = _lib.LLLayerWeights(*([FAKE.value] * 6))
+    ws = lib.llama_layer_workspace_bytes(ctypes.byref(c), 1, 32, 0)
+    assert ws > 0
+
+    def call(**kw):
+        a = dict(w=ctypes.byref(w), hidden=FAKE, pos=FAKE, B=1, S=32, L=32, kc=None, vc=None, ctx=0, out=FAKE,
+                 ws=FAKE, wsb=ws)
+        a.update(kw)
+        return lib.llama_layer_forward(ctypes.byref(c), a["w"], a["hidden"], a["pos"], a["B"], a["S"], a["L"], a["kc"],
+                                       a["vc"], a["ctx"], a["out"], a["ws"], a["wsb"], None)
+
+    assert call(w=None) == _lib.LL_EINVAL
+    assert call(hidden=None) == _lib.LL_EINVAL
+    assert call(pos=None) == _lib.LL_EINVAL
+    assert call(L=0) == _lib.LL_EINVAL
+    assert call(wsb=ws - 1) == _lib.LL_EINVAL
+    assert call(kc=FAKE) == _lib.LL_EINVAL                       # only one cache
+    assert call(kc=FAKE, vc=FAKE, ctx=0) == _lib.LL_EINVAL      # caches without ctx
+    assert call(hidden=ctypes.c_void_p(0x10002)) == _lib.LL_EINVAL  # misaligned
+    assert call(B=-1) == _lib.LL_EINVAL
+    assert call(B=0) == _lib.LL_OK and call(S=0) == _lib.LL_OK   # empty batch: nothing to do
+    bad = _lib.LLLayerWeights(FAKE.value, None, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    assert call(w=ctypes.byref(bad)) == _lib.LL_EINVAL
+
+
+def test_kernel_entry_point_errors():
+    lib = L.load()
+    assert lib.rmsnorm(None, None, None, 4, 64, 1e-5, _lib.LL_BF16, None) == _lib.LL_EINVAL
+    assert lib.rmsnorm(FAKE, FAKE, FAKE, 4, 0, 1e-5, _lib.LL_BF16, None) == _lib.LL_EINVAL
+    assert lib.rmsnorm(FAKE, FAKE, FAKE, 0, 64, 1e-5, _lib.LL_BF16, None) == _lib.LL_OK
+    r = L.Rope().to_c()
+    assert lib.rope_apply(None, FAKE, FAKE, 1, 4, 4, 2, 16, 4, _lib.LL_BF16, None) == _lib.LL_EINVAL
+    assert lib.rope_apply(ctypes.byref(r), FAKE, FAKE, 1, 4, 4, 2, 15, 4, _lib.LL_BF16, None) == _lib.LL_EINVAL
+    assert lib.rope_apply(ctypes.byref(r), FAKE, FAKE, 1, 4, 4, 2, 16, 0, _lib.LL_BF16, None) == _lib.LL_EINVAL
+    assert lib.gqa_attn_prefill(FAKE, ctypes.byref(r), None, 8, FAKE, None, None, 0, 1, 4, 4, 2, 64, _lib.LL_BF16,
+                                None) == _lib.LL_EINVAL                     # rope without positions
+    assert lib.gqa_attn_prefill(FAKE, None, None, 0, FAKE, FAKE, None, 8, 1, 4, 4, 2, 64, _lib.LL_BF16,
+                                None) == _lib.LL_EINVAL                     # one cache only
+    assert lib.gqa_attn_prefill(FAKE, None, None, 0, FAKE, None, None, 0, 1, 4, 3, 2, 64, _lib.LL_BF16,
+                                None) == _lib.LL_EINVAL                     # 3 % 2
+    need = lib.gqa_attn_decode_workspace_bytes(2, 4, 64, 1024)
+    assert need > 0
+    assert lib.gqa_attn_decode(FAKE, None, FAKE, 0, FAKE, FAKE, 1024, FAKE, 2, 4, 2, 64, _lib.LL_BF16, FAKE, need - 1,
+                               None) == _lib.LL_EINVAL
+    assert lib.gqa_attn_decode(FAKE, None, FAKE, 0, None, None, 1024, FAKE, 2, 4, 2, 64, _lib.LL_BF16, FAKE, need,
+                               None) == _lib.LL_EINVAL
+    mneed = lib.swiglu_mlp_workspace_bytes(8, 64, 128, _lib.LL_BF16)
+    assert lib.swiglu_mlp(FAKE, FAKE, FAKE, None, FAKE, 8, 64, 128, _lib.LL_BF16, FAKE, mneed - 1,
+                          None) == _lib.LL_EINVAL
+    assert lib.swiglu_mlp(FAKE, FAKE, FAKE, None, FAKE, 8, 60, 128, _lib.LL_BF16, FAKE, mneed,
+                          None) == _lib.LL_EUNSUPPORTED
+    # out aliasing x is rejected
+    assert lib.swiglu_mlp(FAKE, FAKE, FAKE, None, FAKE, 8, 64, 128, _lib.LL_BF16, FAKE, mneed, None) == _lib.LL_EINVAL
+
+
+def test_profile_stage_names():
+    lib = L.load()
+    names = [lib.ll_profile_stage_name(i).decode() for i in range(7)]
+    assert names == ["rmsnorm_attn", "qkv_proj", "attention", "o_proj_residual", "rmsnorm_mlp", "gate_up_silu",
+                     "down_residual"]
+    assert lib.ll_profile_stage_name(7) == b""
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    """The binding and library sources never reference the oracle or a CPU implementation."""
+    pkg = os.path.join(ROOT, "transformer_layer_forward_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "numpy" not in text or f == "build.py", f

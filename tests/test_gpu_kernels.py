@@ -1,0 +1,236 @@
+"""GPU parity of each C-ABI entry point against the fp64 oracle, on seeded inputs.
+
+Sizes span several tiles plus a ragged tail. Bounds: normwise max relative error <= 2e-2 (bf16) or
+1e-4 (fp32); integer-valued outcomes (untouched values, cache slots not written) are compared
+bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import transformer_layer_forward_amd as L
+from oracle import ref
+from synth_inputs import RopeCfg, normal, to_f64 as bits_to_f64
+from tests.gpu_util import DEV, require_gpu, tol, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TD = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _rope(rc: RopeCfg) -> L.Rope:
+    return L.Rope(type=rc.type, theta=rc.theta, factor=rc.factor, low_freq_factor=rc.low_freq_factor,
+                  high_freq_factor=rc.high_freq_factor, original_max_pos=rc.original_max_pos,
+                  interleaved=rc.interleaved)
+
+
+# ------------------------------------------------------------------ RMSNorm
+@pytest.mark.parametrize("dtype,rows,H", [("bf16", 37, 4096), ("bf16", 5, 2048), ("bf16", 3, 8200), ("bf16", 4, 60),
+                                          ("f32", 32, 64), ("f32", 7, 102), ("f32", 9, 4096)])
+def test_rmsnorm(dtype, rows, H):
+    require_gpu()
+    x = normal(0, 100, (rows, H), dtype)
+    g = normal(0, 101, (H,), dtype, std=0.1, mean=1.0)
+    y = L.rmsnorm(to_dev(x, dtype), to_dev(g, dtype), 1e-5)
+    torch.cuda.synchronize()
+    want = ref.rmsnorm(bits_to_f64(x, dtype), bits_to_f64(g, dtype), 1e-5)
+    assert ref.max_rel_err(to_f64(y), want) <= tol(dtype)
+
+
+def test_rmsnorm_constant_rows_return_gain():
+    """RMSNorm of a constant row c*1 is g*sign(c) up to eps (llama3 结构详解 §3.1)."""
+    require_gpu()
+    H = 4096
+    x = torch.full((3, H), 2.5, device=DEV, dtype=torch.bfloat16)
+    x[1] = -0.75
+    g = to_dev(normal(0, 102, (H,), "bf16", std=0.1, mean=1.0), "bf16")
+    y = to_f64(L.rmsnorm(x, g, 1e-5))
+    gg = to_f64(g)
+    np.testing.assert_allclose(y[0], gg, rtol=8e-3)
+    np.testing.assert_allclose(y[1], -gg, rtol=8e-3)
+
+
+# ------------------------------------------------------------------ RoPE apply
+ROPES = [RopeCfg(theta=500000.0), RopeCfg(type="linear", theta=10000.0, factor=4.0),
+         RopeCfg(type="dynamic_ntk", theta=10000.0, factor=2.0, original_max_pos=256),
+         RopeCfg(type="llama3", theta=500000.0, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
+                 original_max_pos=8192)]
+
+
+@pytest.mark.parametrize("rc", ROPES, ids=lambda r: r.type)
+@pytest.mark.parametrize("il", [False, True])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 16)])
+def test_rope_apply(rc, il, dtype, d):
+    require_gpu()
+    import dataclasses
+    rc = dataclasses.replace(rc, interleaved=il)
+    B, S, nh, nkv = 2, 37, 4, 2
+    L_ = 20000
+    qkv = normal(1, 110, (B, S, (nh + 2 * nkv) * d), dtype)
+    pos = np.random.default_rng([1, 111]).integers(0, L_, (B, S)).astype(np.int64)
+    t = to_dev(qkv, dtype)
+    L.rope_apply(_rope(rc), t, torch.from_numpy(pos).to(DEV), nh, nkv, d, L_)
+    got = to_f64(t)
+    x = bits_to_f64(qkv, dtype)
+    f = ref.rope_frequencies(d, rc, L_)
+    q, k, v = ref.split_qkv(x, nh, nkv, d)
+    gq, gk, gv = ref.split_qkv(got, nh, nkv, d)
+    assert ref.max_rel_err(gq, ref.rope_rotate(q, pos[..., None], f, il)) <= tol(dtype)
+    assert ref.max_rel_err(gk, ref.rope_rotate(k, pos[..., None], f, il)) <= tol(dtype)
+    np.testing.assert_array_equal(gv, v)
+
+
+# ------------------------------------------------------------------ projections (via the MLP entry point)
+@pytest.mark.parametrize("dtype,M,H,I", [("bf16", 1, 256, 512), ("bf16", 37, 512, 1000), ("bf16", 64, 256, 384),
+                                         ("bf16", 65, 256, 384), ("bf16", 300, 1024, 2048),
+                                         ("bf16", 515, 512, 1032), ("f32", 32, 64, 176), ("f32", 45, 96, 200)])
+@pytest.mark.parametrize("with_residual", [False, True])
+def test_swiglu_mlp(dtype, M, H, I, with_residual):
+    require_gpu()
+    x = normal(2, 120, (M, H), dtype)
+    wgu = normal(2, 121, (2 * I, H), dtype, std=0.02)
+    wd = normal(2, 122, (H, I), dtype, std=0.02)
+    r = normal(2, 123, (M, H), dtype)
+    res = to_dev(r, dtype) if with_residual else None
+    out = L.swiglu_mlp(to_dev(x, dtype), to_dev(wgu, dtype), to_dev(wd, dtype), residual=res)
+    want = ref.linear(ref.swiglu_act(bits_to_f64(x, dtype), bits_to_f64(wgu, dtype), I), bits_to_f64(wd, dtype))
+    got = to_f64(out)
+    if with_residual:
+        rr = bits_to_f64(r, dtype)
+        assert ref.max_rel_err(got, want + rr) <= tol(dtype)
+        # the branch alone: out - residual inherits out's own rounding (half an ulp, 2^-9 |out| in bf16)
+        bound = tol(dtype) * np.max(np.abs(want)) + (2.0 ** -8 if dtype == "bf16" else 1e-6) * np.max(np.abs(got))
+        assert np.max(np.abs(got - rr - want)) <= bound
+    else:
+        assert ref.max_rel_err(got, want) <= tol(dtype)
+
+
+# ------------------------------------------------------------------ prefill attention
+PREFILL = [
+    # dtype, B, S, nh, nkv, d
+    ("bf16", 2, 130, 8, 2, 128),
+    ("bf16", 1, 200, 8, 8, 64),
+    ("bf16", 2, 64, 4, 2, 64),
+    ("bf16", 1, 100, 16, 2, 128),
+    ("bf16", 3, 1, 4, 1, 128),
+    ("bf16", 1, 257, 6, 2, 64),      # g = 3 (one head per block)
+    ("bf16", 1, 50, 4, 2, 96),       # generic kernel
+    ("f32", 1, 32, 4, 2, 16),
+    ("f32", 2, 45, 6, 3, 32),
+]
+
+
+def _attn_inputs(dtype, B, S, nh, nkv, d, seed=3):
+    qkv = normal(seed, 130, (B, S, (nh + 2 * nkv) * d), dtype)
+    return qkv, bits_to_f64(qkv, dtype)
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("mode", ["rotated", "rope", "rope_il_cache"])
+def test_attn_prefill(case, mode):
+    require_gpu()
+    dtype, B, S, nh, nkv, d = case
+    qkv, x = _attn_inputs(dtype, B, S, nh, nkv, d)
+    pos = np.broadcast_to(np.arange(S, dtype=np.int64), (B, S)).copy()
+    rc = None
+    q, k, v = ref.split_qkv(x, nh, nkv, d)
+    if mode != "rotated":
+        rc = RopeCfg(type="llama3", theta=500000.0, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
+                     original_max_pos=64, interleaved=(mode == "rope_il_cache"))
+        f = ref.rope_frequencies(d, rc, S)
+        q = ref.rope_rotate(q, pos[..., None], f, rc.interleaved)
+        k = ref.rope_rotate(k, pos[..., None], f, rc.interleaved)
+    want = ref.attention_prefill(q, k, v)
+    kc = vc = None
+    ctx = S + 7
+    if mode == "rope_il_cache":
+        kc = torch.zeros((B, ctx, nkv, d), device=DEV, dtype=TD[dtype])
+        vc = torch.zeros((B, ctx, nkv, d), device=DEV, dtype=TD[dtype])
+    o = L.gqa_attn_prefill(to_dev(qkv, dtype), torch.from_numpy(pos).to(DEV), nh, nkv, d,
+                           rope=_rope(rc) if rc else None, kv_seq_len=S, k_cache=kc, v_cache=vc)
+    got = to_f64(o)
+    assert got.shape == (B, S, nh * d)
+    assert ref.max_rel_err(got, want) <= tol(dtype)
+    if kc is not None:
+        gk, gv = to_f64(kc), to_f64(vc)
+        assert ref.max_rel_err(gk[:, :S], k) <= tol(dtype)
+        np.testing.assert_array_equal(gv[:, :S], v)
+        assert np.all(gk[:, S:] == 0) and np.all(gv[:, S:] == 0)
+
+
+def test_attn_prefill_causality_bitwise():
+    """Perturbing tokens after t leaves outputs of tokens <= t bit-identical (CSDN answer "#### 5." mask)."""
+    require_gpu()
+    B, S, nh, nkv, d = 1, 192, 8, 2, 128
+    qkv, _ = _attn_inputs("bf16", B, S, nh, nkv, d, seed=4)
+    a = to_dev(qkv, "bf16")
+    o1 = L.gqa_attn_prefill(a, None, nh, nkv, d)
+    b = a.clone()
+    b[:, 100:] = torch.randn_like(b[:, 100:].float()).to(torch.bfloat16)
+    o2 = L.gqa_attn_prefill(b, None, nh, nkv, d)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :100], o2[:, :100])
+    assert not torch.equal(o1[:, 100:], o2[:, 100:])
+
+
+def test_attn_prefill_mha_equals_repeated_gqa():
+    """GQA with n_kv < n_h equals MHA on explicitly repeated K/V (llama3 结构详解 §3.2)."""
+    require_gpu()
+    B, S, nh, nkv, d = 1, 150, 8, 2, 64
+    qkv, x = _attn_inputs("bf16", B, S, nh, nkv, d, seed=5)
+    q, k, v = ref.split_qkv(qkv.reshape(B, S, -1).view(np.uint16), nh, nkv, d)
+    k_rep = np.repeat(k, nh // nkv, axis=2)
+    v_rep = np.repeat(v, nh // nkv, axis=2)
+    mha = np.concatenate([q.reshape(B, S, -1), k_rep.reshape(B, S, -1), v_rep.reshape(B, S, -1)], axis=-1)
+    o_gqa = L.gqa_attn_prefill(to_dev(qkv, "bf16"), None, nh, nkv, d)
+    o_mha = L.gqa_attn_prefill(to_dev(np.ascontiguousarray(mha), "bf16"), None, nh, nh, d)
+    torch.cuda.synchronize()
+    assert ref.max_rel_err(to_f64(o_gqa), to_f64(o_mha)) <= 1e-2
+
+
+# ------------------------------------------------------------------ decode attention
+DECODE = [
+    # dtype, B, ctx, nh, nkv, d
+    ("bf16", 4, 1500, 8, 2, 128),
+    ("bf16", 2, 700, 4, 4, 64),
+    ("bf16", 3, 1100, 32, 8, 128),
+    ("bf16", 2, 300, 4, 2, 96),      # generic kernel
+    ("f32", 2, 40, 4, 2, 16),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("with_rope", [False, True])
+def test_attn_decode(case, with_rope):
+    require_gpu()
+    dtype, B, ctx, nh, nkv, d = case
+    qkv = normal(6, 140, (B, (nh + 2 * nkv) * d), dtype)
+    kc = normal(6, 141, (B, ctx, nkv, d), dtype)
+    vc = normal(6, 142, (B, ctx, nkv, d), dtype)
+    pos = np.array(([0, ctx - 1, 511, 512, 1023, 1024][:B] + [ctx // 2] * B)[:B], dtype=np.int64)
+    pos = np.minimum(pos, ctx - 1)
+    rc = RopeCfg(theta=500000.0) if with_rope else None
+    x = bits_to_f64(qkv, dtype)
+    q, k, v = ref.split_qkv(x, nh, nkv, d)
+    if rc:
+        f = ref.rope_frequencies(d, rc, ctx)
+        q = ref.rope_rotate(q, pos[:, None], f)
+        k = ref.rope_rotate(k, pos[:, None], f)
+    tk, tv = to_dev(kc, dtype), to_dev(vc, dtype)
+    o = L.gqa_attn_decode(to_dev(qkv, dtype), torch.from_numpy(pos).to(DEV), tk, tv, nh, nkv, d,
+                          rope=_rope(rc) if rc else None, kv_seq_len=ctx)
+    got = to_f64(o)
+    K0, V0 = bits_to_f64(kc, dtype), bits_to_f64(vc, dtype)
+    gk, gv = to_f64(tk), to_f64(tv)
+    for b in range(B):
+        p = int(pos[b])
+        K = K0[b, :p + 1].copy()
+        V = V0[b, :p + 1].copy()
+        K[p], V[p] = k[b], v[b]
+        want = ref.attention_one_query(q[b], K, V)
+        assert ref.max_rel_err(got[b], want) <= tol(dtype), b
+        assert ref.max_rel_err(gk[b, p], k[b]) <= tol(dtype)
+        np.testing.assert_array_equal(gv[b, p], v[b])
+        keep = np.ones(ctx, bool)
+        keep[p] = False
+        np.testing.assert_array_equal(gk[b, keep], K0[b, keep])
+        np.testing.assert_array_equal(gv[b, keep], V0[b, keep])

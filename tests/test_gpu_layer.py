@@ -1,0 +1,212 @@
+"""GPU parity of llama_layer_forward against the fp64 oracle.
+
+Small members of each workload family are compared in full; the full-size workloads are compared on
+seeded sampled rows the oracle evaluates one by one (rows 0 and S-1 always included). Besides the
+output, out - hidden (the two residual branches together, o_proj + MLP) is compared, since the
+N(0,1) residual stream would otherwise hide branch errors."""
+import dataclasses
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_layer_forward_amd as L
+from oracle import ref
+from synth_inputs import (CONFIGS, RopeCfg, make_cache, make_cache_row, make_decode_positions, make_hidden,
+                          make_prefill_positions, make_weights, scaled, to_f64 as bits_to_f64)
+from tests.gpu_util import DEV, require_gpu, tol, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TD = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def layer_cfg(cfg) -> L.LayerConfig:
+    rc = cfg.rope
+    rope = L.Rope(type=rc.type, theta=rc.theta, factor=rc.factor, low_freq_factor=rc.low_freq_factor,
+                  high_freq_factor=rc.high_freq_factor, original_max_pos=rc.original_max_pos,
+                  interleaved=rc.interleaved)
+    return L.LayerConfig(cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.intermediate, cfg.eps, rope,
+                         TD[cfg.dtype])
+
+
+def dev_weights(W, dtype):
+    return {k: to_dev(v, dtype) for k, v in W.items()}
+
+
+def w64(W, dtype):
+    return {k: bits_to_f64(v, dtype) for k, v in W.items()}
+
+
+def check(got_out, x64, want_out, want_branch, dtype, label=""):
+    e_out = ref.max_rel_err(got_out, want_out)
+    e_br = ref.max_rel_err(got_out - x64, want_branch)
+    print(f"{label} out err {e_out:.3e} branch err {e_br:.3e}", flush=True)
+    assert e_out <= tol(dtype), label
+    # out - hidden inherits out's own rounding (half an ulp: 2^-9 |out| in bf16), so the branch bound is
+    # the tolerance on the branch plus that rounding
+    ulp = 2.0 ** -8 if dtype == "bf16" else 1e-6
+    bound = tol(dtype) * np.max(np.abs(want_branch)) + ulp * np.max(np.abs(got_out))
+    assert np.max(np.abs(got_out - x64 - want_branch)) <= bound, label
+
+
+SMALL = [
+    CONFIGS["tiny_f32"],
+    scaled(CONFIGS["tiny_f32"], B=2, S=45, rope=RopeCfg(type="llama3", theta=10000.0, factor=8.0,
+                                                        original_max_pos=16, interleaved=True)),
+    scaled(CONFIGS["llama32_1b_prefill"], B=2, S=160),
+    scaled(CONFIGS["llama3_8b_prefill"], B=1, S=100),
+    scaled(CONFIGS["llama3_8b_prefill"], B=2, S=70, rope=RopeCfg(type="dynamic_ntk", theta=500000.0, factor=2.0,
+                                                                 original_max_pos=32)),
+    scaled(CONFIGS["llama3_8b_prefill"], B=1, S=129, rope=RopeCfg(type="linear", theta=500000.0, factor=4.0,
+                                                                  interleaved=True)),
+    scaled(CONFIGS["llama3_8b_long_llama3rope"], S=300),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"{c.name}-B{c.B}-S{c.S}-{c.rope.type}")
+def test_layer_prefill_small(cfg):
+    require_gpu()
+    W = make_weights(cfg, seed=0)
+    x = make_hidden(cfg, seed=0)
+    pos = make_prefill_positions(cfg)
+    out = L.llama_layer_forward(layer_cfg(cfg), dev_weights(W, cfg.dtype), to_dev(x, cfg.dtype),
+                                torch.from_numpy(pos).to(DEV), kv_seq_len=cfg.S)
+    got = to_f64(out)
+    x64 = bits_to_f64(x, cfg.dtype)
+    want = ref.layer_prefill(cfg, w64(W, cfg.dtype), x64, pos, cfg.S)
+    check(got, x64, want["out"], want["attn_proj"] + want["mlp_out"], cfg.dtype, cfg.name)
+
+
+def test_layer_in_place_and_causality():
+    """out may equal hidden; perturbing later tokens leaves earlier rows bit-identical."""
+    require_gpu()
+    cfg = scaled(CONFIGS["llama32_1b_prefill"], B=1, S=200)
+    W = dev_weights(make_weights(cfg, seed=1), cfg.dtype)
+    x = to_dev(make_hidden(cfg, seed=1), cfg.dtype)
+    pos = torch.from_numpy(make_prefill_positions(cfg)).to(DEV)
+    lc = layer_cfg(cfg)
+    a = L.llama_layer_forward(lc, W, x, pos)
+    x2 = x.clone()
+    x2[:, 120:] = -x2[:, 120:]
+    b = L.llama_layer_forward(lc, W, x2, pos)
+    inplace = x.clone()
+    L.llama_layer_forward(lc, W, inplace, pos, out=inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, :120], b[:, :120])
+    assert not torch.equal(a[:, 120:], b[:, 120:])
+    assert torch.equal(inplace, a)
+
+
+def test_layer_zero_branches_is_identity():
+    """W_o = W_down = 0 makes both branches exactly zero: out == hidden bit for bit (nanotron §9.5)."""
+    require_gpu()
+    cfg = scaled(CONFIGS["llama3_8b_prefill"], B=1, S=80)
+    W = dev_weights(make_weights(cfg, seed=2), cfg.dtype)
+    W["w_o"].zero_()
+    W["w_down"].zero_()
+    x = to_dev(make_hidden(cfg, seed=2), cfg.dtype)
+    out = L.llama_layer_forward(layer_cfg(cfg), W, x, torch.from_numpy(make_prefill_positions(cfg)).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out, x)
+
+
+@pytest.mark.parametrize("cfg", [scaled(CONFIGS["llama3_8b_decode"], B=5, ctx=1300),
+                                 scaled(CONFIGS["tiny_f32"], B=3, S=1, ctx=40, decode=True)],
+                         ids=lambda c: c.name)
+def test_layer_decode_small(cfg):
+    require_gpu()
+    W = make_weights(cfg, seed=3)
+    x = make_hidden(cfg, seed=3)
+    lo = 1 if cfg.ctx < 1024 else 1024
+    pos = make_decode_positions(cfg, seed=3, lo=lo)
+    pos[0] = cfg.ctx - 1
+    kc, vc = make_cache(cfg, "k", seed=3), make_cache(cfg, "v", seed=3)
+    tk, tv = to_dev(kc, cfg.dtype), to_dev(vc, cfg.dtype)
+    out = L.llama_layer_forward(layer_cfg(cfg), dev_weights(W, cfg.dtype), to_dev(x, cfg.dtype),
+                                torch.from_numpy(pos).to(DEV), kv_seq_len=cfg.ctx, k_cache=tk, v_cache=tv)
+    got = to_f64(out)[:, 0]
+    x64 = bits_to_f64(x, cfg.dtype)
+    want = ref.layer_decode(cfg, w64(W, cfg.dtype), x64, pos, cfg.ctx, lambda b: bits_to_f64(kc[b], cfg.dtype),
+                            lambda b: bits_to_f64(vc[b], cfg.dtype))
+    check(got, x64[:, 0], want["out"], want["attn_proj"] + want["mlp_out"], cfg.dtype, cfg.name)
+    gk, gv = to_f64(tk), to_f64(tv)
+    for b in range(cfg.B):
+        assert ref.max_rel_err(gk[b, pos[b]].reshape(-1), want["k_new"][b]) <= tol(cfg.dtype)
+        assert ref.max_rel_err(gv[b, pos[b]].reshape(-1), want["v_new"][b]) <= tol(cfg.dtype)
+
+
+def test_layer_decode_matches_prefill_row():
+    """Prefill of tokens 0..P-1 fills the cache; a decode step for token P must reproduce row P of a
+    prefill over tokens 0..P (llama3 结构详解 §3.2; CSDN answer "#### 3.": the cache avoids recompute)."""
+    require_gpu()
+    P = 150
+    cfg = scaled(CONFIGS["llama3_8b_prefill"], B=2, S=P + 1)
+    W = dev_weights(make_weights(cfg, seed=4), cfg.dtype)
+    x = to_dev(make_hidden(cfg, seed=4), cfg.dtype)
+    lc = layer_cfg(cfg)
+    ctx = 256
+    pos = torch.from_numpy(make_prefill_positions(cfg)).to(DEV)
+    full = L.llama_layer_forward(lc, W, x, pos, kv_seq_len=ctx)
+    kc = torch.zeros((2, ctx, cfg.n_kv_heads, cfg.head_dim), device=DEV, dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    L.llama_layer_forward(lc, W, x[:, :P].contiguous(), pos[:, :P].contiguous(), kv_seq_len=ctx, k_cache=kc,
+                          v_cache=vc)
+    step = L.llama_layer_forward(lc, W, x[:, P:P + 1].contiguous(), pos[:, P:P + 1].contiguous(), kv_seq_len=ctx,
+                                 k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    a, b = to_f64(step)[:, 0], to_f64(full)[:, P]
+    xb = to_f64(x)[:, P]
+    assert ref.max_rel_err(a, b) <= 2e-2
+    assert ref.max_rel_err(a - xb, b - xb) <= 3e-2
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+def _sample_rows(cfg, n, seed=7):
+    rng = np.random.default_rng([seed, 99])
+    rows = {(0, 0), (cfg.B - 1, cfg.S - 1)}
+    while len(rows) < n:
+        rows.add((int(rng.integers(0, cfg.B)), int(rng.integers(0, cfg.S))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["llama32_1b_prefill", "llama3_8b_prefill", "llama3_8b_long_llama3rope"])
+def test_layer_full_size_sampled(name):
+    require_gpu()
+    cfg = CONFIGS[name]
+    W = make_weights(cfg, seed=0)
+    x = make_hidden(cfg, seed=0)
+    pos = make_prefill_positions(cfg)
+    out = L.llama_layer_forward(layer_cfg(cfg), dev_weights(W, cfg.dtype), to_dev(x, cfg.dtype),
+                                torch.from_numpy(pos).to(DEV), kv_seq_len=cfg.S)
+    got = to_f64(out)
+    rows = _sample_rows(cfg, 12 if cfg.S > 10000 else 24)
+    x64 = bits_to_f64(x, cfg.dtype)
+    want = ref.layer_prefill_rows(cfg, w64(W, cfg.dtype), x64, pos, cfg.S, rows)
+    g = np.stack([got[b, i] for b, i in rows])
+    xs = np.stack([x64[b, i] for b, i in rows])
+    check(g, xs, want["out"], want["attn_proj"] + want["mlp_out"], cfg.dtype, name)
+
+
+def test_layer_full_size_decode_sampled():
+    require_gpu()
+    cfg = CONFIGS["llama3_8b_decode"]
+    W = make_weights(cfg, seed=0)
+    x = make_hidden(cfg, seed=0)
+    pos = make_decode_positions(cfg, seed=0)
+    kc, vc = make_cache(cfg, "k", seed=0), make_cache(cfg, "v", seed=0)
+    tk, tv = to_dev(kc, cfg.dtype), to_dev(vc, cfg.dtype)
+    del kc, vc
+    out = L.llama_layer_forward(layer_cfg(cfg), dev_weights(W, cfg.dtype), to_dev(x, cfg.dtype),
+                                torch.from_numpy(pos).to(DEV), kv_seq_len=cfg.ctx, k_cache=tk, v_cache=tv)
+    got = to_f64(out)[:, 0]
+    bs = [0, 17, 63]
+    x64 = bits_to_f64(x, cfg.dtype)
+    want = ref.layer_decode(cfg, w64(W, cfg.dtype), x64, pos, cfg.ctx,
+                            lambda b: bits_to_f64(make_cache_row(cfg, "k", b, 0), cfg.dtype),
+                            lambda b: bits_to_f64(make_cache_row(cfg, "v", b, 0), cfg.dtype), batch_rows=bs)
+    check(got[bs], x64[bs, 0], want["out"], want["attn_proj"] + want["mlp_out"], cfg.dtype, cfg.name)
+    for i, b in enumerate(bs):
+        krow = to_f64(tk[b, int(pos[b])]).reshape(-1)
+        assert ref.max_rel_err(krow, want["k_new"][i]) <= tol(cfg.dtype)

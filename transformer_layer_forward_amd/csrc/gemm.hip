@@ -1,0 +1,457 @@
+// Dense projections of the layer: C = X W^T (nn.Linear without bias, W stored [out, in]).
+//
+// Used for the fused QKV projection (nanotron "模型层" §9.3 qkv_proj), o_proj + residual (§9.5),
+// the fused gate_up projection with the silu(gate)*up epilogue (§9.4) and down + residual.
+//
+// bf16 path, prefill-sized M: one workgroup of 8 waves computes a 256 (tokens) x 256 (weight rows)
+// tile over K in steps of 64. Both operands are K-contiguous, so global->LDS copies are 16-byte
+// row chunks; LDS rows are XOR-swizzled per 16-byte chunk so that the 16 lanes of a
+// matrix-core operand read (16 rows, same chunk) hit distinct banks. Two LDS stages: the next
+// K-step is fetched into registers while the current one feeds v_mfma_f32_16x16x32_bf16.
+// The weight tile is the MFMA A operand and the token tile the B operand, so each lane ends with
+// 4 consecutive output columns of one token row (8-byte stores).
+// Tiles are numbered so that each XCD (blocks are dealt round-robin to the 8 XCDs) works on a
+// contiguous range of tiles, grouped 8 token-tiles deep, for L2 reuse of both operands.
+//
+// gate_up: the weight tile interleaves 16-row blocks of W_gate and W_up for the same output
+// columns, so the gate and up accumulators of one output sit in the same lane and
+// silu(g)*u is formed in registers; the [M, 2I] product is never stored.
+//
+// bf16 path, small M (decode): split-K over many workgroups that stream W straight from HBM into
+// matrix-core operands; fp32 partial sums go to workspace and a second kernel reduces them and
+// applies the epilogue.
+//
+// fp32 path: a simple LDS-tiled FMA kernel (no bf16 or reduced-precision step anywhere).
+#include "common.h"
+
+namespace ll {
+
+// ------------------------------------------------------------------ bf16, large M
+constexpr int GB_M = 256, GB_N = 256, GB_K = 64;
+constexpr int GB_WAVES_N = 2, GB_WAVES_M = 4;
+constexpr int GB_THREADS = 64 * GB_WAVES_N * GB_WAVES_M;  // 512
+constexpr int GB_WTN = GB_N / GB_WAVES_N;                 // 128 weight rows per wave
+constexpr int GB_WTM = GB_M / GB_WAVES_M;                 // 64 tokens per wave
+constexpr int GB_FN = GB_WTN / 16, GB_FM = GB_WTM / 16;   // 8 x 4 fragments
+constexpr int GB_STAGE = (GB_M + GB_N) * GB_K;            // elements per LDS stage
+constexpr int GB_LDS_BYTES = 2 * GB_STAGE * 2;            // 128 KiB
+constexpr int GB_LOADS = (GB_M * GB_K / 8) / GB_THREADS;  // 16-byte chunks per lane per operand (4)
+
+// physical 16-byte chunk of logical chunk c in LDS row r (rows are 8 chunks = 128 bytes)
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int EPI>
+__global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_big_kernel(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, const bf16_t* __restrict__ R,
+    int M, int N, int K, int tiles_m, int tiles_n) {
+    extern __shared__ __align__(16) bf16_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave % GB_WAVES_N, wm = wave / GB_WAVES_N;
+
+    // ---- tile order: contiguous range per XCD, then groups of 8 token tiles
+    const int T = tiles_m * tiles_n;
+    int lin = blockIdx.x;
+    if ((T & 7) == 0) lin = (lin & 7) * (T >> 3) + (lin >> 3);
+    constexpr int GROUP = 8;
+    const int group = lin / (GROUP * tiles_n);
+    const int first_m = group * GROUP;
+    const int gsz = min(tiles_m - first_m, GROUP);
+    const int in_g = lin - group * GROUP * tiles_n;
+    const int tm = first_m + in_g % gsz;
+    const int tn = in_g / gsz;
+    const int m0 = tm * GB_M;
+    const int ncols = (EPI == EPI_SILU) ? GB_N / 2 : GB_N;  // output columns per tile
+    const int n0 = tn * ncols;
+
+    // ---- loader bookkeeping: lane handles chunk c = tid & 7 of rows (tid >> 3) + 64 i
+    const int cch = tid & 7;
+    const bf16_t* xsrc[GB_LOADS];
+    const bf16_t* wsrc[GB_LOADS];
+    bool xok[GB_LOADS], wok[GB_LOADS];
+    int xdst[GB_LOADS], wdst[GB_LOADS];
+#pragma unroll
+    for (int i = 0; i < GB_LOADS; ++i) {
+        const int r = (tid >> 3) + i * (GB_THREADS / 8);
+        const int gm = m0 + r;
+        xok[i] = gm < M;
+        xsrc[i] = X + static_cast<int64_t>(xok[i] ? gm : 0) * K + cch * 8;
+        xdst[i] = r * GB_K + ((cch ^ swz8(r)) << 3);
+        int grow;
+        if (EPI == EPI_SILU) {
+            const int blk = r >> 4, col = n0 + (blk >> 1) * 16 + (r & 15);
+            wok[i] = col < N;
+            grow = (blk & 1) ? N + col : col;
+        } else {
+            grow = n0 + r;
+            wok[i] = grow < N;
+        }
+        wsrc[i] = W + static_cast<int64_t>(wok[i] ? grow : 0) * K + cch * 8;
+        wdst[i] = (GB_M + r) * GB_K + ((cch ^ swz8(r)) << 3);
+    }
+    uint4 xr[GB_LOADS], wr[GB_LOADS];
+#define GB_GLOAD(k0)                                                                              \
+    do {                                                                                          \
+        const bool kok_ = ((k0) + cch * 8) < K;                                                   \
+        _Pragma("unroll") for (int i = 0; i < GB_LOADS; ++i) {                                    \
+            xr[i] = make_uint4(0, 0, 0, 0);                                                       \
+            wr[i] = make_uint4(0, 0, 0, 0);                                                       \
+            if (xok[i] && kok_) xr[i] = *reinterpret_cast<const uint4*>(xsrc[i] + (k0)); \
+            if (wok[i] && kok_) wr[i] = *reinterpret_cast<const uint4*>(wsrc[i] + (k0)); \
+        }                                                                                         \
+    } while (0)
+#define GB_SSTORE(stage)                                                                          \
+    do {                                                                                          \
+        bf16_t* s_ = smem + (stage) * GB_STAGE;                                                   \
+        _Pragma("unroll") for (int i = 0; i < GB_LOADS; ++i) {                                    \
+            *reinterpret_cast<uint4*>(s_ + xdst[i]) = xr[i];                                      \
+            *reinterpret_cast<uint4*>(s_ + wdst[i]) = wr[i];                                      \
+        }                                                                                         \
+    } while (0)
+
+    f32x4 acc[GB_FN][GB_FM];
+#pragma unroll
+    for (int a = 0; a < GB_FN; ++a)
+#pragma unroll
+        for (int b = 0; b < GB_FM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // operand read offsets (elements) within a stage, per fragment, for the two 32-wide k halves
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    int aoff[2][GB_FN], boff[2][GB_FM];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int ch = s * 4 + lgrp;
+#pragma unroll
+        for (int f = 0; f < GB_FN; ++f) {
+            const int r = wn * GB_WTN + f * 16 + lrow;
+            aoff[s][f] = (GB_M + r) * GB_K + ((ch ^ swz8(r)) << 3);
+        }
+#pragma unroll
+        for (int f = 0; f < GB_FM; ++f) {
+            const int r = wm * GB_WTM + f * 16 + lrow;
+            boff[s][f] = r * GB_K + ((ch ^ swz8(r)) << 3);
+        }
+    }
+
+    const int nk = (K + GB_K - 1) / GB_K;
+    GB_GLOAD(0);
+    GB_SSTORE(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) GB_GLOAD((kt + 1) * GB_K);
+        const bf16_t* s = smem + cur * GB_STAGE;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            bf16x8 av[GB_FN], bv[GB_FM];
+#pragma unroll
+            for (int f = 0; f < GB_FN; ++f) av[f] = *reinterpret_cast<const bf16x8*>(s + aoff[h][f]);
+#pragma unroll
+            for (int f = 0; f < GB_FM; ++f) bv[f] = *reinterpret_cast<const bf16x8*>(s + boff[h][f]);
+#pragma unroll
+            for (int a = 0; a < GB_FN; ++a)
+#pragma unroll
+                for (int b = 0; b < GB_FM; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+        }
+        if (kt + 1 < nk) GB_SSTORE(cur ^ 1);
+        __syncthreads();
+    }
+
+#undef GB_GLOAD
+#undef GB_SSTORE
+
+    // ---- epilogue: lane holds rows n = base + 4*lgrp + {0..3} of token m = ... + lrow
+    const int ldc = N;
+    const bool vec_ok = (N & 3) == 0;  // 8-byte aligned output rows
+#pragma unroll
+    for (int b = 0; b < GB_FM; ++b) {
+        const int m = m0 + wm * GB_WTM + b * 16 + lrow;
+        if (m >= M) continue;
+        bf16_t* crow = C + static_cast<int64_t>(m) * ldc;
+        if (EPI == EPI_SILU) {
+#pragma unroll
+            for (int a = 0; a < GB_FN; a += 2) {
+                const int n = n0 + (wn * GB_WTN) / 2 + (a >> 1) * 16 + 4 * lgrp;
+                float o[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float g = acc[a][b][r], u = acc[a + 1][b][r];
+                    o[r] = g / (1.f + __expf(-g)) * u;
+                }
+                if (vec_ok && n + 3 < N) {
+                    *reinterpret_cast<uint2*>(crow + n) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N) crow[n + r] = f2bf(o[r]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int a = 0; a < GB_FN; ++a) {
+                const int n = n0 + wn * GB_WTN + a * 16 + 4 * lgrp;
+                float o[4] = {acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]};
+                if (vec_ok && n + 3 < N) {
+                    if (EPI == EPI_RESIDUAL) {
+                        const uint2 rv = *reinterpret_cast<const uint2*>(R + static_cast<int64_t>(m) * ldc + n);
+                        o[0] += __uint_as_float(rv.x << 16); o[1] += __uint_as_float(rv.x & 0xffff0000u);
+                        o[2] += __uint_as_float(rv.y << 16); o[3] += __uint_as_float(rv.y & 0xffff0000u);
+                    }
+                    *reinterpret_cast<uint2*>(crow + n) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (n + r < N) {
+                            float v = o[r];
+                            if (EPI == EPI_RESIDUAL) v += bf2f(R[static_cast<int64_t>(m) * ldc + n + r]);
+                            crow[n + r] = f2bf(v);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ bf16, small M (split-K)
+// Workgroup = 4 waves over SK_N weight rows and all M <= 64 tokens, for one K range; each wave
+// takes every 4th 32-wide k step. Operands come straight from global memory (each weight element
+// is used by one wave only); the 4 wave partials are summed through LDS.
+constexpr int SK_N = 32, SK_MAXM = 64, SK_THREADS = 256;
+
+__global__ __launch_bounds__(SK_THREADS) void gemm_bf16_skinny_kernel(const bf16_t* __restrict__ X,
+                                                                      const bf16_t* __restrict__ W,
+                                                                      float* __restrict__ P, int M, int Nw, int K,
+                                                                      int kchunk) {
+    __shared__ f32x4 red[3][2][4][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * SK_N;
+    const int split = blockIdx.y;
+    const int kbeg = split * kchunk;
+    const int kend = min(K, kbeg + kchunk);
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16_t* wp[2];
+    bool wok[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int n = n0 + a * 16 + lrow;
+        wok[a] = n < Nw;
+        wp[a] = W + static_cast<int64_t>(wok[a] ? n : 0) * K;
+    }
+    const bf16_t* xp[4];
+    bool xok[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int m = b * 16 + lrow;
+        xok[b] = m < M;
+        xp[b] = X + static_cast<int64_t>(xok[b] ? m : 0) * K;
+    }
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    for (int k = kbeg + wave * 32; k < kend; k += 4 * 32) {
+        const int kk = k + lgrp * 8;
+        const bool kok = kk < kend;
+        bf16x8 av[2], bv[4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            uint4 u = zero;
+            if (wok[a] && kok) u = *reinterpret_cast<const uint4*>(wp[a] + kk);
+            av[a] = __builtin_bit_cast(bf16x8, u);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            uint4 u = zero;
+            if (xok[b] && kok) u = *reinterpret_cast<const uint4*>(xp[b] + kk);
+            bv[b] = __builtin_bit_cast(bf16x8, u);
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) red[wave - 1][a][b][lane] = acc[a][b];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            f32x4 v = acc[a][b] + red[0][a][b][lane] + red[1][a][b][lane] + red[2][a][b][lane];
+            const int m = b * 16 + lrow;
+            const int n = n0 + a * 16 + 4 * lgrp;
+            if (m >= M) continue;
+            float* prow = P + (static_cast<int64_t>(split) * M + m) * Nw;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n + r < Nw) prow[n + r] = v[r];
+        }
+}
+
+// Sum split partials P[splits][M][Nw] and apply the epilogue; N = output columns.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __restrict__ P, bf16_t* __restrict__ C,
+                                                                 const bf16_t* __restrict__ R, int M, int N, int Nw,
+                                                                 int splits) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= static_cast<int64_t>(M) * N) return;
+    const int m = static_cast<int>(idx / N), n = static_cast<int>(idx - static_cast<int64_t>(m) * N);
+    float s = 0.f, u = 0.f;
+    for (int k = 0; k < splits; ++k) {
+        const float* prow = P + (static_cast<int64_t>(k) * M + m) * Nw;
+        s += prow[n];
+        if (EPI == EPI_SILU) u += prow[N + n];
+    }
+    if (EPI == EPI_SILU) s = s / (1.f + __expf(-s)) * u;
+    if (EPI == EPI_RESIDUAL) s += bf2f(R[idx]);
+    C[idx] = f2bf(s);
+}
+
+// ------------------------------------------------------------------ fp32
+constexpr int GF_T = 32, GF_K = 16;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ X, const float* __restrict__ W,
+                                                       float* __restrict__ C, const float* __restrict__ R, int M,
+                                                       int N, int K) {
+    __shared__ float xs[GF_T][GF_K + 1];
+    __shared__ float ws[2][GF_T][GF_K + 1];
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+    const int m0 = blockIdx.y * GF_T, n0 = blockIdx.x * GF_T;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f}, accu[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < K; k0 += GF_K) {
+        for (int e = threadIdx.x; e < GF_T * GF_K; e += 256) {
+            const int r = e / GF_K, c = e % GF_K;
+            const int gm = m0 + r, gk = k0 + c, gn = n0 + r;
+            xs[r][c] = (gm < M && gk < K) ? X[static_cast<int64_t>(gm) * K + gk] : 0.f;
+            ws[0][r][c] = (gn < N && gk < K) ? W[static_cast<int64_t>(gn) * K + gk] : 0.f;
+            if (EPI == EPI_SILU) ws[1][r][c] = (gn < N && gk < K) ? W[static_cast<int64_t>(N + gn) * K + gk] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < GF_K; ++c) {
+            const float w0 = ws[0][tx][c];
+            const float w1 = (EPI == EPI_SILU) ? ws[1][tx][c] : 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float xv = xs[ty + 8 * i][c];
+                acc[i] = fmaf(xv, w0, acc[i]);
+                if (EPI == EPI_SILU) accu[i] = fmaf(xv, w1, accu[i]);
+            }
+        }
+        __syncthreads();
+    }
+    const int n = n0 + tx;
+    if (n >= N) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + ty + 8 * i;
+        if (m >= M) continue;
+        float v = acc[i];
+        if (EPI == EPI_SILU) v = v / (1.f + expf(-v)) * accu[i];
+        if (EPI == EPI_RESIDUAL) v += R[static_cast<int64_t>(m) * N + n];
+        C[static_cast<int64_t>(m) * N + n] = v;
+    }
+}
+
+// ------------------------------------------------------------------ dispatch
+static bool use_skinny(int64_t M) { return M <= SK_MAXM; }
+
+static void skinny_plan(int64_t Nw, int64_t K, int* splits, int* kchunk) {
+    const int64_t ntiles = (Nw + SK_N - 1) / SK_N;
+    int64_t s = 1;
+    while (ntiles * s < 1024 && s < 64 && K / (s * 2) >= 256) s *= 2;
+    int64_t kc = (K + s - 1) / s;
+    kc = (kc + 127) / 128 * 128;  // whole 4-wave x 32 steps
+    *kchunk = static_cast<int>(kc);
+    *splits = static_cast<int>((K + kc - 1) / kc);
+}
+
+size_t gemm_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K, int epi) {
+    if (dtype != LL_BF16 || !use_skinny(M)) return 0;
+    const int64_t Nw = epi == EPI_SILU ? 2 * N : N;
+    int splits, kchunk;
+    skinny_plan(Nw, K, &splits, &kchunk);
+    return static_cast<size_t>(splits) * M * Nw * sizeof(float);
+}
+
+template <int EPI>
+static hipError_t big_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N, int64_t K,
+                             hipStream_t st) {
+    static bool attr = [] {
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_big_kernel<EPI>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, GB_LDS_BYTES) == hipSuccess;
+    }();
+    if (!attr) return hipErrorInvalidConfiguration;
+    const int ncols = EPI == EPI_SILU ? GB_N / 2 : GB_N;
+    const int tm = static_cast<int>((M + GB_M - 1) / GB_M), tn = static_cast<int>((N + ncols - 1) / ncols);
+    hipLaunchKernelGGL(gemm_bf16_big_kernel<EPI>, dim3(tm * tn), dim3(GB_THREADS), GB_LDS_BYTES, st,
+                       static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), static_cast<bf16_t*>(C),
+                       static_cast<const bf16_t*>(R), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tm,
+                       tn);
+    return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t skinny_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N, int64_t K,
+                                void* ws, hipStream_t st) {
+    const int64_t Nw = EPI == EPI_SILU ? 2 * N : N;
+    int splits, kchunk;
+    skinny_plan(Nw, K, &splits, &kchunk);
+    dim3 grid(static_cast<unsigned>((Nw + SK_N - 1) / SK_N), static_cast<unsigned>(splits));
+    hipLaunchKernelGGL(gemm_bf16_skinny_kernel, grid, dim3(SK_THREADS), 0, st, static_cast<const bf16_t*>(X),
+                       static_cast<const bf16_t*>(W), static_cast<float*>(ws), static_cast<int>(M),
+                       static_cast<int>(Nw), static_cast<int>(K), kchunk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total = M * N;
+    hipLaunchKernelGGL(gemm_splitk_reduce_kernel<EPI>, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
+                       st, static_cast<const float*>(ws), static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R),
+                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(Nw), splits);
+    return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t f32_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N, int64_t K,
+                             hipStream_t st) {
+    dim3 grid(static_cast<unsigned>((N + GF_T - 1) / GF_T), static_cast<unsigned>((M + GF_T - 1) / GF_T));
+    hipLaunchKernelGGL(gemm_f32_kernel<EPI>, grid, dim3(256), 0, st, static_cast<const float*>(X),
+                       static_cast<const float*>(W), static_cast<float*>(C), static_cast<const float*>(R),
+                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N,
+                       int64_t K, void* ws, size_t ws_bytes, hipStream_t st) {
+    if (M == 0 || N == 0) return hipSuccess;
+    if (dtype == LL_F32) {
+        switch (epi) {
+            case EPI_STORE: return f32_launch<EPI_STORE>(X, W, C, R, M, N, K, st);
+            case EPI_RESIDUAL: return f32_launch<EPI_RESIDUAL>(X, W, C, R, M, N, K, st);
+            default: return f32_launch<EPI_SILU>(X, W, C, R, M, N, K, st);
+        }
+    }
+    if (use_skinny(M)) {
+        if (ws_bytes < gemm_workspace_bytes(dtype, M, N, K, epi)) return hipErrorInvalidValue;
+        switch (epi) {
+            case EPI_STORE: return skinny_launch<EPI_STORE>(X, W, C, R, M, N, K, ws, st);
+            case EPI_RESIDUAL: return skinny_launch<EPI_RESIDUAL>(X, W, C, R, M, N, K, ws, st);
+            default: return skinny_launch<EPI_SILU>(X, W, C, R, M, N, K, ws, st);
+        }
+    }
+    switch (epi) {
+        case EPI_STORE: return big_launch<EPI_STORE>(X, W, C, R, M, N, K, st);
+        case EPI_RESIDUAL: return big_launch<EPI_RESIDUAL>(X, W, C, R, M, N, K, st);
+        default: return big_launch<EPI_SILU>(X, W, C, R, M, N, K, st);
+    }
+}
+
+}  // namespace ll
