@@ -234,7 +234,7 @@ LayerWs layer_ws(const ll_layer_cfg* c, int64_t B, int64_t S, int64_t ctx_for_de
     w.h = off; off += round_up(static_cast<size_t>(s.M * s.H) * s.es);
     w.act = off; off += round_up(static_cast<size_t>(s.M * s.I) * s.es);
     size_t g = 0;
-    g = std::max(g, gemm_workspace_bytes(c->dtype, s.M, s.qkvd, s.H, EPI_STORE));
+    g = std::max(g, gemm_workspace_bytes(c->dtype, s.M, s.qkvd, s.H, EPI_ROPE));
     g = std::max(g, gemm_workspace_bytes(c->dtype, s.M, s.H, s.od, EPI_RESIDUAL));
     g = std::max(g, gemm_workspace_bytes(c->dtype, s.M, s.I, s.H, EPI_SILU));
     g = std::max(g, gemm_workspace_bytes(c->dtype, s.M, s.H, s.I, EPI_RESIDUAL));
@@ -558,19 +558,34 @@ ll_status llama_layer_forward(const ll_layer_cfg* cfg, const ll_layer_weights* w
     e = launch_rmsnorm(dt, hidden, w->g_attn, xn, s.M, s.H, eps, stream_h);
     if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
     LL_CHECK_HIP(mark(), "hipEventRecord");
-    // 2. fused QKV projection
-    e = launch_gemm(dt, EPI_STORE, xn, w->w_qkv, qkv, nullptr, s.M, s.qkvd, s.H, gws, gbytes, stream_h);
-    if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
-    LL_CHECK_HIP(mark(), "hipEventRecord");
-    // 3. attention (RoPE applied to q and k as they are loaded)
-    if (decode) {
-        e = launch_attn_decode(dt, qkv, position_ids, &tab, cfg->rope.interleaved, k_cache, v_cache, ctx, o,
-                               static_cast<int>(B), static_cast<int>(s.nh), static_cast<int>(s.nkv),
-                               static_cast<int>(s.d), dws, dbytes, stream_h);
+    // 2. fused QKV projection; q and k are rotated in its epilogue (or by a rotation pass when the
+    //    head layout does not allow the fused form), so attention reads rotated q and k
+    RopeEpi re;
+    re.pos = position_ids;
+    re.tab = tab;
+    re.rope_cols = static_cast<int>((s.nh + s.nkv) * s.d);
+    re.d = static_cast<int>(s.d);
+    re.interleaved = cfg->rope.interleaved;
+    if (gemm_rope_fusable(dt, s.M, re.d)) {
+        e = launch_gemm(dt, EPI_ROPE, xn, w->w_qkv, qkv, nullptr, s.M, s.qkvd, s.H, gws, gbytes, stream_h, &re);
+        if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
     } else {
-        e = launch_attn_prefill(dt, qkv, position_ids, &tab, cfg->rope.interleaved, o, k_cache, v_cache, ctx,
-                                static_cast<int>(B), static_cast<int>(S), static_cast<int>(s.nh),
-                                static_cast<int>(s.nkv), static_cast<int>(s.d), stream_h);
+        e = launch_gemm(dt, EPI_STORE, xn, w->w_qkv, qkv, nullptr, s.M, s.qkvd, s.H, gws, gbytes, stream_h);
+        if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
+        e = launch_rope_apply(dt, qkv, position_ids, tab, s.M, static_cast<int>(s.nh), static_cast<int>(s.nkv),
+                              re.d, re.interleaved, stream_h);
+        if (e != hipSuccess) return hip_fail(e, "rope launch");
+    }
+    LL_CHECK_HIP(mark(), "hipEventRecord");
+    // 3. attention on rotated q and k
+    if (decode) {
+        e = launch_attn_decode(dt, qkv, position_ids, nullptr, 0, k_cache, v_cache, ctx, o, static_cast<int>(B),
+                               static_cast<int>(s.nh), static_cast<int>(s.nkv), static_cast<int>(s.d), dws, dbytes,
+                               stream_h);
+    } else {
+        e = launch_attn_prefill(dt, qkv, position_ids, nullptr, 0, o, k_cache, v_cache, ctx, static_cast<int>(B),
+                                static_cast<int>(S), static_cast<int>(s.nh), static_cast<int>(s.nkv),
+                                static_cast<int>(s.d), stream_h);
     }
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     LL_CHECK_HIP(mark(), "hipEventRecord");

@@ -33,6 +33,7 @@
 namespace ll {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSlack = 8.f;  // lazy-rescale threshold of the prefill kernel, in log2 units
 
 // ------------------------------------------------------------------ RoPE helpers (device)
 // Rotate the 8 values f[] (dims d0 .. d0+7 of a head) given their partners g[] (dims d0 + d/2 ..),
@@ -130,6 +131,9 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_mfma_kernel(
         }
 #pragma unroll
         for (int k = 0; k < C::KC32; ++k) {
+            // fold log2(e)/sqrt(d) into q: the scores come out in log2 units, ready for exp2
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[k][e] *= scale_log2;
             uint4 u = pack8(f[k]);
             if (qi >= S) u = make_uint4(0, 0, 0, 0);
             qfr[qf][k] = __builtin_bit_cast(bf16x8, u);
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_mfma_kernel(
             for (int kf = 0; kf < 4; ++kf)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float v = sacc[kf][qf][r] * scale_log2;
+                    float v = sacc[kf][qf][r];
                     if (last) {
                         const int key = kt * C::BKV + kf * 16 + 4 * lgrp + r;
                         if (key > qi || key >= S) v = -INFINITY;
@@ -287,9 +291,10 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_mfma_kernel(
                 }
             mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mnew = fmaxf(m_i[qf], mx);
-            const float alpha = exp2f(m_i[qf] - mnew);
-            m_i[qf] = mnew;
+            // the reference max moves only when the tile max exceeds it by more than kSlack (log2
+            // units), so P stays <= 2^kSlack and the O rescale is skipped while no column moves
+            const float mnew = (mx > m_i[qf] + kSlack) ? mx : m_i[qf];
+            const bool moved = mnew != m_i[qf];
             float ls = 0.f;
             float p[4][4];
 #pragma unroll
@@ -299,9 +304,14 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_mfma_kernel(
                     p[kf][r] = exp2f(s[kf][r] - mnew);
                     ls += p[kf][r];
                 }
-            l_i[qf] = l_i[qf] * alpha + ls;
+            if (__any(moved)) {
+                const float alpha = exp2f(m_i[qf] - mnew);
+                l_i[qf] *= alpha;
 #pragma unroll
-            for (int a = 0; a < C::DF; ++a) oacc[a][qf] *= alpha;
+                for (int a = 0; a < C::DF; ++a) oacc[a][qf] *= alpha;
+            }
+            m_i[qf] = mnew;
+            l_i[qf] += ls;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 uint4 u;

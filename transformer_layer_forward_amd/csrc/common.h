@@ -60,7 +60,17 @@ __device__ __forceinline__ int64_t clamp_pos(int64_t p, int64_t rows) {
     return p < 0 ? 0 : (p >= rows ? rows - 1 : p);
 }
 
-enum Epi { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SILU = 2 };
+enum Epi { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SILU = 2, EPI_ROPE = 3 };
+
+// RoPE applied in the QKV projection's epilogue: columns [0, rope_cols) are q and k heads of size d,
+// rotated at position pos[row] (the packed row layout Q|K|V keeps every head inside rope_cols).
+struct RopeEpi {
+    const int64_t* pos;
+    RopeTab tab;
+    int rope_cols;
+    int d;
+    int interleaved;
+};
 
 // ---- launchers (host) ----
 hipError_t launch_rmsnorm(int dtype, const void* x, const void* g, void* y, int64_t rows, int64_t H, float eps,
@@ -70,7 +80,9 @@ hipError_t launch_rope_apply(int dtype, void* qkv, const int64_t* pos, RopeTab t
 // C[M, ldc] (epi) = X[M, K] . W^T; W has N rows (EPI_SILU: 2*inter rows, N = inter output columns).
 size_t gemm_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K, int epi);
 hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C, const void* R, int64_t M,
-                       int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t st);
+                       int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t st, const RopeEpi* re = nullptr);
+// whether EPI_ROPE can be fused for this projection (else the caller rotates with launch_rope_apply)
+bool gemm_rope_fusable(int dtype, int64_t M, int d);
 hipError_t launch_attn_prefill(int dtype, const void* qkv, const int64_t* pos, const RopeTab* tab, int interleaved,
                                void* o, void* kc, void* vc, int64_t ctx, int B, int S, int nh, int nkv, int d,
                                hipStream_t st);

@@ -7,7 +7,9 @@
 // tile over K in steps of 64. Both operands are K-contiguous, so global->LDS copies are 16-byte
 // row chunks; LDS rows are XOR-swizzled per 16-byte chunk so that the 16 lanes of a
 // matrix-core operand read (16 rows, same chunk) hit distinct banks. Two LDS stages: the next
-// K-step is fetched into registers while the current one feeds v_mfma_f32_16x16x32_bf16.
+// K-step is copied global -> LDS with global_load_lds_dwordx4 (no register staging; when K is not a
+// multiple of 64 a register-staged copy with zero-filled K tails is used instead) while the
+// current one feeds v_mfma_f32_16x16x32_bf16, operand reads interleaved with the matrix ops.
 // The weight tile is the MFMA A operand and the token tile the B operand, so each lane ends with
 // 4 consecutive output columns of one token row (8-byte stores).
 // Tiles are numbered so that each XCD (blocks are dealt round-robin to the 8 XCDs) works on a
@@ -29,7 +31,8 @@ namespace ll {
 // ------------------------------------------------------------------ bf16, large M
 constexpr int GB_M = 256, GB_N = 256, GB_K = 64;
 constexpr int GB_WAVES_N = 2, GB_WAVES_M = 4;
-constexpr int GB_THREADS = 64 * GB_WAVES_N * GB_WAVES_M;  // 512
+constexpr int GB_NWAVES = GB_WAVES_N * GB_WAVES_M;
+constexpr int GB_THREADS = 64 * GB_NWAVES;               // 512
 constexpr int GB_WTN = GB_N / GB_WAVES_N;                 // 128 weight rows per wave
 constexpr int GB_WTM = GB_M / GB_WAVES_M;                 // 64 tokens per wave
 constexpr int GB_FN = GB_WTN / 16, GB_FM = GB_WTM / 16;   // 8 x 4 fragments
@@ -40,10 +43,13 @@ constexpr int GB_LOADS = (GB_M * GB_K / 8) / GB_THREADS;  // 16-byte chunks per 
 // physical 16-byte chunk of logical chunk c in LDS row r (rows are 8 chunks = 128 bytes)
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int EPI>
+// RD: head size of the fused RoPE epilogue (EPI_ROPE only; 32, 64 or 128 so that every wave's
+// 128 output columns hold whole heads and a fragment's rotation partner sits in the same lane).
+template <int EPI, bool DIRECT, int RD = 0>
 __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_big_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, const bf16_t* __restrict__ R,
-    int M, int N, int K, int tiles_m, int tiles_n) {
+    int M, int N, int K, int tiles_m, int tiles_n, const int64_t* __restrict__ rpos, const float2* __restrict__ rcs,
+    int64_t rrows, int rope_cols, int ril) {
     extern __shared__ __align__(16) bf16_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave % GB_WAVES_N, wm = wave / GB_WAVES_N;
@@ -88,7 +94,40 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_big_kernel(
         wsrc[i] = W + static_cast<int64_t>(wok[i] ? grow : 0) * K + cch * 8;
         wdst[i] = (GB_M + r) * GB_K + ((cch ^ swz8(r)) << 3);
     }
-    uint4 xr[GB_LOADS], wr[GB_LOADS];
+    // direct path (K % 64 == 0): each wave copies 1 KiB blocks (8 rows x 128 B) global -> LDS with
+    // global_load_lds_dwordx4; lane l lands at block + 16 l, so lane l fetches the logical chunk that the
+    // swizzle puts at physical chunk l % 8 of row l / 8. Rows past M or N read a clamped valid row;
+    // their results are never stored.
+    constexpr int GB_DJ = 64 / GB_NWAVES;
+    const bf16_t* dsrc[GB_DJ];
+    if constexpr (DIRECT) {
+#pragma unroll
+        for (int j = 0; j < GB_DJ; ++j) {
+            const int row = (j * GB_NWAVES + wave) * 8 + (lane >> 3);  // 0..511: X rows then W rows
+            const int r = row & 255;
+            const int c = (lane & 7) ^ swz8(r);
+            if (row < 256) {
+                dsrc[j] = X + static_cast<int64_t>(min(m0 + r, M - 1)) * K + c * 8;
+            } else {
+                int grow;
+                if (EPI == EPI_SILU) {
+                    const int blk = r >> 4, col = min(n0 + (blk >> 1) * 16 + (r & 15), N - 1);
+                    grow = (blk & 1) ? N + col : col;
+                } else {
+                    grow = min(n0 + r, N - 1);
+                }
+                dsrc[j] = W + static_cast<int64_t>(grow) * K + c * 8;
+            }
+        }
+    }
+#define GB_DISSUE(k0, stage)                                                                                  \
+    _Pragma("unroll") for (int jj_ = 0; jj_ < GB_DJ; ++jj_) {                                                 \
+        __builtin_amdgcn_global_load_lds(                                                                     \
+            (const __attribute__((address_space(1))) void*)(dsrc[jj_] + (k0)),                                \
+            (__attribute__((address_space(3))) void*)(smem + (stage) * GB_STAGE + (jj_ * GB_NWAVES + wave) * 8 * GB_K), \
+            16, 0, 0);                                                                                        \
+    }
+    uint4 xr[DIRECT ? 1 : GB_LOADS], wr[DIRECT ? 1 : GB_LOADS];
 #define GB_GLOAD(k0)                                                                              \
     do {                                                                                          \
         const bool kok_ = ((k0) + cch * 8) < K;                                                   \
@@ -133,32 +172,59 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_big_kernel(
     }
 
     const int nk = (K + GB_K - 1) / GB_K;
-    GB_GLOAD(0);
-    GB_SSTORE(0);
+    if constexpr (DIRECT) {
+        GB_DISSUE(0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+    } else {
+        GB_GLOAD(0);
+        GB_SSTORE(0);
+    }
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < nk) GB_GLOAD((kt + 1) * GB_K);
+        if (kt + 1 < nk) {
+            if constexpr (DIRECT) {
+                GB_DISSUE((kt + 1) * GB_K, cur ^ 1);
+            } else {
+                GB_GLOAD((kt + 1) * GB_K);
+            }
+        }
         const bf16_t* s = smem + cur * GB_STAGE;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             bf16x8 av[GB_FN], bv[GB_FM];
 #pragma unroll
-            for (int f = 0; f < GB_FN; ++f) av[f] = *reinterpret_cast<const bf16x8*>(s + aoff[h][f]);
-#pragma unroll
             for (int f = 0; f < GB_FM; ++f) bv[f] = *reinterpret_cast<const bf16x8*>(s + boff[h][f]);
+#pragma unroll
+            for (int f = 0; f < GB_FN; ++f) av[f] = *reinterpret_cast<const bf16x8*>(s + aoff[h][f]);
 #pragma unroll
             for (int a = 0; a < GB_FN; ++a)
 #pragma unroll
                 for (int b = 0; b < GB_FM; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+            // schedule: all token-operand reads plus the first weight read, then each further weight read
+            // interleaved with the matrix ops of the fragment before it
+            __builtin_amdgcn_sched_group_barrier(0x100, GB_FM + 1, 0);
+#pragma unroll
+            for (int a = 0; a < GB_FN - 1; ++a) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, GB_FM, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, GB_FM, 0);
         }
-        if (kt + 1 < nk) GB_SSTORE(cur ^ 1);
+        if (kt + 1 < nk) {
+            if constexpr (DIRECT) {
+                __builtin_amdgcn_s_waitcnt(0);
+            } else {
+                GB_SSTORE(cur ^ 1);
+            }
+        }
         __syncthreads();
     }
 
 #undef GB_GLOAD
 #undef GB_SSTORE
+#undef GB_DISSUE
 
     // ---- epilogue: lane holds rows n = base + 4*lgrp + {0..3} of token m = ... + lrow
     const int ldc = N;
@@ -168,6 +234,35 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_big_kernel(
         const int m = m0 + wm * GB_WTM + b * 16 + lrow;
         if (m >= M) continue;
         bf16_t* crow = C + static_cast<int64_t>(m) * ldc;
+        if constexpr (EPI == EPI_ROPE) {
+            // rotate q/k columns in registers: fragment a starts at head offset (a*16) % RD
+            const float2* cs_row = rcs + clamp_pos(rpos[m], rrows) * (RD / 2);
+#pragma unroll
+            for (int a = 0; a < GB_FN; ++a) {
+                if (n0 + wn * GB_WTN + a * 16 >= rope_cols) continue;  // value columns
+                constexpr int PO = RD / 32;                            // partner fragment (half-split)
+                const int jh = (a * 16) % RD;
+                if (!ril) {
+                    if (jh < RD / 2) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float2 t = cs_row[jh + 4 * lgrp + r];
+                            const float x = acc[a][b][r], y = acc[(a + PO) % GB_FN][b][r];
+                            acc[a][b][r] = x * t.x - y * t.y;
+                            acc[(a + PO) % GB_FN][b][r] = y * t.x + x * t.y;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; r += 2) {
+                        const float2 t = cs_row[(jh + 4 * lgrp + r) >> 1];
+                        const float x = acc[a][b][r], y = acc[a][b][r + 1];
+                        acc[a][b][r] = x * t.x - y * t.y;
+                        acc[a][b][r + 1] = y * t.x + x * t.y;
+                    }
+                }
+            }
+        }
         if (EPI == EPI_SILU) {
 #pragma unroll
             for (int a = 0; a < GB_FN; a += 2) {
@@ -300,7 +395,9 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_bf16_skinny_kernel(const bf16
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __restrict__ P, bf16_t* __restrict__ C,
                                                                  const bf16_t* __restrict__ R, int M, int N, int Nw,
-                                                                 int splits) {
+                                                                 int splits, const int64_t* __restrict__ rpos,
+                                                                 const float2* __restrict__ rcs, int64_t rrows,
+                                                                 int rope_cols, int rd, int ril) {
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= static_cast<int64_t>(M) * N) return;
     const int m = static_cast<int>(idx / N), n = static_cast<int>(idx - static_cast<int64_t>(m) * N);
@@ -309,6 +406,25 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __
         const float* prow = P + (static_cast<int64_t>(k) * M + m) * Nw;
         s += prow[n];
         if (EPI == EPI_SILU) u += prow[N + n];
+    }
+    if (EPI == EPI_ROPE && n < rope_cols) {
+        // rotation partner of column n within its head (half-split pairs (j, j+d/2) or pairs (2j, 2j+1))
+        const int j = n % rd;
+        int partner, t;
+        float sign;
+        if (ril) {
+            partner = n ^ 1;
+            t = j >> 1;
+            sign = (j & 1) ? 1.f : -1.f;
+        } else {
+            partner = j < rd / 2 ? n + rd / 2 : n - rd / 2;
+            t = j < rd / 2 ? j : j - rd / 2;
+            sign = j < rd / 2 ? -1.f : 1.f;
+        }
+        float y = 0.f;
+        for (int k = 0; k < splits; ++k) y += P[(static_cast<int64_t>(k) * M + m) * Nw + partner];
+        const float2 c = rcs[clamp_pos(rpos[m], rrows) * (rd / 2) + t];
+        s = s * c.x + sign * y * c.y;
     }
     if (EPI == EPI_SILU) s = s / (1.f + __expf(-s)) * u;
     if (EPI == EPI_RESIDUAL) s += bf2f(R[idx]);
@@ -383,26 +499,34 @@ size_t gemm_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K, int epi)
     return static_cast<size_t>(splits) * M * Nw * sizeof(float);
 }
 
-template <int EPI>
-static hipError_t big_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N, int64_t K,
-                             hipStream_t st) {
+template <int EPI, bool DIRECT, int RD>
+static hipError_t big_launch_t(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N, int64_t K,
+                               hipStream_t st, const RopeEpi* re) {
     static bool attr = [] {
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_big_kernel<EPI>),
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_big_kernel<EPI, DIRECT, RD>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, GB_LDS_BYTES) == hipSuccess;
     }();
     if (!attr) return hipErrorInvalidConfiguration;
     const int ncols = EPI == EPI_SILU ? GB_N / 2 : GB_N;
     const int tm = static_cast<int>((M + GB_M - 1) / GB_M), tn = static_cast<int>((N + ncols - 1) / ncols);
-    hipLaunchKernelGGL(gemm_bf16_big_kernel<EPI>, dim3(tm * tn), dim3(GB_THREADS), GB_LDS_BYTES, st,
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, DIRECT, RD>), dim3(tm * tn), dim3(GB_THREADS), GB_LDS_BYTES, st,
                        static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), static_cast<bf16_t*>(C),
                        static_cast<const bf16_t*>(R), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tm,
-                       tn);
+                       tn, re ? re->pos : nullptr, re ? re->tab.cs : nullptr, re ? re->tab.rows : 1,
+                       re ? re->rope_cols : 0, re ? re->interleaved : 0);
     return hipGetLastError();
+}
+
+template <int EPI, int RD = 0>
+static hipError_t big_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N, int64_t K,
+                             hipStream_t st, const RopeEpi* re = nullptr) {
+    if (K % GB_K == 0) return big_launch_t<EPI, true, RD>(X, W, C, R, M, N, K, st, re);
+    return big_launch_t<EPI, false, RD>(X, W, C, R, M, N, K, st, re);
 }
 
 template <int EPI>
 static hipError_t skinny_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N, int64_t K,
-                                void* ws, hipStream_t st) {
+                                void* ws, hipStream_t st, const RopeEpi* re = nullptr) {
     const int64_t Nw = EPI == EPI_SILU ? 2 * N : N;
     int splits, kchunk;
     skinny_plan(Nw, K, &splits, &kchunk);
@@ -415,7 +539,9 @@ static hipError_t skinny_launch(const void* X, const void* W, void* C, const voi
     const int64_t total = M * N;
     hipLaunchKernelGGL(gemm_splitk_reduce_kernel<EPI>, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
                        st, static_cast<const float*>(ws), static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R),
-                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(Nw), splits);
+                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(Nw), splits,
+                       re ? re->pos : nullptr, re ? re->tab.cs : nullptr, re ? re->tab.rows : 1,
+                       re ? re->rope_cols : 0, re ? re->d : 2, re ? re->interleaved : 0);
     return hipGetLastError();
 }
 
@@ -429,9 +555,16 @@ static hipError_t f32_launch(const void* X, const void* W, void* C, const void* 
     return hipGetLastError();
 }
 
+bool gemm_rope_fusable(int dtype, int64_t M, int d) {
+    if (dtype != LL_BF16) return false;
+    if (use_skinny(M)) return d >= 2 && d % 2 == 0;
+    return d == 32 || d == 64 || d == 128;
+}
+
 hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N,
-                       int64_t K, void* ws, size_t ws_bytes, hipStream_t st) {
+                       int64_t K, void* ws, size_t ws_bytes, hipStream_t st, const RopeEpi* re) {
     if (M == 0 || N == 0) return hipSuccess;
+    if (epi == EPI_ROPE && (!re || !gemm_rope_fusable(dtype, M, re->d))) return hipErrorInvalidValue;
     if (dtype == LL_F32) {
         switch (epi) {
             case EPI_STORE: return f32_launch<EPI_STORE>(X, W, C, R, M, N, K, st);
@@ -444,12 +577,17 @@ hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C
         switch (epi) {
             case EPI_STORE: return skinny_launch<EPI_STORE>(X, W, C, R, M, N, K, ws, st);
             case EPI_RESIDUAL: return skinny_launch<EPI_RESIDUAL>(X, W, C, R, M, N, K, ws, st);
+            case EPI_ROPE: return skinny_launch<EPI_ROPE>(X, W, C, R, M, N, K, ws, st, re);
             default: return skinny_launch<EPI_SILU>(X, W, C, R, M, N, K, ws, st);
         }
     }
     switch (epi) {
         case EPI_STORE: return big_launch<EPI_STORE>(X, W, C, R, M, N, K, st);
         case EPI_RESIDUAL: return big_launch<EPI_RESIDUAL>(X, W, C, R, M, N, K, st);
+        case EPI_ROPE:
+            if (re->d == 128) return big_launch<EPI_ROPE, 128>(X, W, C, R, M, N, K, st, re);
+            if (re->d == 64) return big_launch<EPI_ROPE, 64>(X, W, C, R, M, N, K, st, re);
+            return big_launch<EPI_ROPE, 32>(X, W, C, R, M, N, K, st, re);
         default: return big_launch<EPI_SILU>(X, W, C, R, M, N, K, st);
     }
 }
