@@ -31,8 +31,84 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="time the oracle on the first N tokens of sequence 0 only (0: the whole workload)")
+    ap.add_argument("--rocpd-summary", metavar="DB",
+                    help="print per-kernel duration statistics from a rocprofv3 results database and exit")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="combine rocprofv3 FETCH_SIZE and WRITE_SIZE databases (bench + copy calibration) "
+                         "into the per-launch HBM traffic record of the gate_up kernel and exit")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the bench, run a plain 1 GiB device-to-device copy 3 times (counter calibration)")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration() -> None:
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes x3", flush=True)
+
+
+def pmc_summary(fetch_db: str, write_db: str) -> None:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the gate_up GEMM, scaled by what the same counters read
+    for the plain copy (which must move COPY_BYTES each way)."""
+    import sqlite3
+
+    def per_kernel(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute("select name, dispatch_id, sum(counter_value) from pmc_events where counter_name = ? "
+                           "group by dispatch_id", (counter,)).fetchall()
+        out = {}
+        for name, _, v in rows:
+            out.setdefault(name, []).append(v)
+        return out
+
+    f = per_kernel(fetch_db, "FETCH_SIZE")
+    w = per_kernel(write_db, "WRITE_SIZE")
+
+    def pick(d, key):
+        vals = [v for name, vs in d.items() if key in name for v in vs]
+        return sorted(vals)[len(vals) // 2] if vals else None  # median dispatch
+
+    def pick_copy(d):
+        # the 1 GiB device copies are the largest copy-kernel dispatches of the run
+        vals = sorted(v for name, vs in d.items() if "copyBuffer" in name for v in vs)
+        return vals[-1] if vals else None
+
+    gu_key = "gemm_bf16_big_kernel<2"
+    f_copy, w_copy = pick_copy(f), pick_copy(w)
+    f_gu, w_gu = pick(f, gu_key), pick(w, gu_key)
+    kib = COPY_BYTES / 1024.0
+    f_scale = kib / f_copy if f_copy else None
+    w_scale = kib / w_copy if w_copy else None
+    rec = {"gemm_source_sha256_16": gemm_source_hash(), "fetch_kib_per_launch_raw": f_gu,
+           "write_kib_per_launch_raw": w_gu, "copy_fetch_kib_raw": f_copy, "copy_write_kib_raw": w_copy,
+           "copy_bytes": COPY_BYTES, "fetch_scale": f_scale, "write_scale": w_scale}
+    if None not in (f_gu, w_gu, f_scale, w_scale):
+        rec["hbm_bytes_per_launch"] = round((f_gu * f_scale + w_gu * w_scale) * 1024.0)
+    print(json.dumps(rec, indent=1))
+
+
+def rocpd_summary(db: str) -> None:
+    """Per-kernel calls / average / min / max durations (microseconds) from a rocprofv3 SQLite database."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+                       "from kernels group by name order by sum(duration) desc").fetchall()
+    total = sum(r[5] for r in rows) or 1
+    print("| kernel | calls | avg us | min us | max us | share |")
+    print("|---|---|---|---|---|---|")
+    for name, n, avg, lo, hi, tot in rows:
+        print(f"| `{name[:110]}` | {n} | {avg / 1e3:.1f} | {lo / 1e3:.1f} | {hi / 1e3:.1f} | {100 * tot / total:.1f}% |")
 
 
 def gemm_source_hash() -> str:
@@ -52,32 +128,41 @@ def measured_traffic():
 
 
 def cpu_baseline(cfg, W_bits, x_bits, tokens):
-    """fp64 oracle on sequence 0, tokens 0..tokens-1 of the same workload (a bounded sample)."""
+    """fp64 oracle timed on the host: the whole workload (tokens = 0) or, to bound the time on a slow host,
+    sequence 0 truncated to its first `tokens` tokens."""
     import numpy as np
 
     from oracle import ref
-    from synth_inputs import to_f64
+    from synth_inputs import scaled, to_f64
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:  # noqa: BLE001
         threads = os.cpu_count() or 1
     W = {k: to_f64(v, "bf16") for k, v in W_bits.items()}
-    x = to_f64(x_bits[:1, :tokens], "bf16")
-    pos = np.arange(tokens, dtype=np.int64)[None, :]
-    from synth_inputs import scaled
-    c = scaled(cfg, B=1, S=tokens)
+    if tokens <= 0 or tokens >= cfg.S:
+        c, x = cfg, to_f64(x_bits, "bf16")
+        sample = f"the whole {WORKLOAD} workload (B={cfg.B}, S={cfg.S}, {cfg.B * cfg.S} tokens)"
+    else:
+        c, x = scaled(cfg, B=1, S=tokens), to_f64(x_bits[:1, :tokens], "bf16")
+        sample = (f"{WORKLOAD} layer on sequence 0, tokens 0..{tokens - 1} ({tokens} of {cfg.B * cfg.S} tokens; "
+                  f"causal attention over a {tokens}-token prefix instead of up to {cfg.S})")
+    pos = np.broadcast_to(np.arange(c.S, dtype=np.int64), (c.B, c.S))
     t0 = time.perf_counter()
-    ref.layer_prefill(c, W, x, pos, tokens)
+    ref.layer_prefill(c, W, x, pos, c.S)
     dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{WORKLOAD} layer on sequence 0, tokens 0..{tokens - 1} ({tokens} of {cfg.B * cfg.S} tokens; "
-                      f"causal attention over a {tokens}-token prefix instead of up to {cfg.S}), fp64 NumPy, "
-                      f"{dt:.1f} s"}
+    return {"value": c.B * c.S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{sample}, fp64 NumPy, {dt:.1f} s"}
 
 
 def main():
     args = parse()
+    if args.rocpd_summary:
+        rocpd_summary(args.rocpd_summary)
+        return
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (each MI355X runs the whole "
               "layer on its own sequences; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
@@ -169,6 +254,8 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, W_bits, x_bits, args.cpu_sample_tokens)
     print(json.dumps(rec), flush=True)
+    if args.copy_calibration:
+        copy_calibration()
 
 
 if __name__ == "__main__":

@@ -35,6 +35,10 @@ namespace ll {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.f;  // lazy-rescale threshold of the prefill kernel, in log2 units
 
+// 2^x with the hardware v_exp_f32 (no denormal range fix-up): exp2(-inf) = 0, and results below
+// 2^-126 (which only arise for weights negligible against the running sum) flush to 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ------------------------------------------------------------------ RoPE helpers (device)
 // Rotate the 8 values f[] (dims d0 .. d0+7 of a head) given their partners g[] (dims d0 + d/2 ..),
 // half-split pairing: x' = x c - y s, y' = y c + x s, with j = d0 + e.
@@ -76,8 +80,11 @@ __device__ __forceinline__ int k_phys(int r, int ch) {
     if constexpr (D == 128) return ch ^ (r & 15);
     else return ch ^ ((r & 7) ^ ((r >> 3) & 1));
 }
-// physical 8-byte unit of V^T row r (16 units of 4 keys per 64-key row)
-__device__ __forceinline__ int v_phys(int r, int u) { return u ^ (r & 15); }
+// V^T rows (one per head dimension, 64 keys = 128 B) hold 8 chunks of 16 B. Chunk 4t + g holds keys
+// 32t + 4g .. +3 (low 8 B) and 32t + 16 + 4g .. +3 (high 8 B): exactly the 8 keys one lane of the
+// P V operand needs, so a fragment is one 16-byte read. Chunks are XOR-swizzled by row so the 16
+// lanes of a read (16 rows, same chunk) hit distinct banks.
+__device__ __forceinline__ int vt_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 template <int D, int HPB, bool ROPE, bool IL>
 __global__ __launch_bounds__(128 * HPB) void attn_prefill_mfma_kernel(
@@ -150,30 +157,44 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_mfma_kernel(
     const bf16_t* kbase = qkv_b + static_cast<int64_t>(nh) * D + static_cast<int64_t>(c) * D;
     const bf16_t* vbase = qkv_b + static_cast<int64_t>(nh + nkv) * D + static_cast<int64_t>(c) * D;
 
+    // per-thread source rows of the tile at key 0 (the tile at key0 adds key0 * rs)
+    const bf16_t* ksrc[KJ];
+    const bf16_t* vsrc[VJ];
+#pragma unroll
+    for (int i = 0; i < KJ; ++i) {
+        const int job = tid + i * NT;
+        const int r = job / (C::KCH / 2), ch = job % (C::KCH / 2);
+        ksrc[i] = kbase + static_cast<int64_t>(r) * rs + (IL ? 2 * ch : ch) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < VJ; ++i) {
+        const int job = tid + i * NT;
+        vsrc[i] = vbase + static_cast<int64_t>((job / C::KCH) * 4) * rs + (job % C::KCH) * 8;
+    }
+
 #define AP_LOAD(kt)                                                                                        \
     do {                                                                                                   \
         const int key0_ = (kt) * C::BKV;                                                                   \
+        const int64_t toff_ = static_cast<int64_t>(key0_) * rs;                                            \
+        /* keys past S (only in the last, masked tile) read the clamped row S-1: finite values, */      \
+        /* masked out of the scores, multiplied by zero weights                                  */      \
         _Pragma("unroll") for (int i = 0; i < KJ; ++i) {                                                   \
             const int job = tid + i * NT;                                                                  \
-            const int r = job / (C::KCH / 2), ch = job % (C::KCH / 2);                                     \
-            const int key = key0_ + r;                                                                     \
-            kr[i][0] = zero;                                                                               \
-            kr[i][1] = zero;                                                                               \
-            if (job < KJOBS && key < S) {                                                                  \
-                const bf16_t* p = kbase + static_cast<int64_t>(key) * rs;                                  \
-                const int c0 = IL ? 2 * ch : ch, c1 = IL ? 2 * ch + 1 : ch + C::KCH / 2;                   \
-                kr[i][0] = *reinterpret_cast<const uint4*>(p + c0 * 8);                                    \
-                kr[i][1] = *reinterpret_cast<const uint4*>(p + c1 * 8);                                    \
+            const int key = key0_ + job / (C::KCH / 2);                                                    \
+            if (job < KJOBS) {                                                                             \
+                const bf16_t* p = ksrc[i] + toff_ - (key < S ? 0 : static_cast<int64_t>(key - S + 1) * rs); \
+                kr[i][0] = *reinterpret_cast<const uint4*>(p);                                             \
+                kr[i][1] = *reinterpret_cast<const uint4*>(p + (IL ? 8 : 8 * (C::KCH / 2)));               \
             }                                                                                              \
         }                                                                                                  \
         _Pragma("unroll") for (int i = 0; i < VJ; ++i) {                                                   \
             const int job = tid + i * NT;                                                                  \
-            const int r4 = job / C::KCH, ch = job % C::KCH;                                                \
+            const bf16_t* p = vsrc[i] + toff_;                                                             \
             _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                                \
-                const int key = key0_ + r4 * 4 + t;                                                        \
-                vr[i][t] = zero;                                                                           \
-                if (job < VJOBS && key < S)                                                                \
-                    vr[i][t] = *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(key) * rs + ch * 8); \
+                const int key = key0_ + (job / C::KCH) * 4 + t;                                            \
+                if (job < VJOBS)                                                                           \
+                    vr[i][t] = *reinterpret_cast<const uint4*>(                                            \
+                        p + static_cast<int64_t>(key < S ? t : S - 1 - (key0_ + (job / C::KCH) * 4)) * rs); \
             }                                                                                              \
         }                                                                                                  \
     } while (0)
@@ -221,12 +242,13 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_mfma_kernel(
                 const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[i][1]);                         \
                 const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[i][2]);                         \
                 const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[i][3]);                         \
+                const int vq_ = (r4 >> 3) * 4 + (r4 & 3), vh_ = ((r4 >> 2) & 1) * 4;                       \
                 _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                            \
                     const int sh = (e & 1) * 16;                                                           \
                     const uint32_t k0 = (w0[e >> 1] >> sh) & 0xffffu, k1 = (w1[e >> 1] >> sh) & 0xffffu;  \
                     const uint32_t k2 = (w2[e >> 1] >> sh) & 0xffffu, k3 = (w3[e >> 1] >> sh) & 0xffffu;  \
                     const int dr = ch * 8 + e;                                                             \
-                    *reinterpret_cast<uint2*>(&sV[st][dr * C::BKV + v_phys(dr, r4) * 4]) =                 \
+                    *reinterpret_cast<uint2*>(&sV[st][dr * C::BKV + ((vq_ ^ vt_swz(dr)) << 3) + vh_]) =    \
                         make_uint2(k0 | (k1 << 16), k2 | (k3 << 16));                                      \
                 }                                                                                          \
                 if (diag_) {                                                                               \
@@ -301,11 +323,11 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_mfma_kernel(
             for (int kf = 0; kf < 4; ++kf)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    p[kf][r] = exp2f(s[kf][r] - mnew);
+                    p[kf][r] = fast_exp2(s[kf][r] - mnew);
                     ls += p[kf][r];
                 }
             if (__any(moved)) {
-                const float alpha = exp2f(m_i[qf] - mnew);
+                const float alpha = fast_exp2(m_i[qf] - mnew);
                 l_i[qf] *= alpha;
 #pragma unroll
                 for (int a = 0; a < C::DF; ++a) oacc[a][qf] *= alpha;
@@ -328,9 +350,8 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_mfma_kernel(
 #pragma unroll
             for (int a = 0; a < C::DF; ++a) {
                 const int dr = a * 16 + lrow;
-                const uint2 lo = *reinterpret_cast<const uint2*>(&sV[st][dr * C::BKV + v_phys(dr, 8 * t + lgrp) * 4]);
-                const uint2 hi = *reinterpret_cast<const uint2*>(&sV[st][dr * C::BKV + v_phys(dr, 8 * t + 4 + lgrp) * 4]);
-                const bf16x8 vfr = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                const bf16x8 vfr =
+                    *reinterpret_cast<const bf16x8*>(&sV[st][dr * C::BKV + (((4 * t + lgrp) ^ vt_swz(dr)) << 3)]);
                 oacc[a][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, pfr[0][t], oacc[a][0], 0, 0, 0);
                 oacc[a][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, pfr[1][t], oacc[a][1], 0, 0, 0);
             }
@@ -629,14 +650,14 @@ __global__ __launch_bounds__(DEC_THREADS) void attn_decode_split_kernel(
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mnew = fmaxf(m_w, mx);
-        const float alpha = exp2f(m_w - mnew);
+        const float alpha = fast_exp2(m_w - mnew);
         m_w = mnew;
         float ls = 0.f;
 #pragma unroll
         for (int kf = 0; kf < 4; ++kf)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float pr = exp2f(s[kf][r] - mnew);
+                const float pr = fast_exp2(s[kf][r] - mnew);
                 ls += pr;
                 if (lrow < g) sP[wave][kf * 16 + 4 * lgrp + r][lrow] = pr;
             }
