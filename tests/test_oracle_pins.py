@@ -167,8 +167,10 @@ def test_rope_dynamic_ntk_reading():
     d=4, theta=1e4, factor=2, orig=100, L=200 gives base 1e4 * (2*2 - 1)^(4/2) = 9e4, f_1 = 1/300."""
     rc = RopeCfg(type="dynamic_ntk", theta=1e4, factor=2.0, original_max_pos=100)
     dft = ref.rope_frequencies(4, RopeCfg(theta=1e4), 0)
-    np.testing.assert_array_equal(ref.rope_frequencies(4, rc, 50), dft)
-    np.testing.assert_array_equal(ref.rope_frequencies(4, rc, 100), dft)
+    for L in (1, 50, 99, 100):                           # the threshold is L > orig, not L >= orig - 1
+        np.testing.assert_array_equal(ref.rope_frequencies(4, rc, L), dft)
+    # first length past the threshold: base 1e4 * (2*101/100 - 1)^2 = 1e4 * 1.02^2, f_1 = 1/102
+    np.testing.assert_allclose(ref.rope_frequencies(4, rc, 101), [1.0, 1.0 / 102.0], rtol=1e-14)
     np.testing.assert_allclose(ref.rope_frequencies(4, rc, 200), [1.0, 1.0 / 300.0], rtol=1e-14)
     np.testing.assert_allclose(brute.inv_freq(4, rc, 200), [1.0, 1.0 / 300.0], rtol=1e-14)
 
