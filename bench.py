@@ -6,7 +6,10 @@ Prints one JSON line: tokens/s, per-stage times from HIP events recorded by the 
 launch stream during the timed steps, the roofline position of the dominant kernel (the fused
 gate_up GEMM) and the fp64 CPU oracle timed on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+The headline run also times the 8B decode step (B=64 against 8192-slot KV caches, caches flushed before
+each call) and reports it under "decode" with its HBM GB/s.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -30,6 +33,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=WORKLOAD,
+                    choices=[WORKLOAD, "llama32_1b_prefill", "llama3_8b_long_llama3rope", "llama3_8b_decode"],
+                    help="the headline line is the 8B prefill; the others print the same record for that workload")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the cache-cold decode measurement that the headline run adds as \"decode\"")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="time the oracle on the first N tokens of sequence 0 only (0: the whole workload)")
@@ -155,6 +163,144 @@ def cpu_baseline(cfg, W_bits, x_bits, tokens):
             "sample": f"{sample}, fp64 NumPy, {dt:.1f} s"}
 
 
+def lib_config(L, cfg, torch):
+    rc = cfg.rope
+    rope = L.Rope(type=rc.type, theta=rc.theta, factor=rc.factor, low_freq_factor=rc.low_freq_factor,
+                  high_freq_factor=rc.high_freq_factor, original_max_pos=rc.original_max_pos,
+                  interleaved=rc.interleaved)
+    return L.LayerConfig(cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.intermediate, cfg.eps, rope,
+                         torch.bfloat16)
+
+
+def stage_ms(stages, key):
+    tot, n = stages[key]
+    return tot / n
+
+
+def gemm_flops_per_token(cfg):
+    return 2.0 * cfg.hidden * (cfg.qkv_dim + cfg.hidden + 2 * cfg.intermediate) + 2.0 * cfg.intermediate * cfg.hidden
+
+
+def weight_bytes(cfg):
+    return 2 * (cfg.hidden * (cfg.qkv_dim + cfg.hidden + 2 * cfg.intermediate) + cfg.intermediate * cfg.hidden
+                + 2 * cfg.hidden)
+
+
+def run_prefill(L, torch, np, cfg, W, args):
+    """K timed prefill layer calls back to back; returns (ms_per_step, stages, out)."""
+    from synth_inputs import make_hidden, make_prefill_positions
+    dev = "cuda:0"
+    x_bits = make_hidden(cfg, seed=0)
+    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    pos = torch.from_numpy(make_prefill_positions(cfg)).to(dev)
+    lc = lib_config(L, cfg, torch)
+    ws = torch.empty(L.layer_workspace_bytes(lc, cfg.B, cfg.S), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+    for _ in range(args.warmup):
+        L.llama_layer_forward(lc, W, x, pos, kv_seq_len=cfg.S, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    L.profile_begin(args.steps)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        L.llama_layer_forward(lc, W, x, pos, kv_seq_len=cfg.S, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = L.profile_end()
+    assert torch.isfinite(out.float()).all().item()
+    return wall * 1e3 / args.steps, stages, x_bits
+
+
+def decode_inputs(L, torch, np, cfg, W):
+    """Decode step inputs on the device: hidden [B,1,H], positions [B] integer-uniform on [1024, ctx),
+    and K/V caches [B, ctx, n_kv, d] of N(0,1) values drawn by torch's seeded device generator (the
+    caches are 2 GiB; their values do not change the work)."""
+    from synth_inputs import make_decode_positions, make_hidden
+    dev = "cuda:0"
+    x = torch.from_numpy(np.ascontiguousarray(make_hidden(cfg, seed=0)).view(np.int16)).to(dev).view(torch.bfloat16)
+    pos_np = make_decode_positions(cfg, seed=0)
+    pos = torch.from_numpy(pos_np).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(8)
+    shape = (cfg.B, cfg.ctx, cfg.n_kv_heads, cfg.head_dim)
+    kc = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    g.manual_seed(9)
+    vc = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    return x, pos, pos_np, kc, vc
+
+
+def decode_bytes(cfg, pos_np):
+    """Algorithmic HBM bytes of one decode layer call: every weight once, K and V of slots 0..pos_b of every
+    sequence, the new K/V slot writes, hidden in and out."""
+    kv_read = int(sum(int(p) + 1 for p in pos_np)) * cfg.n_kv_heads * cfg.head_dim * 2 * 2
+    kv_write = cfg.B * cfg.n_kv_heads * cfg.head_dim * 2 * 2
+    io = 2 * cfg.B * cfg.hidden * 2
+    return weight_bytes(cfg), kv_read, kv_write + io
+
+
+def run_decode(L, torch, np, cfg, W, steps, warmup, cold):
+    """Decode layer calls. cold=True: before each call 512 MiB of scratch is written (outside the timed
+    region) so that L2 and the Infinity Cache start cold, and each call is timed by HIP events on the
+    launch stream; the median is reported. cold=False: `steps` calls back to back, wall clock."""
+    dev = "cuda:0"
+    x, pos, pos_np, kc, vc = decode_inputs(L, torch, np, cfg, W)
+    lc = lib_config(L, cfg, torch)
+    ws = torch.empty(L.layer_workspace_bytes(lc, cfg.B, 1, cfg.ctx), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+
+    def call():
+        L.llama_layer_forward(lc, W, x, pos, kv_seq_len=cfg.ctx, k_cache=kc, v_cache=vc, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    L.profile_begin(steps)
+    if cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream()
+        times = []
+        for _ in range(steps):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        ms = times[len(times) // 2]
+        p10, p90 = times[len(times) // 10], times[(9 * len(times)) // 10]
+    else:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        p10 = p90 = None
+    stages = L.profile_end()
+    assert torch.isfinite(out.float()).all().item()
+    return ms, p10, p90, stages, pos_np
+
+
+def decode_summary(cfg, ms, p10, p90, stages, pos_np, cold):
+    wb, kvb, other = decode_bytes(cfg, pos_np)
+    tot = wb + kvb + other
+    attn_ms = stage_ms(stages, "attention")
+    gemm_ms = sum(stage_ms(stages, k) for k in ("qkv_proj", "o_proj_residual", "gate_up_silu", "down_residual"))
+    rec = {"workload": f"Llama-3-8B-shaped decode step, B={cfg.B} against [{cfg.B}, {cfg.ctx}, {cfg.n_kv_heads}, "
+                       f"{cfg.head_dim}] bf16 K/V caches, positions uniform on [1024, {cfg.ctx})",
+           "timing": "median of per-call HIP events, caches flushed before each call" if cold
+           else "back-to-back calls, wall clock",
+           "ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.B / (ms / 1e3), 1),
+           "algorithmic_bytes": tot, "hbm_gbs": round(tot / (ms / 1e3) / 1e9, 1),
+           "hbm_frac": round(tot / (ms / 1e3) / 1e9 / MI355X_HBM_GBS, 4),
+           "attention_kv_gbs": round(kvb / (attn_ms / 1e3) / 1e9, 1),
+           "gemm_weight_gbs": round(wb / (gemm_ms / 1e3) / 1e9, 1),
+           "stages_ms": {k: round(v[0] / v[1], 4) for k, v in stages.items()}}
+    if p10 is not None:
+        rec["p10_ms"], rec["p90_ms"] = round(p10, 4), round(p90, 4)
+    return rec
+
+
 def main():
     args = parse()
     if args.rocpd_summary:
@@ -172,71 +318,70 @@ def main():
     import torch
 
     import transformer_layer_forward_amd as L
-    from synth_inputs import CONFIGS, make_hidden, make_prefill_positions, make_weights
+    from synth_inputs import CONFIGS, make_weights
 
-    cfg = CONFIGS[WORKLOAD]
+    cfg = CONFIGS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
     W_bits = make_weights(cfg, seed=0)
-    x_bits = make_hidden(cfg, seed=0)
 
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     W = {k: to_dev(v) for k, v in W_bits.items()}
-    x = to_dev(x_bits)
-    pos = torch.from_numpy(make_prefill_positions(cfg)).to(dev)
     rc = cfg.rope
-    lc = L.LayerConfig(cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.intermediate, cfg.eps,
-                       L.Rope(type=rc.type, theta=rc.theta), torch.bfloat16)
-    ws = torch.empty(L.layer_workspace_bytes(lc, cfg.B, cfg.S), dtype=torch.uint8, device=dev)
-    out = torch.empty_like(x)
+    H, I, d = cfg.hidden, cfg.intermediate, cfg.head_dim
+    common = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "bf16"}
+    shape = {"hidden": H, "n_heads": cfg.n_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": d, "intermediate": I,
+             "rope": rc.type, "rope_theta": rc.theta}
 
-    for _ in range(args.warmup):
-        L.llama_layer_forward(lc, W, x, pos, kv_seq_len=cfg.S, out=out, workspace=ws)
-    torch.cuda.synchronize()
+    if cfg.decode:
+        ms, p10, p90, stages, pos_np = run_decode(L, torch, np, cfg, W, args.steps, args.warmup, cold=False)
+        summ = decode_summary(cfg, ms, p10, p90, stages, pos_np, cold=False)
+        wb, kvb, other = decode_bytes(cfg, pos_np)
+        attn_ms = stage_ms(stages, "attention")
+        rec = {"metric": "decode-step tokens/s (Llama-3-8B shape, bf16, B=64, KV cache) + HBM GB/s",
+               "value": summ["tokens_per_s"], "unit": "tokens/s", **common, "ms_per_step": round(ms, 4),
+               "data": "synthetic (seeded N(0,1) hidden and caches, N(0,0.02) weights, 1+N(0,0.1) gains)",
+               "config": {"workload": summ["workload"], "B": cfg.B, "ctx": cfg.ctx, **shape},
+               "hbm_gbs": summ["hbm_gbs"], "stages_ms": summ["stages_ms"],
+               "roofline": {"kernel": "attention stage (cache append + attn_decode_split_kernel + combine)",
+                            "bound": "hbm", "achieved": round(kvb / (attn_ms / 1e3) / 1e9, 1),
+                            "peak": MI355X_HBM_GBS, "unit": "GB/s",
+                            "frac": round(kvb / (attn_ms / 1e3) / 1e9 / MI355X_HBM_GBS, 4), "traffic": None},
+               "cold": decode_summary(cfg, *run_decode(L, torch, np, cfg, W, args.steps, 2, cold=True), cold=True),
+               "cpu_baseline": None}
+        print(json.dumps(rec), flush=True)
+        return
 
-    L.profile_begin(args.steps)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        L.llama_layer_forward(lc, W, x, pos, kv_seq_len=cfg.S, out=out, workspace=ws)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    stages = L.profile_end()
-    assert torch.isfinite(out.float()).all().item()
-
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step, stages, x_bits = run_prefill(L, torch, np, cfg, W, args)
     tokens = cfg.B * cfg.S
     value = tokens / (ms_per_step / 1e3)
-
-    M, H, I, d = cfg.M, cfg.hidden, cfg.intermediate, cfg.head_dim
+    M = cfg.M
     gate_up_flops = 2.0 * M * (2 * I) * H
-    gu_ms = stages["gate_up_silu"][0] / stages["gate_up_silu"][1]
-    achieved = gate_up_flops / (gu_ms / 1e3) / 1e12
+    achieved = gate_up_flops / (stage_ms(stages, "gate_up_silu") / 1e3) / 1e12
     attn_flops = 4.0 * cfg.B * cfg.n_heads * d * (cfg.S * (cfg.S + 1) / 2)   # QK^T and PV over visible pairs
-    attn_ms = stages["attention"][0] / stages["attention"][1]
-    gemm_flops = 2.0 * M * H * (cfg.qkv_dim + H + 2 * I) + 2.0 * M * I * H
-    gemm_ms = sum(stages[k][0] / stages[k][1] for k in ("qkv_proj", "o_proj_residual", "gate_up_silu", "down_residual"))
+    gemm_flops = gemm_flops_per_token(cfg) * M
+    gemm_ms = sum(stage_ms(stages, k) for k in ("qkv_proj", "o_proj_residual", "gate_up_silu", "down_residual"))
     norm_bytes = 2 * (2 * M * H * 2 + H * 2)
-    norm_ms = sum(stages[k][0] / stages[k][1] for k in ("rmsnorm_attn", "rmsnorm_mlp"))
-
+    norm_ms = sum(stage_ms(stages, k) for k in ("rmsnorm_attn", "rmsnorm_mlp"))
+    name = {"llama3_8b_prefill": "Llama-3-8B-shaped decoder layer, bf16 prefill, causal",
+            "llama32_1b_prefill": "Llama-3.2-1B-shaped decoder layer, bf16 prefill, causal",
+            "llama3_8b_long_llama3rope": "Llama-3-8B-shaped decoder layer, bf16 32k prefill, causal, "
+                                         "Llama3 RoPE scaling"}[args.workload]
+    metric = ("decoder-layer tokens/s (Llama-3-8B shape, bf16) + attention MFMA util %"
+              if args.workload == WORKLOAD else f"decoder-layer tokens/s ({name})")
     rec = {
-        "metric": "decoder-layer tokens/s (Llama-3-8B shape, bf16) + attention MFMA util %",
+        "metric": metric,
         "value": round(value, 1),
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        **common,
         "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) hidden, N(0,0.02) weights, 1+N(0,0.1) gains)",
-        "config": {"workload": "Llama-3-8B-shaped decoder layer, bf16 prefill, causal", "B": cfg.B, "S": cfg.S,
-                   "hidden": H, "n_heads": cfg.n_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": d,
-                   "intermediate": I, "rope_theta": rc.theta, "tokens_per_step": tokens},
-        "attention_mfma_util_pct": round(100.0 * attn_flops / (attn_ms / 1e3) / 1e12 / MI355X_BF16_DENSE_TFLOPS, 2),
+        "config": {"workload": name, "B": cfg.B, "S": cfg.S, **shape, "tokens_per_step": tokens},
+        "attention_mfma_util_pct": round(100.0 * attn_flops / (stage_ms(stages, "attention") / 1e3) / 1e12
+                                         / MI355X_BF16_DENSE_TFLOPS, 2),
         "gemm_mfma_util_pct": round(100.0 * gemm_flops / (gemm_ms / 1e3) / 1e12 / MI355X_BF16_DENSE_TFLOPS, 2),
         "rmsnorm_hbm_gbs": round(norm_bytes / (norm_ms / 1e3) / 1e9, 1),
         "stages_ms": {k: round(v[0] / v[1], 4) for k, v in stages.items()},
@@ -247,11 +392,14 @@ def main():
             "peak": MI355X_BF16_DENSE_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4),
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic() if args.workload == WORKLOAD else None,
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if args.workload == WORKLOAD and not args.no_decode:
+        dcfg = CONFIGS["llama3_8b_decode"]      # same 8B weights (same seed and shapes)
+        rec["decode"] = decode_summary(dcfg, *run_decode(L, torch, np, dcfg, W, 30, 3, cold=True), cold=True)
+    if args.workload == WORKLOAD and not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, W_bits, x_bits, args.cpu_sample_tokens)
     print(json.dumps(rec), flush=True)
     if args.copy_calibration:

@@ -193,28 +193,31 @@ DECODE = [
     ("bf16", 4, 1500, 8, 2, 128),
     ("bf16", 2, 700, 4, 4, 64),
     ("bf16", 3, 1100, 32, 8, 128),
+    ("bf16", 12, 1300, 16, 2, 128),  # 8 query heads per kv head; positions at tile and chunk edges
+    ("bf16", 12, 900, 4, 2, 64),
     ("bf16", 2, 300, 4, 2, 96),      # generic kernel
     ("f32", 2, 40, 4, 2, 16),
 ]
 
 
 @pytest.mark.parametrize("case", DECODE, ids=lambda c: "-".join(map(str, c)))
-@pytest.mark.parametrize("with_rope", [False, True])
+@pytest.mark.parametrize("with_rope", [False, "half", "interleaved"])
 def test_attn_decode(case, with_rope):
     require_gpu()
     dtype, B, ctx, nh, nkv, d = case
     qkv = normal(6, 140, (B, (nh + 2 * nkv) * d), dtype)
     kc = normal(6, 141, (B, ctx, nkv, d), dtype)
     vc = normal(6, 142, (B, ctx, nkv, d), dtype)
-    pos = np.array(([0, ctx - 1, 511, 512, 1023, 1024][:B] + [ctx // 2] * B)[:B], dtype=np.int64)
+    pos = np.array(([0, ctx - 1, 511, 512, 1023, 1024, 31, 32, 33, 127, 128, 129][:B] + [ctx // 2] * B)[:B],
+                   dtype=np.int64)
     pos = np.minimum(pos, ctx - 1)
-    rc = RopeCfg(theta=500000.0) if with_rope else None
+    rc = RopeCfg(theta=500000.0, interleaved=with_rope == "interleaved") if with_rope else None
     x = bits_to_f64(qkv, dtype)
     q, k, v = ref.split_qkv(x, nh, nkv, d)
     if rc:
         f = ref.rope_frequencies(d, rc, ctx)
-        q = ref.rope_rotate(q, pos[:, None], f)
-        k = ref.rope_rotate(k, pos[:, None], f)
+        q = ref.rope_rotate(q, pos[:, None], f, rc.interleaved)
+        k = ref.rope_rotate(k, pos[:, None], f, rc.interleaved)
     tk, tv = to_dev(kc, dtype), to_dev(vc, dtype)
     o = L.gqa_attn_decode(to_dev(qkv, dtype), torch.from_numpy(pos).to(DEV), tk, tv, nh, nkv, d,
                           rope=_rope(rc) if rc else None, kv_seq_len=ctx)

@@ -18,12 +18,13 @@
 // cycle over (b, c), so one (b, c) pair keeps landing on the same XCD and its K/V stays in
 // that XCD's L2.
 //
-// Decode (bf16, d in {64, 128}): an append kernel writes the new key (rotated) and value to slot
-// pos[b]; the split kernel gives each workgroup (b, c, 512-key chunk) 4 waves x 2 tiles of 64
-// keys. Q K^T uses the matrix cores with K streamed from HBM straight into operand registers
-// (every K element is used once); P V runs on the vector ALUs with 16-byte V loads. Waves merge
-// through LDS; each workgroup writes (max, sum, o) to workspace and a combine kernel merges the
-// chunks with the log-sum-exp rule.
+// Decode (bf16, d in {64, 128}, n_h/n_kv in {1, 2, 4, 8}): an append kernel writes the new key
+// (rotated) and value to slot pos[b]; the split kernel gives each workgroup (b, c, 512-key chunk)
+// 4 waves that step through 32-key tiles with the next tile's K and V already loading. Q K^T uses
+// the matrix cores with K streamed from HBM straight into operand registers (every K element is
+// used once); P V runs on the vector ALUs on V rows as stored, so V is never transposed. Waves
+// merge through LDS; each workgroup writes (max, sum, o) to workspace and a combine kernel merges
+// the chunks with the log-sum-exp rule.
 //
 // Generic kernels (fp32, or any even d <= 256): one wave per query, lanes over d, exact two-level
 // online softmax; used for the fp32 configuration and for head sizes the matrix-core kernels
@@ -554,208 +555,270 @@ __global__ __launch_bounds__(256) void attn_decode_generic_kernel(const T* __res
 }
 
 // ------------------------------------------------------------------ decode, matrix cores
+// Workgroup = (sequence b, kv head c, 512-key chunk), 4 waves. Wave w takes the 32-key tiles
+// w, w+4, w+8, w+12 of the chunk, so in each step the 4 waves stream 128 consecutive cache slots.
+// Every lane loads its K fragments (MFMA A operand: key row l%16, 8 dims) and its V rows (8 dims of
+// one key) for the next tile before it computes the current one, so two tiles of K and V (32 KiB
+// per wave) are in flight while the matrix and vector units work; loads use clamped slot indices
+// and are masked afterwards. No workgroup barrier or memory fence sits inside the key loop.
 constexpr int DEC_CHUNK = 512;   // keys per workgroup
-constexpr int DEC_TILE = 64;     // keys per wave step
-constexpr int DEC_THREADS = 256;
-constexpr int DEC_MAXG = 8;      // query heads per kv head handled in one pass
+constexpr int DEC_TILE = 32;     // keys per wave step
+constexpr int DEC_WAVES = 4;
+constexpr int DEC_THREADS = 64 * DEC_WAVES;
+constexpr int DEC_TPW = DEC_CHUNK / (DEC_TILE * DEC_WAVES);   // tiles per wave
+
+template <int D>
+struct DecTile {
+    static constexpr int KC32 = D / 32;          // 32-dim k steps of Q K^T
+    static constexpr int DL = D / 8;             // lanes per V row (8 dims each)
+    static constexpr int KPI = 64 / DL;          // keys per V row load
+    static constexpr int PV_IT = DEC_TILE / KPI;
+    uint4 k[2][KC32];
+    uint4 v[PV_IT];
+};
+
+template <int D>
+__device__ __forceinline__ void dec_load(DecTile<D>& t, const bf16_t* __restrict__ kb, const bf16_t* __restrict__ vb,
+                                         int64_t kstride, int64_t t0, int64_t last, int lrow, int lgrp, int dch,
+                                         int ksub) {
+#pragma unroll
+    for (int kf = 0; kf < 2; ++kf) {
+        const int64_t kk = t0 + kf * 16 + lrow, key = kk < last ? kk : last;
+#pragma unroll
+        for (int k = 0; k < DecTile<D>::KC32; ++k)
+            t.k[kf][k] = *reinterpret_cast<const uint4*>(kb + key * kstride + k * 32 + lgrp * 8);
+    }
+#pragma unroll
+    for (int it = 0; it < DecTile<D>::PV_IT; ++it) {
+        const int64_t kk = t0 + it * DecTile<D>::KPI + ksub, key = kk < last ? kk : last;
+        t.v[it] = *reinterpret_cast<const uint4*>(vb + key * kstride + dch * 8);
+    }
+}
+
+// One 32-key tile: S = K q (matrix cores; column = query head, only the first G are real),
+// online softmax per head in the log2 domain, then o[h][8 dims] += p V on the vector ALUs.
+// P goes through this wave's private LDS rows; LDS instructions of one wave execute in order, so
+// the exchange needs only a compiler barrier.
+template <int D, int G>
+__device__ __forceinline__ void dec_compute(const DecTile<D>& t, const bf16x8* qfr, int64_t t0, int64_t L,
+                                            float scale_log2, float& m_w, float& l_w, float (&o)[G][8],
+                                            float (*sPw)[G], int lrow, int lgrp, int dch, int ksub) {
+    using TT = DecTile<D>;
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int k = 0; k < TT::KC32; ++k)
+#pragma unroll
+        for (int kf = 0; kf < 2; ++kf)
+            sacc[kf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[kf][k]), qfr[k],
+                                                                sacc[kf], 0, 0, 0);
+    float s[2][4], mx = -INFINITY;
+#pragma unroll
+    for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t key = t0 + kf * 16 + 4 * lgrp + r;
+            const float v = key < L ? sacc[kf][r] * scale_log2 : -INFINITY;
+            s[kf][r] = v;
+            mx = fmaxf(mx, v);
+        }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(m_w, mx);
+    const float alpha = fast_exp2(m_w - mnew);
+    m_w = mnew;
+    float ls = 0.f;
+#pragma unroll
+    for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pr = fast_exp2(s[kf][r] - mnew);
+            ls += pr;
+            if (lrow < G) sPw[kf * 16 + 4 * lgrp + r][lrow] = pr;
+        }
+    l_w = l_w * alpha + ls;
+    // alpha of head h is the same in every lane of column h: move it to scalar registers
+    float al[G];
+    bool rescale = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        al[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
+        rescale |= al[h] != 1.f;
+    }
+    if (rescale) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[h][e] *= al[h];
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int it = 0; it < TT::PV_IT; ++it) {
+        const int kr = it * TT::KPI + ksub;
+        float pv[G];
+        if constexpr (G % 4 == 0) {
+#pragma unroll
+            for (int h = 0; h < G; h += 4) {
+                const float4 q4 = *reinterpret_cast<const float4*>(&sPw[kr][h]);
+                pv[h] = q4.x; pv[h + 1] = q4.y; pv[h + 2] = q4.z; pv[h + 3] = q4.w;
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < G; ++h) pv[h] = sPw[kr][h];
+        }
+        float vf[8];
+        unpack8(t.v[it], vf);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[h][e] += pv[h] * vf[e];
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // partial record per (b, h, chunk): [0] = max (log2 domain), [1] = sum, [2..2+d) = unnormalised o
-template <int D, bool ROPE, bool IL>
+template <int D, int G, bool ROPE, bool IL>
 __global__ __launch_bounds__(DEC_THREADS) void attn_decode_split_kernel(
     const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, const float2* __restrict__ cs, int64_t rope_rows,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, int64_t ctx, float* __restrict__ part, int nchunks,
     int nh, int nkv, float scale_log2) {
-    constexpr int KC32 = D / 32;
-    constexpr int DL = D / 8;             // lanes per V row in the P V step
-    constexpr int KPI = 64 / DL;          // keys per P V instruction
-    constexpr int PV_IT = DEC_TILE / KPI;
-    __shared__ float sQ[DEC_MAXG][D];
-    __shared__ float sP[4][DEC_TILE][DEC_MAXG];
-    __shared__ float sM[4][DEC_MAXG], sL[4][DEC_MAXG];
-    __shared__ float sO[4][DEC_MAXG][D];
+    using TT = DecTile<D>;
+    __shared__ __align__(16) float sP[DEC_WAVES][DEC_TILE][G];
+    __shared__ float sM[DEC_WAVES][G], sL[DEC_WAVES][G];
+    __shared__ float sO[DEC_WAVES][G][D];
 
-    const int chunk = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-    const int g = nh / nkv;
-    const int64_t p = clamp_pos(pos[b], ctx);
-    const int64_t L = p + 1;
+    // the kv heads of one (b, chunk) are adjacent block ids: they read adjacent 256-byte pieces of
+    // the same cache rows
+    const int blk = blockIdx.x;
+    const int c = blk % nkv;
+    const int chunk = (blk / nkv) % nchunks;
+    const int b = blk / (nkv * nchunks);
+    const int64_t L = clamp_pos(pos[b], ctx) + 1;
     const int64_t k0 = static_cast<int64_t>(chunk) * DEC_CHUNK;
     if (k0 >= L) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lrow = lane & 15, lgrp = lane >> 4;
-    const int64_t rs = static_cast<int64_t>(nh + 2 * nkv) * D;
-
-    // q heads of this kv head (rotated when ROPE) -> LDS fp32
-    for (int e = tid; e < g * D; e += DEC_THREADS) {
-        const int hh = e / D, dd = e % D;
-        const bf16_t* qp = qkv + b * rs + static_cast<int64_t>(c * g + hh) * D;
-        float x = bf2f(qp[dd]);
-        if (ROPE) {
-            const float2* row = cs + clamp_pos(pos[b], rope_rows) * (D / 2);
-            int partner, j;
-            float sign;
-            if (IL) { partner = dd ^ 1; j = dd >> 1; sign = (dd & 1) ? 1.f : -1.f; }
-            else { partner = dd < D / 2 ? dd + D / 2 : dd - D / 2; j = dd < D / 2 ? dd : dd - D / 2; sign = dd < D / 2 ? -1.f : 1.f; }
-            const float2 t = row[j];
-            x = x * t.x + sign * bf2f(qp[partner]) * t.y;
-        }
-        sQ[hh][dd] = x;
-    }
-    __syncthreads();
-    // B operand: column = head (lrow < g), k = dims
-    bf16x8 qfr[KC32];
-#pragma unroll
-    for (int k = 0; k < KC32; ++k) {
-        float f[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = lrow < g ? sQ[lrow][k * 32 + lgrp * 8 + e] : 0.f;
-        qfr[k] = __builtin_bit_cast(bf16x8, pack8(f));
-    }
-
-    float m_w = -1e30f, l_w = 0.f;            // per lane: stats of head column lrow (valid for lrow < g)
-    float o[DEC_MAXG][8];
-#pragma unroll
-    for (int hh = 0; hh < DEC_MAXG; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+    const int dch = lane % TT::DL, ksub = lane / TT::DL;
+    const int64_t kstride = static_cast<int64_t>(nkv) * D;
     const bf16_t* kb = kc + (static_cast<int64_t>(b) * ctx * nkv + c) * D;
     const bf16_t* vb = vc + (static_cast<int64_t>(b) * ctx * nkv + c) * D;
-    const int64_t kstride = static_cast<int64_t>(nkv) * D;
+    const int64_t last = L - 1;
+    const int64_t base = k0 + static_cast<int64_t>(wave) * DEC_TILE;
+    constexpr int64_t STEP = static_cast<int64_t>(DEC_WAVES) * DEC_TILE;
 
-    for (int t = wave; t < DEC_CHUNK / DEC_TILE; t += 4) {
-        const int64_t t0 = k0 + static_cast<int64_t>(t) * DEC_TILE;
-        if (t0 >= L) break;
-        f32x4 sacc[4];
+    // B operand of S = K q: column lrow = query head c*G + lrow (zero for lrow >= G), k = dims.
+    // Loaded before the first K/V tile and without branches, so no wait on it holds back the tiles.
+    bf16x8 qfr[TT::KC32];
+    {
+        const int64_t rs = static_cast<int64_t>(nh + 2 * nkv) * D;
+        const bf16_t* qp = qkv + b * rs + static_cast<int64_t>(c * G + (lrow < G ? lrow : 0)) * D;
+        const float2* row = ROPE ? cs + clamp_pos(pos[b], rope_rows) * (D / 2) : nullptr;
 #pragma unroll
-        for (int kf = 0; kf < 4; ++kf) sacc[kf] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < KC32; ++k) {
-#pragma unroll
-            for (int kf = 0; kf < 4; ++kf) {
-                const int64_t key = t0 + kf * 16 + lrow;
-                uint4 u = make_uint4(0, 0, 0, 0);
-                if (key < L) u = *reinterpret_cast<const uint4*>(kb + key * kstride + k * 32 + lgrp * 8);
-                sacc[kf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), qfr[k], sacc[kf], 0, 0, 0);
-            }
-        }
-        float s[4][4], mx = -1e30f;
-#pragma unroll
-        for (int kf = 0; kf < 4; ++kf)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t key = t0 + kf * 16 + 4 * lgrp + r;
-                const float v = key < L ? sacc[kf][r] * scale_log2 : -INFINITY;
-                s[kf][r] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m_w, mx);
-        const float alpha = fast_exp2(m_w - mnew);
-        m_w = mnew;
-        float ls = 0.f;
-#pragma unroll
-        for (int kf = 0; kf < 4; ++kf)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float pr = fast_exp2(s[kf][r] - mnew);
-                ls += pr;
-                if (lrow < g) sP[wave][kf * 16 + 4 * lgrp + r][lrow] = pr;
-            }
-        l_w = l_w * alpha + ls;
-        if (lgrp == 0 && lrow < g) sM[wave][lrow] = alpha;  // broadcast alpha per head
-        // sP / sM rows are private to this wave: order its LDS writes before the reads below
-        // (no workgroup barrier: waves leave this loop after different numbers of tiles)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        // P V on vector ALUs: lane owns dims (lane % DL)*8 .. +7 of keys it*KPI + lane/DL
-        float al[DEC_MAXG];
-#pragma unroll
-        for (int hh = 0; hh < DEC_MAXG; ++hh) al[hh] = hh < g ? sM[wave][hh] : 0.f;
-#pragma unroll
-        for (int hh = 0; hh < DEC_MAXG; ++hh)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[hh][e] *= al[hh];
-        const int dch = lane % DL, ksub = lane / DL;
-#pragma unroll 4
-        for (int it = 0; it < PV_IT; ++it) {
-            const int kr = it * KPI + ksub;
-            const int64_t key = t0 + kr;
-            if (key >= L) continue;
-            float vf[8];
-            unpack8(*reinterpret_cast<const uint4*>(vb + key * kstride + dch * 8), vf);
-#pragma unroll
-            for (int hh = 0; hh < DEC_MAXG; ++hh) {
-                if (hh < g) {
-                    const float pr = sP[wave][kr][hh];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) o[hh][e] += pr * vf[e];
+        for (int k = 0; k < TT::KC32; ++k) {
+            const int d0 = k * 32 + lgrp * 8;
+            float f[8];
+            unpack8(*reinterpret_cast<const uint4*>(qp + d0), f);
+            if (ROPE) {
+                if (IL) {
+                    rope8_inter(f, row, d0);
+                } else {
+                    float g8[8];
+                    const int pd = d0 < D / 2 ? d0 + D / 2 : d0 - D / 2;
+                    unpack8(*reinterpret_cast<const uint4*>(qp + pd), g8);
+                    if (d0 < D / 2) rope8_half(f, g8, row, d0);
+                    else rope8_half(g8, f, row, pd);
                 }
             }
-        }
-        // all lanes' reads of sP / sM precede the next tile's writes
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    }
-    // reduce o over the KPI key sub-groups of the wave
 #pragma unroll
-    for (int hh = 0; hh < DEC_MAXG; ++hh)
+            for (int e = 0; e < 8; ++e) f[e] = lrow < G ? f[e] : 0.f;
+            qfr[k] = __builtin_bit_cast(bf16x8, pack8(f));
+        }
+    }
+
+    // two tiles in flight from the start; tile loads are unconditional (slot indices are clamped to
+    // the last valid slot), only the compute of a tile past the end is skipped
+    DecTile<D> ta, tb;
+    dec_load<D>(ta, kb, vb, kstride, base, last, lrow, lgrp, dch, ksub);
+    dec_load<D>(tb, kb, vb, kstride, base + STEP, last, lrow, lgrp, dch, ksub);
+
+    float m_w = -INFINITY, l_w = 0.f;   // per lane: stats of head column lrow
+    float o[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+
+#pragma unroll
+    for (int i = 0; i < DEC_TPW; i += 2) {
+        const int64_t t0 = base + i * STEP, t1 = t0 + STEP;
+        if (t0 < L) dec_compute<D, G>(ta, qfr, t0, L, scale_log2, m_w, l_w, o, sP[wave], lrow, lgrp, dch, ksub);
+        if (i + 2 < DEC_TPW) dec_load<D>(ta, kb, vb, kstride, t0 + 2 * STEP, last, lrow, lgrp, dch, ksub);
+        if (t1 < L) dec_compute<D, G>(tb, qfr, t1, L, scale_log2, m_w, l_w, o, sP[wave], lrow, lgrp, dch, ksub);
+        if (i + 3 < DEC_TPW) dec_load<D>(tb, kb, vb, kstride, t0 + 3 * STEP, last, lrow, lgrp, dch, ksub);
+    }
+
+    // reduce o over the KPI key groups of the wave, l over the 4 row groups
+#pragma unroll
+    for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            for (int off = DL; off < 64; off <<= 1) o[hh][e] += __shfl_xor(o[hh][e], off, 64);
+#pragma unroll
+            for (int off = TT::DL; off < 64; off <<= 1) o[h][e] += __shfl_xor(o[h][e], off, 64);
     float lt = l_w;
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
-    if (lgrp == 0 && lrow < g) {
-        sM[wave][lrow] = m_w;
+    if (lgrp == 0 && lrow < G) {
+        sM[wave][lrow] = m_w;      // -inf for a wave that saw no key
         sL[wave][lrow] = lt;
     }
-    if (lane < DL) {
+    if (lane < TT::DL) {
 #pragma unroll
-        for (int hh = 0; hh < DEC_MAXG; ++hh)
-            if (hh < g)
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sO[wave][hh][lane * 8 + e] = o[hh][e];
+            for (int e = 0; e < 8; ++e) sO[wave][h][lane * 8 + e] = o[h][e];
     }
     __syncthreads();
-    // merge the 4 waves (waves that saw no key have m = -1e30, l = 0) and write the chunk partial
-    for (int e = tid; e < g * (D + 2); e += DEC_THREADS) {
-        const int hh = e / (D + 2), k = e % (D + 2);
-        float M = -1e30f;
+    // merge the waves (wave 0 always saw key k0, so M is finite) and write the chunk partial
+    for (int e = tid; e < G * (D + 2); e += DEC_THREADS) {
+        const int h = e / (D + 2), k = e % (D + 2);
+        float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, sM[w][hh]);
+        for (int w = 0; w < DEC_WAVES; ++w) M = fmaxf(M, sM[w][h]);
         float v = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float sc = exp2f(sM[w][hh] - M);
-            if (k == 1) v += sL[w][hh] * sc;
-            else if (k >= 2) v += sO[w][hh][k - 2] * sc;
+        for (int w = 0; w < DEC_WAVES; ++w) {
+            const float sc = exp2f(sM[w][h] - M);
+            if (k == 1) v += sL[w][h] * sc;
+            else if (k >= 2) v += sO[w][h][k - 2] * sc;
         }
         if (k == 0) v = M;
-        part[((static_cast<int64_t>(b) * nh + c * g + hh) * nchunks + chunk) * (D + 2) + k] = v;
+        part[((static_cast<int64_t>(b) * nh + c * G + h) * nchunks + chunk) * (D + 2) + k] = v;
     }
 }
 
+// One wave per (b, h): log-sum-exp merge of the chunk partials. The chunk loop is unrolled so the
+// partial rows of several chunks are loaded together.
 template <typename T>
-__global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* __restrict__ part,
-                                                                  const int64_t* __restrict__ pos, int64_t ctx,
-                                                                  T* __restrict__ out, int nh, int d, int nchunks) {
-    const int bh = blockIdx.x;
+__global__ __launch_bounds__(64) void attn_decode_combine_kernel(const float* __restrict__ part,
+                                                                 const int64_t* __restrict__ pos, int64_t ctx,
+                                                                 T* __restrict__ out, int nh, int d, int nchunks) {
+    const int bh = blockIdx.x, lane = threadIdx.x;
     const int b = bh / nh;
     const int64_t L = clamp_pos(pos[b], ctx) + 1;
     const int nc = static_cast<int>((L + DEC_CHUNK - 1) / DEC_CHUNK);
-    const float* pr = part + static_cast<int64_t>(bh) * nchunks * (d + 2);
-    float M = -1e30f;
-    for (int k = 0; k < nc; ++k) M = fmaxf(M, pr[k * (d + 2)]);
-    for (int dd = threadIdx.x; dd < d; dd += blockDim.x) {
-        float num = 0.f, den = 0.f;
-        for (int k = 0; k < nc; ++k) {
-            const float sc = exp2f(pr[k * (d + 2)] - M);
-            den += pr[k * (d + 2) + 1] * sc;
-            num += pr[k * (d + 2) + 2 + dd] * sc;
-        }
-        stf<T>(out + static_cast<int64_t>(bh) * d + dd, num / den);
+    const int64_t rec = d + 2;
+    const float* pr = part + static_cast<int64_t>(bh) * nchunks * rec;
+    float M = -INFINITY;
+    for (int k = lane; k < nc; k += 64) M = fmaxf(M, pr[k * rec]);
+    M = wave_max(M);
+    float den = 0.f;
+    for (int k = lane; k < nc; k += 64) den += pr[k * rec + 1] * exp2f(pr[k * rec] - M);
+    den = wave_sum(den);
+    const float inv = 1.f / den;
+    for (int dd = lane; dd < d; dd += 64) {
+        float num = 0.f;
+#pragma unroll 8
+        for (int k = 0; k < nc; ++k) num += pr[k * rec + 2 + dd] * exp2f(pr[k * rec] - M);
+        stf<T>(out + static_cast<int64_t>(bh) * d + dd, num * inv);
     }
 }
 
@@ -834,29 +897,42 @@ size_t attn_decode_workspace_bytes(int64_t B, int64_t nh, int64_t d, int64_t ctx
     return static_cast<size_t>(B * nh * nchunks * (d + 2)) * sizeof(float);
 }
 
-template <int D, bool ROPE, bool IL>
+template <int D, int G, bool ROPE, bool IL>
 static hipError_t decode_go(const void* qkv, const int64_t* pos, const RopeTab* tab, const void* kc, const void* vc,
                             int64_t ctx, void* o, int B, int nh, int nkv, void* ws, hipStream_t st) {
     const int nchunks = static_cast<int>((ctx + DEC_CHUNK - 1) / DEC_CHUNK);
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
-    hipLaunchKernelGGL((attn_decode_split_kernel<D, ROPE, IL>), dim3(nchunks, nkv, B), dim3(DEC_THREADS), 0, st,
+    const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(B) * nchunks * nkv);
+    hipLaunchKernelGGL((attn_decode_split_kernel<D, G, ROPE, IL>), dim3(blocks), dim3(DEC_THREADS), 0, st,
                        static_cast<const bf16_t*>(qkv), pos, tab ? tab->cs : nullptr, tab ? tab->rows : 1,
                        static_cast<const bf16_t*>(kc), static_cast<const bf16_t*>(vc), ctx, static_cast<float*>(ws),
                        nchunks, nh, nkv, scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_decode_combine_kernel<bf16_t>, dim3(B * nh), dim3(128), 0, st,
+    hipLaunchKernelGGL(attn_decode_combine_kernel<bf16_t>, dim3(B * nh), dim3(64), 0, st,
                        static_cast<const float*>(ws), pos, ctx, static_cast<bf16_t*>(o), nh, D, nchunks);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, int G>
 static hipError_t decode_rope_sel(const void* qkv, const int64_t* pos, const RopeTab* tab, int il, const void* kc,
                                   const void* vc, int64_t ctx, void* o, int B, int nh, int nkv, void* ws,
                                   hipStream_t st) {
-    if (!tab) return decode_go<D, false, false>(qkv, pos, tab, kc, vc, ctx, o, B, nh, nkv, ws, st);
-    if (il) return decode_go<D, true, true>(qkv, pos, tab, kc, vc, ctx, o, B, nh, nkv, ws, st);
-    return decode_go<D, true, false>(qkv, pos, tab, kc, vc, ctx, o, B, nh, nkv, ws, st);
+    if (!tab) return decode_go<D, G, false, false>(qkv, pos, tab, kc, vc, ctx, o, B, nh, nkv, ws, st);
+    if (il) return decode_go<D, G, true, true>(qkv, pos, tab, kc, vc, ctx, o, B, nh, nkv, ws, st);
+    return decode_go<D, G, true, false>(qkv, pos, tab, kc, vc, ctx, o, B, nh, nkv, ws, st);
+}
+
+template <int D>
+static hipError_t decode_g_sel(const void* qkv, const int64_t* pos, const RopeTab* tab, int il, const void* kc,
+                               const void* vc, int64_t ctx, void* o, int B, int nh, int nkv, void* ws,
+                               hipStream_t st) {
+    switch (nh / nkv) {
+        case 1: return decode_rope_sel<D, 1>(qkv, pos, tab, il, kc, vc, ctx, o, B, nh, nkv, ws, st);
+        case 2: return decode_rope_sel<D, 2>(qkv, pos, tab, il, kc, vc, ctx, o, B, nh, nkv, ws, st);
+        case 4: return decode_rope_sel<D, 4>(qkv, pos, tab, il, kc, vc, ctx, o, B, nh, nkv, ws, st);
+        default: return decode_rope_sel<D, 8>(qkv, pos, tab, il, kc, vc, ctx, o, B, nh, nkv, ws, st);
+    }
 }
 
 hipError_t launch_attn_decode(int dtype, const void* qkv, const int64_t* pos, const RopeTab* tab, int il, void* kc,
@@ -876,10 +952,11 @@ hipError_t launch_attn_decode(int dtype, const void* qkv, const int64_t* pos, co
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // 2) attention over slots 0..pos[b]
-    if (attn_mfma_supported(dtype, d, nh, nkv) && nh / nkv <= DEC_MAXG) {
+    const int g = nkv > 0 ? nh / nkv : 0;
+    if (attn_mfma_supported(dtype, d, nh, nkv) && (g == 1 || g == 2 || g == 4 || g == 8)) {
         if (ws_bytes < attn_decode_workspace_bytes(B, nh, d, ctx)) return hipErrorInvalidValue;
-        if (d == 128) return decode_rope_sel<128>(qkv, pos, tab, il, kc, vc, ctx, o, B, nh, nkv, ws, st);
-        return decode_rope_sel<64>(qkv, pos, tab, il, kc, vc, ctx, o, B, nh, nkv, ws, st);
+        if (d == 128) return decode_g_sel<128>(qkv, pos, tab, il, kc, vc, ctx, o, B, nh, nkv, ws, st);
+        return decode_g_sel<64>(qkv, pos, tab, il, kc, vc, ctx, o, B, nh, nkv, ws, st);
     }
     const unsigned blocks = static_cast<unsigned>((static_cast<int64_t>(B) * nh + 3) / 4);
     const float scale = 1.f / sqrtf(static_cast<float>(d));
