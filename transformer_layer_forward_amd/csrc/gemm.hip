@@ -309,85 +309,100 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_big_kernel(
 }
 
 // ------------------------------------------------------------------ bf16, small M (split-K)
-// Workgroup = 4 waves over SK_N weight rows and all M <= 64 tokens, for one K range; each wave
-// takes every 4th 32-wide k step. Operands come straight from global memory (each weight element
-// is used by one wave only); the 4 wave partials are summed through LDS.
-constexpr int SK_N = 32, SK_MAXM = 64, SK_THREADS = 256;
+// With M <= 64 tokens the product is bound by streaming W from HBM once. A workgroup of 8 waves
+// owns 128*FR weight rows and one 1024-wide K chunk. The 64 x 1024 activation chunk is staged in
+// LDS once (rows >= M and columns >= K are zero; 16-byte chunks XOR-swizzled by row so the 16 rows
+// of a B fragment read distinct banks); each wave then streams its own 16*FR weight rows through
+// a ring of SK_U 32-wide k steps of loads in flight and feeds the matrix cores with W as the A
+// operand. Chunk partials go to workspace; a reduce kernel sums them and applies the epilogue.
+constexpr int SK_MAXM = 64, SK_KC = 1024, SK_THREADS = 512, SK_U = 8;
+constexpr int SK_CPR = SK_KC / 8;                 // 16-byte chunks per staged activation row
+constexpr int SK_LDS_BYTES = 64 * SK_KC * 2;
 
+// The k steps of one chunk. TAIL: the chunk ends before SK_KC (k offsets are clamped to the last
+// valid 8-column group, whose re-read weights meet zero activations).
+template <int FR, bool TAIL>
+__device__ __forceinline__ void skinny_steps(uint4* __restrict__ sX, const bf16_t* __restrict__ X, int M, int K,
+                                             int k0, int kvalid, int tid, const bf16_t* const* wrow, int kofs0,
+                                             int kmax, int lrow, int lgrp, f32x4 (&acc)[FR][4]) {
+    constexpr int KS = SK_KC / 32;
+    auto kof = [&](int step) { const int k = kofs0 + 32 * step; return TAIL ? min(k, kmax) : k; };
+    // first SK_U steps of weights in flight before the activation chunk is staged
+    uint4 wr[SK_U][FR];
+#pragma unroll
+    for (int u = 0; u < SK_U; ++u)
+#pragma unroll
+        for (int f = 0; f < FR; ++f) wr[u][f] = *reinterpret_cast<const uint4*>(wrow[f] + kof(u));
+    for (int e = tid; e < 64 * SK_CPR; e += SK_THREADS) {
+        const int m = e / SK_CPR, c = e % SK_CPR;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (m < M && c * 8 < kvalid) v = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(m) * K + k0 + c * 8);
+        sX[m * SK_CPR + (c ^ (m & 15))] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+        bf16x8 xb[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int m = 16 * b + lrow, c = 4 * st + lgrp;
+            xb[b] = __builtin_bit_cast(bf16x8, sX[m * SK_CPR + (c ^ (m & 15))]);
+        }
+        uint4 cur[FR];
+#pragma unroll
+        for (int f = 0; f < FR; ++f) cur[f] = wr[st % SK_U][f];
+        if (st + SK_U < KS) {
+#pragma unroll
+            for (int f = 0; f < FR; ++f) wr[st % SK_U][f] = *reinterpret_cast<const uint4*>(wrow[f] + kof(st + SK_U));
+        }
+#pragma unroll
+        for (int f = 0; f < FR; ++f)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur[f]), xb[b],
+                                                                    acc[f][b], 0, 0, 0);
+    }
+}
+
+template <int FR>
 __global__ __launch_bounds__(SK_THREADS) void gemm_bf16_skinny_kernel(const bf16_t* __restrict__ X,
                                                                       const bf16_t* __restrict__ W,
                                                                       float* __restrict__ P, int M, int Nw, int K,
-                                                                      int kchunk) {
-    __shared__ f32x4 red[3][2][4][64];
+                                                                      int nrb) {
+    extern __shared__ uint4 sX[];                 // [64][SK_CPR]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = blockIdx.x * SK_N;
-    const int split = blockIdx.y;
-    const int kbeg = split * kchunk;
-    const int kend = min(K, kbeg + kchunk);
     const int lrow = lane & 15, lgrp = lane >> 4;
-    f32x4 acc[2][4];
+    const int rb = blockIdx.x % nrb, kc = blockIdx.x / nrb;
+    const int k0 = kc * SK_KC;
+    const int kvalid = min(SK_KC, K - k0);        // a multiple of 8
+    const int n0 = rb * (128 * FR) + wave * (16 * FR);
+    const bf16_t* wrow[FR];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int f = 0; f < FR; ++f) wrow[f] = W + static_cast<int64_t>(min(n0 + 16 * f + lrow, Nw - 1)) * K;
+    f32x4 acc[FR][4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bf16_t* wp[2];
-    bool wok[2];
+    for (int f = 0; f < FR; ++f)
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-        const int n = n0 + a * 16 + lrow;
-        wok[a] = n < Nw;
-        wp[a] = W + static_cast<int64_t>(wok[a] ? n : 0) * K;
-    }
-    const bf16_t* xp[4];
-    bool xok[4];
+        for (int b = 0; b < 4; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (kvalid == SK_KC)
+        skinny_steps<FR, false>(sX, X, M, K, k0, kvalid, tid, wrow, k0 + lgrp * 8, K - 8, lrow, lgrp, acc);
+    else
+        skinny_steps<FR, true>(sX, X, M, K, k0, kvalid, tid, wrow, k0 + lgrp * 8, K - 8, lrow, lgrp, acc);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int m = b * 16 + lrow;
-        xok[b] = m < M;
-        xp[b] = X + static_cast<int64_t>(xok[b] ? m : 0) * K;
-    }
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    for (int k = kbeg + wave * 32; k < kend; k += 4 * 32) {
-        const int kk = k + lgrp * 8;
-        const bool kok = kk < kend;
-        bf16x8 av[2], bv[4];
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            uint4 u = zero;
-            if (wok[a] && kok) u = *reinterpret_cast<const uint4*>(wp[a] + kk);
-            av[a] = __builtin_bit_cast(bf16x8, u);
-        }
+    for (int f = 0; f < FR; ++f)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            uint4 u = zero;
-            if (xok[b] && kok) u = *reinterpret_cast<const uint4*>(xp[b] + kk);
-            bv[b] = __builtin_bit_cast(bf16x8, u);
-        }
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
-    }
-    if (wave > 0) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) red[wave - 1][a][b][lane] = acc[a][b];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            f32x4 v = acc[a][b] + red[0][a][b][lane] + red[1][a][b][lane] + red[2][a][b][lane];
-            const int m = b * 16 + lrow;
-            const int n = n0 + a * 16 + 4 * lgrp;
+            const int m = 16 * b + lrow;
+            const int n = n0 + 16 * f + 4 * lgrp;
             if (m >= M) continue;
-            float* prow = P + (static_cast<int64_t>(split) * M + m) * Nw;
+            float* prow = P + (static_cast<int64_t>(kc) * M + m) * Nw;
+            if (n + 4 <= Nw) {
+                *reinterpret_cast<f32x4*>(prow + n) = acc[f][b];
+            } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (n + r < Nw) prow[n + r] = v[r];
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < Nw) prow[n + r] = acc[f][b][r];
+            }
         }
 }
 
@@ -481,21 +496,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // ------------------------------------------------------------------ dispatch
 static bool use_skinny(int64_t M) { return M <= SK_MAXM; }
 
-static void skinny_plan(int64_t Nw, int64_t K, int* splits, int* kchunk) {
-    const int64_t ntiles = (Nw + SK_N - 1) / SK_N;
-    int64_t s = 1;
-    while (ntiles * s < 1024 && s < 64 && K / (s * 2) >= 256) s *= 2;
-    int64_t kc = (K + s - 1) / s;
-    kc = (kc + 127) / 128 * 128;  // whole 4-wave x 32 steps
-    *kchunk = static_cast<int>(kc);
-    *splits = static_cast<int>((K + kc - 1) / kc);
+// K chunks of SK_KC; 256-row workgroups (FR = 2) when that still gives ~192 or more workgroups,
+// 128-row ones otherwise.
+static void skinny_plan(int64_t Nw, int64_t K, int* fr, int* splits, int* nrb) {
+    *splits = static_cast<int>((K + SK_KC - 1) / SK_KC);
+    *fr = ((Nw + 255) / 256) * *splits >= 192 ? 2 : 1;
+    *nrb = static_cast<int>((Nw + 128 * *fr - 1) / (128 * *fr));
 }
 
 size_t gemm_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K, int epi) {
     if (dtype != LL_BF16 || !use_skinny(M)) return 0;
     const int64_t Nw = epi == EPI_SILU ? 2 * N : N;
-    int splits, kchunk;
-    skinny_plan(Nw, K, &splits, &kchunk);
+    int fr, splits, nrb;
+    skinny_plan(Nw, K, &fr, &splits, &nrb);
     return static_cast<size_t>(splits) * M * Nw * sizeof(float);
 }
 
@@ -524,17 +537,28 @@ static hipError_t big_launch(const void* X, const void* W, void* C, const void* 
     return big_launch_t<EPI, false, RD>(X, W, C, R, M, N, K, st, re);
 }
 
+template <int FR>
+static hipError_t skinny_gemm_t(const void* X, const void* W, void* P, int64_t M, int64_t Nw, int64_t K, int nrb,
+                                int splits, hipStream_t st) {
+    static bool attr = [] {
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_skinny_kernel<FR>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, SK_LDS_BYTES) == hipSuccess;
+    }();
+    if (!attr) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(gemm_bf16_skinny_kernel<FR>, dim3(static_cast<unsigned>(nrb) * splits), dim3(SK_THREADS),
+                       SK_LDS_BYTES, st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W),
+                       static_cast<float*>(P), static_cast<int>(M), static_cast<int>(Nw), static_cast<int>(K), nrb);
+    return hipGetLastError();
+}
+
 template <int EPI>
 static hipError_t skinny_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N, int64_t K,
                                 void* ws, hipStream_t st, const RopeEpi* re = nullptr) {
     const int64_t Nw = EPI == EPI_SILU ? 2 * N : N;
-    int splits, kchunk;
-    skinny_plan(Nw, K, &splits, &kchunk);
-    dim3 grid(static_cast<unsigned>((Nw + SK_N - 1) / SK_N), static_cast<unsigned>(splits));
-    hipLaunchKernelGGL(gemm_bf16_skinny_kernel, grid, dim3(SK_THREADS), 0, st, static_cast<const bf16_t*>(X),
-                       static_cast<const bf16_t*>(W), static_cast<float*>(ws), static_cast<int>(M),
-                       static_cast<int>(Nw), static_cast<int>(K), kchunk);
-    hipError_t e = hipGetLastError();
+    int fr, splits, nrb;
+    skinny_plan(Nw, K, &fr, &splits, &nrb);
+    hipError_t e = fr == 2 ? skinny_gemm_t<2>(X, W, ws, M, Nw, K, nrb, splits, st)
+                           : skinny_gemm_t<1>(X, W, ws, M, Nw, K, nrb, splits, st);
     if (e != hipSuccess) return e;
     const int64_t total = M * N;
     hipLaunchKernelGGL(gemm_splitk_reduce_kernel<EPI>, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
