@@ -92,7 +92,7 @@ def pmc_summary(fetch_db: str, write_db: str) -> None:
         vals = sorted(v for name, vs in d.items() if "copyBuffer" in name for v in vs)
         return vals[-1] if vals else None
 
-    gu_key = "gemm_bf16_big_kernel<2"
+    gu_key = "gemm_bf16_mfma32_kernel<2"
     f_copy, w_copy = pick_copy(f), pick_copy(w)
     f_gu, w_gu = pick(f, gu_key), pick(w, gu_key)
     kib = COPY_BYTES / 1024.0
@@ -386,7 +386,7 @@ def main():
         "rmsnorm_hbm_gbs": round(norm_bytes / (norm_ms / 1e3) / 1e9, 1),
         "stages_ms": {k: round(v[0] / v[1], 4) for k, v in stages.items()},
         "roofline": {
-            "kernel": "gemm_bf16_big_kernel<EPI_SILU> (fused gate_up + silu*up)",
+            "kernel": "gemm_bf16_mfma32_kernel<EPI_SILU> (fused gate_up + silu*up)",
             "bound": "mfma",
             "achieved": round(achieved, 1),
             "peak": MI355X_BF16_DENSE_TFLOPS,

@@ -308,6 +308,209 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_big_kernel(
     }
 }
 
+// ------------------------------------------------------------------ bf16, large M, 32x32 matrix ops
+// One workgroup of 4 waves (one per SIMD) computes a 256 (tokens) x 256 (weight rows) tile; each wave
+// owns a 128 x 128 block as 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators (256 accumulation
+// registers). Larger per-wave blocks than the 8-wave kernel above read a third less operand data
+// from LDS per matrix op. K runs in 64-wide stages through two LDS slots filled by direct
+// global->LDS loads (full 128-byte row segments); operand fragments are double-buffered in
+// registers across the four k16 quarters of a stage, and the loads of the next stage are spread
+// over the first two quarters. The epilogue stages each wave's results through LDS and writes whole
+// output rows. Used when K % 64 == 0 and N % 8 == 0, for every epilogue but the fused RoPE.
+constexpr int MF_M = 256, MF_N = 256, MF_K = 64;
+constexpr int MF_THREADS = 256;                         // 4 waves, one per SIMD, 128 x 128 each
+constexpr int MF_STAGE = (MF_M + MF_N) * MF_K;          // elements per LDS stage (64 KiB)
+constexpr int MF_NSLOT = 2;
+constexpr int MF_LDS_BYTES = MF_NSLOT * MF_STAGE * 2;   // 128 KiB
+constexpr int MF_LPW = 16;                              // 1 KiB direct loads per wave per stage
+
+// physical 16-byte chunk of logical chunk c in an LDS row of 8 chunks (128 bytes)
+__device__ __forceinline__ int mf_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+#define MF_WAITVM0() __builtin_amdgcn_s_waitcnt(0x0F70)   // vmcnt(0) only
+
+template <int EPI>
+__global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, const bf16_t* __restrict__ R,
+    int M, int N, int K, int tiles_m, int tiles_n) {
+    static_assert(EPI == EPI_STORE || EPI == EPI_RESIDUAL || EPI == EPI_SILU, "no fused RoPE in this kernel");
+    extern __shared__ __align__(16) bf16_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int l32 = lane & 31, lh = lane >> 5;
+
+    // ---- tile order: a contiguous range per XCD, then groups of 8 token tiles
+    const int T = tiles_m * tiles_n;
+    int lin = blockIdx.x;
+    if ((T & 7) == 0) lin = (lin & 7) * (T >> 3) + (lin >> 3);
+    constexpr int GROUP = 8;
+    const int group = lin / (GROUP * tiles_n);
+    const int first_m = group * GROUP;
+    const int gsz = min(tiles_m - first_m, GROUP);
+    const int in_g = lin - group * GROUP * tiles_n;
+    const int tm = first_m + in_g % gsz, tn = in_g / gsz;
+    const int m0 = tm * MF_M;
+    constexpr int OUT_T = EPI == EPI_SILU ? MF_N / 2 : MF_N;     // output columns per tile
+    const int n0 = tn * OUT_T;
+
+    // ---- direct loads: instruction j (0..15) of this wave fills the 128-byte segments of stage rows
+    // 32(j % 8) + 8*wave + lane/8 of the X (j < 8) or W (j >= 8) half; lane l lands at physical chunk
+    // l % 8, so it fetches the logical chunk cj that the row swizzle puts there (the same for every j).
+    // Rows past M or N read a clamped valid row; their results are never stored.
+    const int rsub = 8 * wave + (lane >> 3);
+    const int cj = (lane & 7) ^ mf_swz(rsub);
+    auto issue1 = [&](int slot, int k0, int j) {
+        const int r = 32 * (j & 7) + rsub;
+        const bf16_t* src;
+        if (j < 8) {
+            src = X + static_cast<int64_t>(min(m0 + r, M - 1)) * K;
+        } else {
+            int grow;
+            if (EPI == EPI_SILU) {      // 16-row blocks alternate W_gate and W_up rows of the same columns
+                const int blk = r >> 4, col = min(n0 + (blk >> 1) * 16 + (r & 15), N - 1);
+                grow = (blk & 1) ? N + col : col;
+            } else {
+                grow = min(n0 + r, N - 1);
+            }
+            src = W + static_cast<int64_t>(grow) * K;
+        }
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(src + k0 + cj * 8),
+            (__attribute__((address_space(3))) void*)(smem + slot * MF_STAGE + (4 * j + wave) * 8 * MF_K), 16, 0, 0);
+    };
+    // operand fragment offsets within a stage (A: weight rows, B: tokens), one per 32-row block; k16
+    // quarter q of a fragment sits at chunk (2q + lh) ^ swizzle = chunk(0) ^ 2q, i.e. offset(0) ^ 16q
+    int aoff[4], boff[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const int ra = wn * 128 + 32 * f + l32, rb = wm * 128 + 32 * f + l32;
+        aoff[f] = (MF_M + ra) * MF_K + ((lh ^ mf_swz(ra)) << 3);
+        boff[f] = rb * MF_K + ((lh ^ mf_swz(rb)) << 3);
+    }
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+    // ---- main loop. Two 64-wide K stages. At the top of iteration t every wave waits for its own loads
+    // of stage t and meets the others at a barrier: stage t is then complete in LDS and every wave is
+    // done with stage t-1, whose slot receives stage t+1, its 16 loads spread over the first two k16
+    // quarters of stage t. The last iteration re-reads the final stage into the free slot (never read),
+    // which keeps the loop free of branches.
+    const int nk = K / MF_K;
+#pragma unroll
+    for (int j = 0; j < MF_LPW; ++j) issue1(0, 0, j);
+    bf16x8 fa[2][4], fb[2][4];
+#define MF_MMA2(FA, FB, p)                                                                                   \
+    {                                                                                                      \
+        const int a_ = (p) >> 1, b_ = ((p) & 1) * 2;                                                       \
+        acc[a_][b_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[a_], FB[b_], acc[a_][b_], 0, 0, 0);       \
+        acc[a_][b_ + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[a_], FB[b_ + 1], acc[a_][b_ + 1], 0, 0, 0); \
+    }
+    for (int t = 0; t < nk; ++t) {
+        const int slot = t & 1;
+        const bf16_t* st = smem + slot * MF_STAGE;
+        const int kn = min(t + 1, nk - 1) * MF_K;
+        MF_WAITVM0();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            fa[0][f] = *reinterpret_cast<const bf16x8*>(st + aoff[f]);
+            fb[0][f] = *reinterpret_cast<const bf16x8*>(st + boff[f]);
+        }
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                MF_MMA2(fa[h & 1], fb[h & 1], p)
+                if (h < 3 && p < 4) {
+                    fa[(h + 1) & 1][p] = *reinterpret_cast<const bf16x8*>(st + (aoff[p] ^ (16 * (h + 1))));
+                    fb[(h + 1) & 1][p] = *reinterpret_cast<const bf16x8*>(st + (boff[p] ^ (16 * (h + 1))));
+                }
+                if (h < 2) issue1(slot ^ 1, kn, 8 * h + p);   // 16 loads over the first two quarters
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+#undef MF_MMA2
+    // ---- epilogue. Lane holds, for 32x32 block (a, b): token m = 32b + l32 of the wave's 128 and
+    // weight rows 8*(r/4) + 4*lh + r%4 of block a (r = 0..15). Results are rounded once to bf16,
+    // written to this wave's 32 KiB of LDS as [token][column] rows (16-byte chunks XOR-swizzled by
+    // row), and then stored with full-row 16-byte-per-lane writes.
+    MF_WAITVM0();                        // tail loads have landed: the ring may be overwritten
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int OC = EPI == EPI_SILU ? 64 : 128;           // output columns of this wave
+    constexpr int GPR = OC / 8;                               // 16-byte chunks per LDS row
+    bf16_t* reg = smem + wave * (128 * 128);                  // 32 KiB per wave
+    const int mw = m0 + wm * 128;                             // first token of the wave
+    const int nw = n0 + wn * OC;                              // first output column of the wave
+    auto lds_at = [&](int m, int c) { return reg + m * OC + (((c >> 3) ^ (m & (GPR - 1))) << 3) + (c & 7); };
+
+    if constexpr (EPI == EPI_RESIDUAL) {
+        // residual rows of the wave into LDS (coalesced), to be added in fp32 below
+#pragma unroll 4
+        for (int i = 0; i < 128 * GPR / 64; ++i) {
+            const int e = i * 64 + lane, m = e / GPR, g = e % GPR;
+            const int gm = min(mw + m, M - 1), gn = nw + 8 * g;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (gn < N) v = *reinterpret_cast<const uint4*>(R + static_cast<int64_t>(gm) * N + gn);
+            *reinterpret_cast<uint4*>(lds_at(m, 8 * g)) = v;
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int m = 32 * b + l32;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            if constexpr (EPI == EPI_SILU) {
+                // rows 0..15 of block a are gate columns 16a.., rows 16..31 the up columns of the same outputs
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    float o[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float gt = acc[a][b][4 * g + q], up = acc[a][b][4 * g + q + 8];
+                        o[q] = gt / (1.f + __expf(-gt)) * up;
+                    }
+                    const int c = 16 * a + 8 * g + 4 * lh;
+                    *reinterpret_cast<uint2*>(lds_at(m, c)) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c = 32 * a + 8 * g + 4 * lh;
+                    float o[4] = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
+                    uint2* p = reinterpret_cast<uint2*>(lds_at(m, c));
+                    if constexpr (EPI == EPI_RESIDUAL) {
+                        const uint2 rv = *p;
+                        o[0] += __uint_as_float(rv.x << 16); o[1] += __uint_as_float(rv.x & 0xffff0000u);
+                        o[2] += __uint_as_float(rv.y << 16); o[3] += __uint_as_float(rv.y & 0xffff0000u);
+                    }
+                    *p = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                }
+            }
+        }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    // LDS instructions of one wave execute in order: the rows are complete for this wave's reads
+#pragma unroll 4
+    for (int i = 0; i < 128 * GPR / 64; ++i) {
+        const int e = i * 64 + lane, m = e / GPR, g = e % GPR;
+        const int gm = mw + m, gn = nw + 8 * g;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds_at(m, 8 * g));
+        if (gm < M && gn < N) *reinterpret_cast<uint4*>(C + static_cast<int64_t>(gm) * N + gn) = v;
+    }
+}
+#undef MF_WAITVM0
+
 // ------------------------------------------------------------------ bf16, small M (split-K)
 // With M <= 64 tokens the product is bound by streaming W from HBM once. A workgroup of 8 waves
 // owns 128*FR weight rows and one 1024-wide K chunk. The 64 x 1024 activation chunk is staged in
@@ -537,6 +740,23 @@ static hipError_t big_launch(const void* X, const void* W, void* C, const void* 
     return big_launch_t<EPI, false, RD>(X, W, C, R, M, N, K, st, re);
 }
 
+template <int EPI>
+static hipError_t mfma32_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N,
+                                int64_t K, hipStream_t st) {
+    static bool attr = [] {
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_mfma32_kernel<EPI>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, MF_LDS_BYTES) == hipSuccess;
+    }();
+    if (!attr) return hipErrorInvalidConfiguration;
+    const int ncols = EPI == EPI_SILU ? MF_N / 2 : MF_N;
+    const int tm = static_cast<int>((M + MF_M - 1) / MF_M), tn = static_cast<int>((N + ncols - 1) / ncols);
+    hipLaunchKernelGGL(gemm_bf16_mfma32_kernel<EPI>, dim3(tm * tn), dim3(MF_THREADS), MF_LDS_BYTES, st,
+                       static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), static_cast<bf16_t*>(C),
+                       static_cast<const bf16_t*>(R), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tm,
+                       tn);
+    return hipGetLastError();
+}
+
 template <int FR>
 static hipError_t skinny_gemm_t(const void* X, const void* W, void* P, int64_t M, int64_t Nw, int64_t K, int nrb,
                                 int splits, hipStream_t st) {
@@ -603,6 +823,13 @@ hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C
             case EPI_RESIDUAL: return skinny_launch<EPI_RESIDUAL>(X, W, C, R, M, N, K, ws, st);
             case EPI_ROPE: return skinny_launch<EPI_ROPE>(X, W, C, R, M, N, K, ws, st, re);
             default: return skinny_launch<EPI_SILU>(X, W, C, R, M, N, K, ws, st);
+        }
+    }
+    if (epi != EPI_ROPE && K % MF_K == 0 && N % 8 == 0) {
+        switch (epi) {
+            case EPI_STORE: return mfma32_launch<EPI_STORE>(X, W, C, R, M, N, K, st);
+            case EPI_RESIDUAL: return mfma32_launch<EPI_RESIDUAL>(X, W, C, R, M, N, K, st);
+            default: return mfma32_launch<EPI_SILU>(X, W, C, R, M, N, K, st);
         }
     }
     switch (epi) {
