@@ -113,6 +113,7 @@ PREFILL = [
     ("bf16", 1, 100, 16, 2, 128),
     ("bf16", 3, 1, 4, 1, 128),
     ("bf16", 1, 257, 6, 2, 64),      # g = 3 (one head per block)
+    ("bf16", 1, 700, 8, 2, 128),     # 11 key tiles, ragged last tile
     ("bf16", 1, 50, 4, 2, 96),       # generic kernel
     ("f32", 1, 32, 4, 2, 16),
     ("f32", 2, 45, 6, 3, 32),
@@ -125,7 +126,7 @@ def _attn_inputs(dtype, B, S, nh, nkv, d, seed=3):
 
 
 @pytest.mark.parametrize("case", PREFILL, ids=lambda c: "-".join(map(str, c)))
-@pytest.mark.parametrize("mode", ["rotated", "rope", "rope_il_cache"])
+@pytest.mark.parametrize("mode", ["rotated", "rotated_cache", "rope", "rope_il_cache"])
 def test_attn_prefill(case, mode):
     require_gpu()
     dtype, B, S, nh, nkv, d = case
@@ -133,7 +134,7 @@ def test_attn_prefill(case, mode):
     pos = np.broadcast_to(np.arange(S, dtype=np.int64), (B, S)).copy()
     rc = None
     q, k, v = ref.split_qkv(x, nh, nkv, d)
-    if mode != "rotated":
+    if mode.startswith("rope"):
         rc = RopeCfg(type="llama3", theta=500000.0, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
                      original_max_pos=64, interleaved=(mode == "rope_il_cache"))
         f = ref.rope_frequencies(d, rc, S)
@@ -142,7 +143,7 @@ def test_attn_prefill(case, mode):
     want = ref.attention_prefill(q, k, v)
     kc = vc = None
     ctx = S + 7
-    if mode == "rope_il_cache":
+    if mode.endswith("_cache"):
         kc = torch.zeros((B, ctx, nkv, d), device=DEV, dtype=TD[dtype])
         vc = torch.zeros((B, ctx, nkv, d), device=DEV, dtype=TD[dtype])
     o = L.gqa_attn_prefill(to_dev(qkv, dtype), torch.from_numpy(pos).to(DEV), nh, nkv, d,

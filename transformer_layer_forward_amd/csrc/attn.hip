@@ -11,8 +11,12 @@
 // transposed, S^T = K Q^T, with K as the MFMA A operand and Q (in registers) as B: the
 // 16x16 output fragment then holds, per lane, one query column and 4 keys, which after the
 // fp32 online softmax (exp2 with log2(e)/sqrt(d) folded into the scale) is exactly the B-operand
-// layout of O^T += V^T P^T. V is transposed into LDS as [d][key] when the tile is staged.
-// K rows and V^T rows are XOR-swizzled so the 16 lanes of an operand read hit distinct banks.
+// layout of O^T += V^T P^T. Two variants stage the tiles: with q and k already rotated (the layer
+// path) K and V go global -> LDS by direct loads, V stays [key][d] and its V^T operand comes from
+// transposing LDS reads, and a per-wave software pipeline overlaps the next tile's Q K^T with the
+// current softmax; with RoPE applied on load (the standalone entry point) tiles pass through
+// registers, are rotated there, and V is transposed into LDS as [d][key] while it is stored.
+// Rows are XOR-swizzled so the lanes of an operand read hit distinct banks.
 // Causality: query block qb only visits key tiles 0..qb; only the diagonal tile is masked.
 // Blocks are issued heaviest-first (largest qb first); consecutive blocks of one qb level
 // cycle over (b, c), so one (b, c) pair keeps landing on the same XCD and its K/V stays in
@@ -362,6 +366,285 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_mfma_kernel(
     }
 #undef AP_LOAD
 #undef AP_STORE
+
+    // ---- normalise and store: lane holds dims a*16 + 4 lgrp + {0..3} of query q0 + qf*16 + lrow
+#pragma unroll
+    for (int qf = 0; qf < 2; ++qf) {
+        float l = l_i[qf];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        const float inv = 1.f / l;
+        const int qi = q0 + qf * 16 + lrow;
+        if (qi >= S) continue;
+        bf16_t* op = out + (static_cast<int64_t>(b) * S + qi) * nh * D + static_cast<int64_t>(h) * D;
+#pragma unroll
+        for (int a = 0; a < C::DF; ++a) {
+            const f32x4 v = oacc[a][qf];
+            *reinterpret_cast<uint2*>(op + a * 16 + 4 * lgrp) =
+                make_uint2(pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv));
+        }
+    }
+}
+
+// ------------------------------------------------------------------ prefill, matrix cores, direct tile loads
+// Used when no RoPE is applied inside attention (the layer path: q and k arrive rotated). Workgroup
+// and wave layout as above; differences:
+//  * K and V tiles go global -> LDS with global_load_lds_dwordx4 (no register staging, no vector ALU
+//    work); both are stored row-major [key][dim] with 16-byte chunks XOR-swizzled by row.
+//  * V^T fragments are read with the transposing ds_read_b64_tr_b16: within each 16-lane group,
+//    lane i receives element i % 4 of the 8-byte words addressed by lanes 4e + i/4 (e = 0..3), so
+//    lanes addressing 4 consecutive key rows x 4 dim groups hand every lane 4 keys of one dim. Two
+//    such reads give the 8 keys {32t + 4g + 0..3, 32t + 16 + 4g + 0..3} that the P^T operand holds.
+//  * per-wave software pipeline: tile j+1's score matrix ops overlap tile j's softmax, tile j's P V
+//    overlaps its second half of exponentials; K runs one tile ahead of V (two buffers each). Score
+//    accumulators start at minus the reference max the wave held when they were issued; a moved
+//    reference (rare: only by more than kSlack) is corrected under a wave-uniform branch.
+template <int D>
+__device__ __forceinline__ int vt_phys(int r, int c) {
+    if constexpr (D == 128) return c ^ (2 * (r & 3)) ^ (8 * ((r >> 2) & 1));
+    else return c ^ (2 * ((r >> 1) & 1)) ^ (4 * ((r >> 2) & 1));
+}
+
+template <int D, int HPB>
+__global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
+    const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, bf16_t* __restrict__ out, bf16_t* __restrict__ kc,
+    bf16_t* __restrict__ vc, int64_t ctx, int B, int S, int nh, int nkv, float scale_log2) {
+    using C = PrefillCfg<D>;
+    constexpr int NT = 128 * HPB, NW = NT / 64;
+    constexpr int CH = D / 8;                        // 16-byte chunks per row
+    constexpr int RPI = 64 / CH;                     // rows per 1 KiB direct load
+    constexpr int LOADS = C::BKV / RPI;              // direct loads per K (or V) tile
+    constexpr int LPW = (2 * LOADS) / NW;            // direct loads per wave per iteration (K and V)
+    static_assert((2 * LOADS) % NW == 0, "loads split evenly over the waves");
+    constexpr int KH = C::KC32 / 2;
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    __shared__ __align__(16) bf16_t sK[2][C::K_ELEMS];
+    __shared__ __align__(16) bf16_t sV[2][C::V_ELEMS];
+
+    const int g = nh / nkv;
+    const int hchunks = g / HPB;
+    const int nqb = (S + C::BQ - 1) / C::BQ;
+    const int per_qb = B * nkv * hchunks;
+    const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / per_qb;
+    int rem = static_cast<int>(blockIdx.x) % per_qb;
+    const int hc = rem % hchunks;
+    rem /= hchunks;
+    const int c = rem % nkv;
+    const int b = rem / nkv;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    const int h = c * g + hc * HPB + (wave >> 1);
+    const int64_t rs = static_cast<int64_t>(nh + 2 * nkv) * D;  // packed row stride
+    const bf16_t* qkv_b = qkv + static_cast<int64_t>(b) * S * rs;
+    const int q0 = qb * C::BQ + (wave & 1) * 32;
+
+    // ---- Q fragments (B operand of S^T = K Q^T): lane holds query q0 + qf*16 + lrow, dims k*32 + lgrp*8 ..
+    bf16x8 qfr[2][C::KC32];
+#pragma unroll
+    for (int qf = 0; qf < 2; ++qf) {
+        const int qi = q0 + qf * 16 + lrow;
+        const int qs = qi < S ? qi : S - 1;
+        const bf16_t* qp = qkv_b + static_cast<int64_t>(qs) * rs + static_cast<int64_t>(h) * D;
+#pragma unroll
+        for (int k = 0; k < C::KC32; ++k) {
+            float f[8];
+            unpack8(*reinterpret_cast<const uint4*>(qp + k * 32 + lgrp * 8), f);
+            // fold log2(e)/sqrt(d) into q: the scores come out in log2 units, ready for exp2
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] *= scale_log2;
+            uint4 u = pack8(f);
+            if (qi >= S) u = make_uint4(0, 0, 0, 0);
+            qfr[qf][k] = __builtin_bit_cast(bf16x8, u);
+        }
+    }
+
+    // ---- direct tile loads. Load q (0 .. 2*LOADS-1; q < LOADS: K, else V) covers rows (q % LOADS)*RPI ..
+    // + RPI-1 of the tile; lane l lands at physical chunk l % CH of row l / CH and fetches the logical
+    // chunk the swizzle puts there. Keys past S read the clamped row S-1 (masked, zero weight).
+    const bf16_t* kbase = qkv_b + static_cast<int64_t>(nh + c) * D;
+    const bf16_t* vbase = qkv_b + static_cast<int64_t>(nh + nkv + c) * D;
+
+    // ---- cache append: the first head chunk of each query block copies the block's own keys and
+    // values (its diagonal tile) to their slots, so every token is written exactly once
+    if (kc != nullptr && hc == 0) {
+        const int64_t* pos_b = pos + static_cast<int64_t>(b) * S;
+        for (int job = tid; job < 2 * C::BKV * CH; job += NT) {
+            const bool isv = job >= C::BKV * CH;
+            const int jj = isv ? job - C::BKV * CH : job;
+            const int r = jj / CH, ch = jj % CH;
+            const int key = qb * C::BKV + r;
+            if (key < S) {
+                const int64_t slot = clamp_pos(pos_b[key], ctx);
+                const uint4 v = *reinterpret_cast<const uint4*>((isv ? vbase : kbase) + static_cast<int64_t>(key) * rs + ch * 8);
+                bf16_t* dst = (isv ? vc : kc) + ((static_cast<int64_t>(b) * ctx + slot) * nkv + c) * D + ch * 8;
+                *reinterpret_cast<uint4*>(dst) = v;
+            }
+        }
+    }
+    auto issue_tiles = [&](int ktile, int kbuf, int vtile, int vbuf) {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int q = wave * LPW + i;
+            const bool isv = q >= LOADS;
+            const int r = (q % LOADS) * RPI + lane / CH, pc = lane % CH;
+            const int key = min((isv ? vtile : ktile) * C::BKV + r, S - 1);
+            const int lc = isv ? vt_phys<D>(r, pc) : k_phys<D>(r, pc);
+            const bf16_t* src = (isv ? vbase : kbase) + static_cast<int64_t>(key) * rs + lc * 8;
+            bf16_t* dst = isv ? &sV[vbuf][(q % LOADS) * RPI * D] : &sK[kbuf][(q % LOADS) * RPI * D];
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        }
+    };
+    auto issue_k_only = [&](int ktile, int kbuf) {   // prologue: K of tile 1
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int q = wave * LPW + i;
+            if (q < LOADS) {
+                const int r = q * RPI + lane / CH, pc = lane % CH;
+                const int key = min(ktile * C::BKV + r, S - 1);
+                const bf16_t* src = kbase + static_cast<int64_t>(key) * rs + k_phys<D>(r, pc) * 8;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                                 (__attribute__((address_space(3))) void*)&sK[kbuf][q * RPI * D], 16, 0, 0);
+            }
+        }
+    };
+
+    // Q K^T k steps [k0, k0 + KH) of the tile in K buffer kb into accumulators SN
+#define PD_QK_HALF(SN, kb, k0)                                                                             \
+    _Pragma("unroll") for (int k = (k0); k < (k0) + KH; ++k) {                                             \
+        _Pragma("unroll") for (int kf = 0; kf < 4; ++kf) {                                                 \
+            const int r = kf * 16 + lrow;                                                                  \
+            const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&sK[kb][r * D + k_phys<D>(r, k * 4 + lgrp) * 8]); \
+            SN[kf][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qfr[0][k], SN[kf][0], 0, 0, 0);        \
+            SN[kf][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qfr[1][k], SN[kf][1], 0, 0, 0);        \
+        }                                                                                                  \
+    }
+    // O^T += V^T P^T for the 32 keys of half t (V buffer vb); V^T fragments by two transposing reads
+#define PD_PV_HALF(vb, t)                                                                                  \
+    _Pragma("unroll") for (int a = 0; a < C::DF; ++a) {                                                    \
+        s16x4 h_[2];                                                                                       \
+        _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                    \
+            const int r = 32 * (t) + 16 * u + 4 * lgrp + (lrow >> 2);                                      \
+            const int cc = 2 * a + ((lrow & 3) >> 1);                                                      \
+            h_[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(      \
+                &sV[vb][r * D + vt_phys<D>(r, cc) * 8 + (lrow & 1) * 4]));                                 \
+        }                                                                                                  \
+        const bf16x8 vfr = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h_[0], h_[1], 0, 1, 2, 3, 4, 5, 6, 7)); \
+        oacc[a][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, pfr[0][t], oacc[a][0], 0, 0, 0);          \
+        oacc[a][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, pfr[1][t], oacc[a][1], 0, 0, 0);          \
+    }
+#define PD_EXP_HALF(SC, t)                                                                                 \
+    _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                                     \
+        float p_[2][4];                                                                                    \
+        _Pragma("unroll") for (int u = 0; u < 2; ++u)                                                      \
+            _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                                \
+                p_[u][r] = fast_exp2(SC[2 * (t) + u][qf][r]);                                              \
+                ls[qf] += p_[u][r];                                                                        \
+            }                                                                                              \
+        uint4 u_;                                                                                          \
+        u_.x = pack_bf16x2(p_[0][0], p_[0][1]);                                                            \
+        u_.y = pack_bf16x2(p_[0][2], p_[0][3]);                                                            \
+        u_.z = pack_bf16x2(p_[1][0], p_[1][1]);                                                            \
+        u_.w = pack_bf16x2(p_[1][2], p_[1][3]);                                                            \
+        pfr[qf][t] = __builtin_bit_cast(bf16x8, u_);                                                       \
+    }
+
+    float m_i[2] = {0.f, 0.f}, l_i[2] = {0.f, 0.f};
+    f32x4 oacc[C::DF][2];
+#pragma unroll
+    for (int a = 0; a < C::DF; ++a) oacc[a][0] = oacc[a][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 sA[4][2], sB[4][2];
+    float mbA[2] = {0.f, 0.f}, mbB[2] = {0.f, 0.f};   // reference max each accumulator set started from
+    bf16x8 pfr[2][2];
+
+    const int nkt = qb + 1;
+    issue_tiles(0, 0, 0, 0);
+    issue_k_only(1, 1);
+    __syncthreads();
+#pragma unroll
+    for (int kf = 0; kf < 4; ++kf) sA[kf][0] = sA[kf][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    PD_QK_HALF(sA, 0, 0)
+    PD_QK_HALF(sA, 0, KH)
+    __syncthreads();   // K buffer 0 is refilled by the first iteration
+
+    // One iteration: tile j's scores are in SC (started from MBC); SN/MBN receive tile j+1. Every
+    // iteration issues the same work (past the end: clamped rows into buffers nobody reads), so each
+    // stage is one basic block in which matrix ops and vector work interleave.
+#define PD_ITER(SC, MBC, SN, MBN)                                                                          \
+    {                                                                                                      \
+        const bool first_ = j == 0;                                                                        \
+        /* K(j+2) into the buffer K(j) used, V(j+1) into the buffer V(j-1) used: both free since the */    \
+        /* barrier that ended the previous iteration                                                 */    \
+        issue_tiles(j + 2, j & 1, j + 1, (j + 1) & 1);                                                     \
+        if (j == nkt - 1) {                                                                                \
+            _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                             \
+                const int qi = q0 + qf * 16 + lrow;                                                        \
+                _Pragma("unroll") for (int kf = 0; kf < 4; ++kf)                                           \
+                    _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                        \
+                        const int key = j * C::BKV + kf * 16 + 4 * lgrp + r;                               \
+                        if (key > qi || key >= S) SC[kf][qf][r] = -INFINITY;                               \
+                    }                                                                                      \
+            }                                                                                              \
+        }                                                                                                  \
+        /* stage 1: first half of tile j+1's scores || column max of tile j */                            \
+        _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                                 \
+            MBN[qf] = first_ ? 0.f : m_i[qf];                                                              \
+            _Pragma("unroll") for (int kf = 0; kf < 4; ++kf) SN[kf][qf] = f32x4{-MBN[qf], -MBN[qf], -MBN[qf], -MBN[qf]}; \
+        }                                                                                                  \
+        PD_QK_HALF(SN, (j + 1) & 1, 0)                                                                     \
+        float sub_[2], shift_[2];                                                                          \
+        bool any_sub_ = false;                                                                             \
+        _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                                 \
+            float mx = -INFINITY;                                                                          \
+            _Pragma("unroll") for (int kf = 0; kf < 4; ++kf)                                               \
+                _Pragma("unroll") for (int r = 0; r < 4; ++r) mx = fmaxf(mx, SC[kf][qf][r]);               \
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));                                                        \
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                                                        \
+            const float delta = first_ ? 0.f : m_i[qf] - MBC[qf];                                          \
+            const float rel = mx - delta;                                                                  \
+            shift_[qf] = (first_ || rel > kSlack) ? rel : 0.f;                                             \
+            sub_[qf] = delta + shift_[qf];                                                                 \
+            any_sub_ |= sub_[qf] != 0.f;                                                                   \
+        }                                                                                                  \
+        /* stage 2 (rare): re-reference tile j's scores, rescale O and l where the reference moved */     \
+        if (__any(any_sub_)) {                                                                             \
+            _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                             \
+                const float alpha = first_ ? 1.f : fast_exp2(-shift_[qf]);                                 \
+                m_i[qf] = (first_ ? MBC[qf] : m_i[qf]) + shift_[qf];                                       \
+                l_i[qf] *= alpha;                                                                          \
+                _Pragma("unroll") for (int a = 0; a < C::DF; ++a) oacc[a][qf] *= alpha;                    \
+                _Pragma("unroll") for (int kf = 0; kf < 4; ++kf) SC[kf][qf] -= sub_[qf];                   \
+            }                                                                                              \
+        }                                                                                                  \
+        float ls[2] = {0.f, 0.f};                                                                          \
+        /* stage 3: second half of tile j+1's scores || exponentials of keys 0..31 */                      \
+        PD_QK_HALF(SN, (j + 1) & 1, KH)                                                                    \
+        PD_EXP_HALF(SC, 0)                                                                                 \
+        /* stage 4: P V of keys 0..31 || exponentials of keys 32..63 */                                    \
+        PD_PV_HALF(j & 1, 0)                                                                               \
+        PD_EXP_HALF(SC, 1)                                                                                 \
+        /* stage 5: P V of keys 32..63 */                                                                  \
+        PD_PV_HALF(j & 1, 1)                                                                               \
+        l_i[0] += ls[0];                                                                                   \
+        l_i[1] += ls[1];                                                                                   \
+        __syncthreads();                                                                                   \
+    }
+    for (int j = 0; j < nkt; j += 2) {
+        PD_ITER(sA, mbA, sB, mbB)
+        if (j + 1 >= nkt) break;
+        {
+            const int j_ = j;
+            {
+                const int j = j_ + 1;
+                PD_ITER(sB, mbB, sA, mbA)
+            }
+        }
+    }
+#undef PD_ITER
+#undef PD_QK_HALF
+#undef PD_PV_HALF
+#undef PD_EXP_HALF
 
     // ---- normalise and store: lane holds dims a*16 + 4 lgrp + {0..3} of query q0 + qf*16 + lrow
 #pragma unroll
@@ -834,10 +1117,15 @@ static hipError_t prefill_go(const void* qkv, const int64_t* pos, const RopeTab*
     const int nqb = (S + 63) / 64;
     const unsigned blocks = static_cast<unsigned>(nqb) * B * nkv * (g / HPB);
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
-    hipLaunchKernelGGL((attn_prefill_mfma_kernel<D, HPB, ROPE, IL>), dim3(blocks), dim3(128 * HPB), 0, st,
-                       static_cast<const bf16_t*>(qkv), pos, tab ? tab->cs : nullptr, tab ? tab->rows : 1,
-                       static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv,
-                       scale_log2);
+    if constexpr (!ROPE)
+        hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB>), dim3(blocks), dim3(128 * HPB), 0, st,
+                           static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
+                           static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2);
+    else
+        hipLaunchKernelGGL((attn_prefill_mfma_kernel<D, HPB, ROPE, IL>), dim3(blocks), dim3(128 * HPB), 0, st,
+                           static_cast<const bf16_t*>(qkv), pos, tab ? tab->cs : nullptr, tab ? tab->rows : 1,
+                           static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, B, S, nh,
+                           nkv, scale_log2);
     return hipGetLastError();
 }
 
