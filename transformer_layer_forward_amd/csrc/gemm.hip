@@ -271,7 +271,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_big_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float g = acc[a][b][r], u = acc[a + 1][b][r];
-                    o[r] = g / (1.f + __expf(-g)) * u;
+                    o[r] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
                 }
                 if (vec_ok && n + 3 < N) {
                     *reinterpret_cast<uint2*>(crow + n) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
@@ -356,27 +356,36 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     // ---- direct loads: instruction j (0..15) of this wave fills the 128-byte segments of stage rows
     // 32(j % 8) + 8*wave + lane/8 of the X (j < 8) or W (j >= 8) half; lane l lands at physical chunk
     // l % 8, so it fetches the logical chunk cj that the row swizzle puts there (the same for every j).
-    // Rows past M or N read a clamped valid row; their results are never stored.
+    // Rows past M or N read a clamped valid row; their results are never stored. The loads are buffer
+    // loads (MUBUF) into LDS: descriptors based at the tile's first token row and first weight row,
+    // per-lane byte offsets fixed per instruction, the stage's k offset in the scalar offset. (The
+    // global_load_lds form is a flat-segment op, after which the compiler can only wait for all LDS
+    // reads at once, lgkmcnt(0), where the buffer form lets it wait for just the oldest ones.)
     const int rsub = 8 * wave + (lane >> 3);
     const int cj = (lane & 7) ^ mf_swz(rsub);
-    auto issue1 = [&](int slot, int k0, int j) {
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(X + static_cast<int64_t>(m0) * K), (short)0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(W + static_cast<int64_t>(n0) * K), (short)0, -1, 0x00020000);
+    uint32_t voff[MF_LPW];
+#pragma unroll
+    for (int j = 0; j < MF_LPW; ++j) {
         const int r = 32 * (j & 7) + rsub;
-        const bf16_t* src;
+        int row;
         if (j < 8) {
-            src = X + static_cast<int64_t>(min(m0 + r, M - 1)) * K;
+            row = min(m0 + r, M - 1) - m0;
+        } else if (EPI == EPI_SILU) {   // 16-row blocks alternate W_gate and W_up rows of the same columns
+            const int blk = r >> 4, col = min(n0 + (blk >> 1) * 16 + (r & 15), N - 1);
+            row = ((blk & 1) ? N + col : col) - n0;
         } else {
-            int grow;
-            if (EPI == EPI_SILU) {      // 16-row blocks alternate W_gate and W_up rows of the same columns
-                const int blk = r >> 4, col = min(n0 + (blk >> 1) * 16 + (r & 15), N - 1);
-                grow = (blk & 1) ? N + col : col;
-            } else {
-                grow = min(n0 + r, N - 1);
-            }
-            src = W + static_cast<int64_t>(grow) * K;
+            row = min(n0 + r, N - 1) - n0;
         }
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(src + k0 + cj * 8),
-            (__attribute__((address_space(3))) void*)(smem + slot * MF_STAGE + (4 * j + wave) * 8 * MF_K), 16, 0, 0);
+        voff[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>(cj) * 16u;
+    }
+    auto issue1 = [&](int slot, int k0, int j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            j < 8 ? rx : rw, (__attribute__((address_space(3))) void*)(smem + slot * MF_STAGE + (4 * j + wave) * 8 * MF_K),
+            16, voff[j], k0 * 2, 0, 0);
     };
     // operand fragment offsets within a stage (A: weight rows, B: tokens), one per 32-row block; k16
     // quarter q of a fragment sits at chunk (2q + lh) ^ swizzle = chunk(0) ^ 2q, i.e. offset(0) ^ 16q
@@ -477,7 +486,7 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const float gt = acc[a][b][4 * g + q], up = acc[a][b][4 * g + q + 8];
-                        o[q] = gt / (1.f + __expf(-gt)) * up;
+                        o[q] = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
                     }
                     const int c = 16 * a + 8 * g + 4 * lh;
                     *reinterpret_cast<uint2*>(lds_at(m, c)) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
@@ -825,7 +834,11 @@ hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C
             default: return skinny_launch<EPI_SILU>(X, W, C, R, M, N, K, ws, st);
         }
     }
-    if (epi != EPI_ROPE && K % MF_K == 0 && N % 8 == 0) {
+    // the 4-wave kernel addresses operands by 32-bit byte offsets from its tile's first rows: 256 token
+    // rows, and 256 weight rows (gate_up: up to row 2N - 1)
+    const int64_t wspan = epi == EPI_SILU ? 2 * N : MF_N;
+    const bool mf_offsets_ok = 2 * wspan * K < (int64_t(1) << 32) && 2 * int64_t(MF_M) * K < (int64_t(1) << 32);
+    if (epi != EPI_ROPE && K % MF_K == 0 && N % 8 == 0 && mf_offsets_ok) {
         switch (epi) {
             case EPI_STORE: return mfma32_launch<EPI_STORE>(X, W, C, R, M, N, K, st);
             case EPI_RESIDUAL: return mfma32_launch<EPI_RESIDUAL>(X, W, C, R, M, N, K, st);
