@@ -399,6 +399,21 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_mfma_kernel(
 //    overlaps its second half of exponentials; K runs one tile ahead of V (two buffers each). Score
 //    accumulators start at minus the reference max the wave held when they were issued; a moved
 //    reference (rare: only by more than kSlack) is corrected under a wave-uniform branch.
+// max / sum over lanes l, l^16, l^32, l^48 (the four 16-lane rows of a wave) with the gfx950 lane
+// swaps: vector ALU only, so unlike an LDS-routed shuffle it does not wait behind pending LDS reads
+__device__ __forceinline__ float rows_max(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D>
 __device__ __forceinline__ int vt_phys(int r, int c) {
     if constexpr (D == 128) return c ^ (2 * (r & 3)) ^ (8 * ((r >> 2) & 1));
@@ -432,7 +447,8 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     const int c = rem % nkv;
     const int b = rem / nkv;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar descriptor choice
     const int lrow = lane & 15, lgrp = lane >> 4;
     const int h = c * g + hc * HPB + (wave >> 1);
     const int64_t rs = static_cast<int64_t>(nh + 2 * nkv) * D;  // packed row stride
@@ -461,9 +477,15 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
 
     // ---- direct tile loads. Load q (0 .. 2*LOADS-1; q < LOADS: K, else V) covers rows (q % LOADS)*RPI ..
     // + RPI-1 of the tile; lane l lands at physical chunk l % CH of row l / CH and fetches the logical
-    // chunk the swizzle puts there. Keys past S read the clamped row S-1 (masked, zero weight).
+    // chunk the swizzle puts there. Keys past S read the clamped row S-1 (masked, zero weight). Buffer
+    // (MUBUF) loads based at this kv head's first K and V element, with 32-bit byte offsets (the
+    // caller checks S * row stride fits); unlike the flat-segment form they let the compiler wait for
+    // individual LDS reads rather than all of them.
     const bf16_t* kbase = qkv_b + static_cast<int64_t>(nh + c) * D;
     const bf16_t* vbase = qkv_b + static_cast<int64_t>(nh + nkv + c) * D;
+    const uint32_t rs_bytes = static_cast<uint32_t>(rs) * 2u;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kbase), (short)0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vbase), (short)0, -1, 0x00020000);
 
     // ---- cache append: the first head chunk of each query block copies the block's own keys and
     // values (its diagonal tile) to their slots, so every token is written exactly once
@@ -490,10 +512,10 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
             const int r = (q % LOADS) * RPI + lane / CH, pc = lane % CH;
             const int key = min((isv ? vtile : ktile) * C::BKV + r, S - 1);
             const int lc = isv ? vt_phys<D>(r, pc) : k_phys<D>(r, pc);
-            const bf16_t* src = (isv ? vbase : kbase) + static_cast<int64_t>(key) * rs + lc * 8;
+            const uint32_t off = static_cast<uint32_t>(key) * rs_bytes + static_cast<uint32_t>(lc) * 16u;
             bf16_t* dst = isv ? &sV[vbuf][(q % LOADS) * RPI * D] : &sK[kbuf][(q % LOADS) * RPI * D];
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (__attribute__((address_space(3))) void*)dst, 16,
+                                                     off, 0, 0, 0);
         }
     };
     auto issue_k_only = [&](int ktile, int kbuf) {   // prologue: K of tile 1
@@ -503,9 +525,9 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
             if (q < LOADS) {
                 const int r = q * RPI + lane / CH, pc = lane % CH;
                 const int key = min(ktile * C::BKV + r, S - 1);
-                const bf16_t* src = kbase + static_cast<int64_t>(key) * rs + k_phys<D>(r, pc) * 8;
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                                 (__attribute__((address_space(3))) void*)&sK[kbuf][q * RPI * D], 16, 0, 0);
+                const uint32_t off = static_cast<uint32_t>(key) * rs_bytes + static_cast<uint32_t>(k_phys<D>(r, pc)) * 16u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)&sK[kbuf][q * RPI * D],
+                                                         16, off, 0, 0, 0);
             }
         }
     };
@@ -599,8 +621,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
             float mx = -INFINITY;                                                                          \
             _Pragma("unroll") for (int kf = 0; kf < 4; ++kf)                                               \
                 _Pragma("unroll") for (int r = 0; r < 4; ++r) mx = fmaxf(mx, SC[kf][qf][r]);               \
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));                                                        \
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                                                        \
+            mx = rows_max(mx);                                                                             \
             const float delta = first_ ? 0.f : m_i[qf] - MBC[qf];                                          \
             const float rel = mx - delta;                                                                  \
             shift_[qf] = (first_ || rel > kSlack) ? rel : 0.f;                                             \
@@ -649,10 +670,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     // ---- normalise and store: lane holds dims a*16 + 4 lgrp + {0..3} of query q0 + qf*16 + lrow
 #pragma unroll
     for (int qf = 0; qf < 2; ++qf) {
-        float l = l_i[qf];
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
-        const float inv = 1.f / l;
+        const float inv = 1.f / rows_sum(l_i[qf]);
         const int qi = q0 + qf * 16 + lrow;
         if (qi >= S) continue;
         bf16_t* op = out + (static_cast<int64_t>(b) * S + qi) * nh * D + static_cast<int64_t>(h) * D;
@@ -1117,7 +1135,8 @@ static hipError_t prefill_go(const void* qkv, const int64_t* pos, const RopeTab*
     const int nqb = (S + 63) / 64;
     const unsigned blocks = static_cast<unsigned>(nqb) * B * nkv * (g / HPB);
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
-    if constexpr (!ROPE)
+    const bool offsets_ok = static_cast<int64_t>(S) * (nh + 2 * nkv) * D * 2 < (int64_t(1) << 32);
+    if (!ROPE && offsets_ok)
         hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB>), dim3(blocks), dim3(128 * HPB), 0, st,
                            static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
                            static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2);
