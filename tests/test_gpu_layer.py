@@ -62,6 +62,11 @@ SMALL = [
     scaled(CONFIGS["llama3_8b_prefill"], B=1, S=129, rope=RopeCfg(type="linear", theta=500000.0, factor=4.0,
                                                                   interleaved=True)),
     scaled(CONFIGS["llama3_8b_long_llama3rope"], S=300),
+    scaled(CONFIGS["llama32_1b_prefill"], B=1, S=90, rope=RopeCfg(type="llama3", theta=500000.0, factor=32.0,
+                                                                  original_max_pos=64, interleaved=True)),
+    # d = 64 with (n_h + n_kv) odd: the rotated q/k columns end half-way through a 128-column block
+    scaled(CONFIGS["llama32_1b_prefill"], name="d64_odd_heads", B=1, S=150, hidden=384, n_heads=6, n_kv_heads=3,
+           intermediate=512),
 ]
 
 

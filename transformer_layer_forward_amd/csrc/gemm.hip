@@ -329,13 +329,15 @@ __device__ __forceinline__ int mf_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); 
 
 #define MF_WAITVM0() __builtin_amdgcn_s_waitcnt(0x0F70)   // vmcnt(0) only
 
-template <int EPI>
+template <int EPI, int RD = 0>
 __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, const bf16_t* __restrict__ R,
-    int M, int N, int K, int tiles_m, int tiles_n) {
-    static_assert(EPI == EPI_STORE || EPI == EPI_RESIDUAL || EPI == EPI_SILU, "no fused RoPE in this kernel");
+    int M, int N, int K, int tiles_m, int tiles_n, const int64_t* __restrict__ rpos, const float2* __restrict__ rcs,
+    int64_t rrows, int rope_cols, int ril) {
+    static_assert(EPI != EPI_ROPE || RD == 64 || RD == 128, "fused RoPE for head sizes 64 and 128");
     extern __shared__ __align__(16) bf16_t smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
     const int wn = wave & 1, wm = wave >> 1;
     const int l32 = lane & 31, lh = lane >> 5;
 
@@ -476,6 +478,38 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const int m = 32 * b + l32;
+        if constexpr (EPI == EPI_ROPE) {
+            // rotate q/k columns in fp32 before the single rounding. The wave's 128 columns start on a
+            // head boundary, so block a covers head dims (32a) % RD ..; a lane's register i of block a
+            // is dim 8(i/4) + 4*lh + i%4 of it. Half-split: its partner (dim + RD/2) is the same
+            // register of block a + RD/64; interleaved: the neighbouring register.
+            const float2* cs_row = rcs + clamp_pos(rpos[min(mw + m, M - 1)], rrows) * (RD / 2);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                if (nw + 32 * a >= rope_cols) continue;   // value columns
+                const int jb = (32 * a) % RD;
+                if (!ril) {
+                    constexpr int PA = RD / 64;
+                    if (jb < RD / 2) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const float2 t = cs_row[jb + 8 * (i / 4) + 4 * lh + i % 4];
+                            const float x = acc[a][b][i], y = acc[a + PA][b][i];
+                            acc[a][b][i] = x * t.x - y * t.y;
+                            acc[a + PA][b][i] = y * t.x + x * t.y;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; i += 2) {
+                        const float2 t = cs_row[(jb + 8 * (i / 4) + 4 * lh + i % 4) >> 1];
+                        const float x = acc[a][b][i], y = acc[a][b][i + 1];
+                        acc[a][b][i] = x * t.x - y * t.y;
+                        acc[a][b][i + 1] = y * t.x + x * t.y;
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             if constexpr (EPI == EPI_SILU) {
@@ -749,20 +783,21 @@ static hipError_t big_launch(const void* X, const void* W, void* C, const void* 
     return big_launch_t<EPI, false, RD>(X, W, C, R, M, N, K, st, re);
 }
 
-template <int EPI>
+template <int EPI, int RD = 0>
 static hipError_t mfma32_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N,
-                                int64_t K, hipStream_t st) {
+                                int64_t K, hipStream_t st, const RopeEpi* re = nullptr) {
     static bool attr = [] {
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_mfma32_kernel<EPI>),
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_mfma32_kernel<EPI, RD>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, MF_LDS_BYTES) == hipSuccess;
     }();
     if (!attr) return hipErrorInvalidConfiguration;
     const int ncols = EPI == EPI_SILU ? MF_N / 2 : MF_N;
     const int tm = static_cast<int>((M + MF_M - 1) / MF_M), tn = static_cast<int>((N + ncols - 1) / ncols);
-    hipLaunchKernelGGL(gemm_bf16_mfma32_kernel<EPI>, dim3(tm * tn), dim3(MF_THREADS), MF_LDS_BYTES, st,
+    hipLaunchKernelGGL((gemm_bf16_mfma32_kernel<EPI, RD>), dim3(tm * tn), dim3(MF_THREADS), MF_LDS_BYTES, st,
                        static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), static_cast<bf16_t*>(C),
                        static_cast<const bf16_t*>(R), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tm,
-                       tn);
+                       tn, re ? re->pos : nullptr, re ? re->tab.cs : nullptr, re ? re->tab.rows : 1,
+                       re ? re->rope_cols : 0, re ? re->interleaved : 0);
     return hipGetLastError();
 }
 
@@ -838,10 +873,14 @@ hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C
     // rows, and 256 weight rows (gate_up: up to row 2N - 1)
     const int64_t wspan = epi == EPI_SILU ? 2 * N : MF_N;
     const bool mf_offsets_ok = 2 * wspan * K < (int64_t(1) << 32) && 2 * int64_t(MF_M) * K < (int64_t(1) << 32);
-    if (epi != EPI_ROPE && K % MF_K == 0 && N % 8 == 0 && mf_offsets_ok) {
+    const bool mf_rope_ok = epi != EPI_ROPE || re->d == 64 || re->d == 128;
+    if (K % MF_K == 0 && N % 8 == 0 && mf_offsets_ok && mf_rope_ok) {
         switch (epi) {
             case EPI_STORE: return mfma32_launch<EPI_STORE>(X, W, C, R, M, N, K, st);
             case EPI_RESIDUAL: return mfma32_launch<EPI_RESIDUAL>(X, W, C, R, M, N, K, st);
+            case EPI_ROPE:
+                if (re->d == 128) return mfma32_launch<EPI_ROPE, 128>(X, W, C, R, M, N, K, st, re);
+                return mfma32_launch<EPI_ROPE, 64>(X, W, C, R, M, N, K, st, re);
             default: return mfma32_launch<EPI_SILU>(X, W, C, R, M, N, K, st);
         }
     }
