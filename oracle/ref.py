@@ -205,6 +205,33 @@ def attention_one_query(q: np.ndarray, keys: np.ndarray, values: np.ndarray) -> 
     return out.reshape(nh * d)
 
 
+def attention_chunk(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, positions: np.ndarray,
+                    cache_k: np.ndarray, cache_v: np.ndarray):
+    """Chunked prefill on a cache prefix ([llama3] §3.2: cache_k[:bsz, start_pos : start_pos + seqlen] = xk,
+    then keys = cache_k[:bsz, : start_pos + seqlen]; [meta-qa] #### 5: for start_pos > 0 the mask is the
+    causal triangle preceded by start_pos zero columns).
+
+    q [B,S,n_h,d] and k_new [B,S,n_kv,d] already rotated, v_new [B,S,n_kv,d], positions [B,S];
+    cache_k/cache_v [B,ctx,n_kv,d] before the write. The chunk's keys and values are written at their
+    positions first; query (b, s) then attends over cache slots 0 .. positions[b, s].
+    Returns o [B,S,n_h*d] and the caches after the write.
+    """
+    K = np.array(cache_k, dtype=F64, copy=True)
+    V = np.array(cache_v, dtype=F64, copy=True)
+    B, S = positions.shape
+    for b in range(B):
+        for s in range(S):
+            K[b, int(positions[b, s])] = k_new[b, s]
+            V[b, int(positions[b, s])] = v_new[b, s]
+    nh, d = q.shape[2], q.shape[3]
+    o = np.empty((B, S, nh * d), dtype=F64)
+    for b in range(B):
+        for s in range(S):
+            p = int(positions[b, s])
+            o[b, s] = attention_one_query(np.asarray(q[b, s], dtype=F64), K[b, :p + 1], V[b, :p + 1])
+    return o, K, V
+
+
 # ---------------------------------------------------------------- MLP
 def silu(z: np.ndarray) -> np.ndarray:
     """silu(z) = z * sigmoid(z) = z / (1 + e^-z) ([nju] "SwiGLU模块")."""
@@ -291,6 +318,27 @@ def layer_prefill_rows(cfg, W: dict, x: np.ndarray, position_ids: np.ndarray, kv
     for key in res:
         res[key] = np.stack([row[key] for row in out_rows])
     return res
+
+
+def layer_prefill_chunk(cfg, W: dict, x: np.ndarray, position_ids: np.ndarray, kv_seq_len: int,
+                        cache_k: np.ndarray, cache_v: np.ndarray) -> dict:
+    """The decoder layer over a chunk of S tokens per sequence that continues a cached prefix
+    ([llama3] §3.2 with start_pos > 0 and seqlen > 1; [meta-qa] #### 5 mask with start_pos zero
+    columns): as layer_prefill, except that attention is attention_chunk over the caches
+    (cache_k/cache_v [B,ctx,n_kv,d] before the call). Returns the layer outputs and the caches after."""
+    x = np.asarray(x, dtype=F64)
+    xn = rmsnorm(x, W["g_attn"], cfg.eps)
+    qkv = linear(xn, W["w_qkv"])
+    q, k, v = split_qkv(qkv, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim)
+    qr, kr = _rope_qk(cfg, q, k, np.asarray(position_ids), kv_seq_len)
+    o, K, V = attention_chunk(qr, kr, v, np.asarray(position_ids), cache_k, cache_v)
+    attn_proj = linear(o, W["w_o"])
+    h = attn_proj + x
+    hn = rmsnorm(h, W["g_mlp"], eps=cfg.eps)
+    act = swiglu_act(hn, W["w_gate_up"], cfg.intermediate)
+    mlp_out = linear(act, W["w_down"])
+    return {"o": o, "attn_proj": attn_proj, "h": h, "act": act, "mlp_out": mlp_out, "out": h + mlp_out,
+            "k_rot": kr, "v": v, "cache_k": K, "cache_v": V}
 
 
 def layer_decode(cfg, W: dict, x: np.ndarray, pos: np.ndarray, kv_seq_len: int, cache_row_k, cache_row_v,

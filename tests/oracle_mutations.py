@@ -41,6 +41,12 @@ MUTS = [
     ("decode new key unrotated", "        K[p] = kr\n", "        K[p] = k\n"),
     ("decode attends p slots", "K = cache_row_k(b)[:p + 1].copy()\n        V = cache_row_v(b)[:p + 1].copy()", "K = cache_row_k(b)[:p + 2].copy()\n        V = cache_row_v(b)[:p + 2].copy()"),
     ("softmax sum over all rows", "return p / np.sum(p, axis=-1, keepdims=True)", "return p / np.sum(p)"),
+    ("chunk attends one slot too many", "o[b, s] = attention_one_query(np.asarray(q[b, s], dtype=F64), K[b, :p + 1], V[b, :p + 1])", "o[b, s] = attention_one_query(np.asarray(q[b, s], dtype=F64), K[b, :p + 2], V[b, :p + 2])"),
+    ("chunk v not written", "            V[b, int(positions[b, s])] = v_new[b, s]\n", "            pass\n"),
+    ("chunk writes slot by index", "            K[b, int(positions[b, s])] = k_new[b, s]", "            K[b, s] = k_new[b, s]"),
+    ("chunk layer unrotated k", "o, K, V = attention_chunk(qr, kr, v, np.asarray(position_ids), cache_k, cache_v)", "o, K, V = attention_chunk(qr, k, v, np.asarray(position_ids), cache_k, cache_v)"),
+    ("chunk attn residual dropped", "    h = attn_proj + x\n", "    h = attn_proj\n"),
+    ("chunk second norm uses g_attn", "hn = rmsnorm(h, W[\"g_mlp\"], eps=cfg.eps)", "hn = rmsnorm(h, W[\"g_attn\"], eps=cfg.eps)"),
     ("rows path second norm eps", "hn = rmsnorm(h, W[\"g_mlp\"], cfg.eps)\n            act", "hn = rmsnorm(h, W[\"g_mlp\"], 0.1)\n            act"),
 ]
 results = []

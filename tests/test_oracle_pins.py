@@ -375,6 +375,78 @@ def test_decode_equals_prefill_last_row():
     np.testing.assert_allclose(dec["k_new"], full["k_rot"][:, 12].reshape(2, -1), rtol=1e-13, atol=1e-14)
 
 
+# ------------------------------------------------------------------ chunked prefill on a cache prefix
+def test_attention_chunk_empty_prefix_equals_prefill():
+    """llama3 结构详解 §3.2 with start_pos = 0: a chunk at positions 0..S-1 writes its own keys to the
+    cache and attends over them causally, exactly the one-call prefill (junk in other slots unused)."""
+    B, S, nh, nkv, d, ctx = 2, 9, 4, 2, 16, 13
+    q, k, v = _qkv(B, S, nh, nkv, d)
+    ck, cv = RNG.standard_normal((B, ctx, nkv, d)), RNG.standard_normal((B, ctx, nkv, d))
+    pos = np.broadcast_to(np.arange(S), (B, S))
+    o, K, V = ref.attention_chunk(q, k, v, pos, ck, cv)
+    np.testing.assert_allclose(o, ref.attention_prefill(q, k, v), rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(K[:, :S], k)
+    np.testing.assert_array_equal(V[:, S:], cv[:, S:])
+
+
+@pytest.mark.parametrize("starts", [(5, 9), (0, 7), (16, 1)])
+def test_attention_chunk_continues_one_shot_prefill(starts):
+    """CSDN answer "#### 5." start_pos > 0: the chunk's rows equal rows start_pos.. of one causal
+    prefill over prefix + chunk, when the cache holds the prefix's keys and values (one-shot reference:
+    attention_prefill, itself pinned to torch's scaled_dot_product_attention)."""
+    B, S, nh, nkv, d, ctx = 2, 6, 4, 2, 16, 32
+    ck, cv = RNG.standard_normal((B, ctx, nkv, d)), RNG.standard_normal((B, ctx, nkv, d))
+    pos = np.stack([np.arange(P, P + S) for P in starts])
+    q = RNG.standard_normal((B, S, nh, d))
+    k = RNG.standard_normal((B, S, nkv, d))
+    v = RNG.standard_normal((B, S, nkv, d))
+    o, K, V = ref.attention_chunk(q, k, v, pos, ck, cv)
+    for b, P in enumerate(starts):
+        qq = np.concatenate([RNG.standard_normal((1, P, nh, d)), q[b:b + 1]], axis=1)
+        kk = np.concatenate([ck[b:b + 1, :P], k[b:b + 1]], axis=1)
+        vv = np.concatenate([cv[b:b + 1, :P], v[b:b + 1]], axis=1)
+        full = ref.attention_prefill(qq, kk, vv)
+        np.testing.assert_allclose(o[b], full[0, P:], rtol=1e-12, atol=1e-13)
+        np.testing.assert_array_equal(K[b, P:P + S], k[b])
+        np.testing.assert_array_equal(K[b, :P], ck[b, :P])
+
+
+def test_attention_chunk_reads_only_slots_up_to_its_position():
+    """Slots after a query's position (later cache contents) cannot change it; a prefix slot can."""
+    B, S, nh, nkv, d, ctx = 1, 4, 2, 1, 8, 20
+    q, k, v = _qkv(B, S, nh, nkv, d)
+    ck, cv = RNG.standard_normal((B, ctx, nkv, d)), RNG.standard_normal((B, ctx, nkv, d))
+    pos = np.array([[7, 8, 9, 10]])
+    o, _, _ = ref.attention_chunk(q, k, v, pos, ck, cv)
+    ck2, cv2 = ck.copy(), cv.copy()
+    ck2[:, 11:] += 3.0
+    cv2[:, 11:] -= 7.0
+    o2, _, _ = ref.attention_chunk(q, k, v, pos, ck2, cv2)
+    np.testing.assert_array_equal(o2, o)
+    cv2[:, 3] += 1.0
+    o3, _, _ = ref.attention_chunk(q, k, v, pos, ck2, cv2)
+    assert not np.array_equal(o3, o)
+
+
+def test_layer_chunk_continues_one_shot_prefill():
+    """The decoder layer over a chunk at positions P..P+S-1 on top of a cache filled from tokens
+    0..P-1 reproduces rows P.. of the one-call layer over all P+S tokens (llama3 结构详解 §3.2)."""
+    base = CONFIGS["tiny_f32"]
+    P, S, ctx = 11, 6, 24
+    cfg = scaled(base, B=2, S=P + S)
+    W = _w64(cfg)
+    x = to_f64(make_hidden(cfg), cfg.dtype)
+    pos = make_prefill_positions(cfg)
+    full = ref.layer_prefill(cfg, W, x, pos, 64)
+    ck = RNG.standard_normal((2, ctx, cfg.n_kv_heads, cfg.head_dim))
+    cv = RNG.standard_normal((2, ctx, cfg.n_kv_heads, cfg.head_dim))
+    ck[:, :P] = full["k_rot"][:, :P]
+    cv[:, :P] = full["v"][:, :P]
+    ch = ref.layer_prefill_chunk(scaled(base, B=2, S=S), W, x[:, P:], pos[:, P:], 64, ck, cv)
+    np.testing.assert_allclose(ch["out"], full["out"][:, P:], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ch["cache_k"][:, P:P + S], full["k_rot"][:, P:], rtol=1e-13, atol=1e-14)
+
+
 # ------------------------------------------------------------------ shapes
 def test_layer_shapes_match_lecture_printout():
     """Golden: the Llama-3.2-1B layer dump on NJU lecture 5 fixes the projection shapes of the
