@@ -111,6 +111,21 @@ ll_status llama_layer_forward(const ll_layer_cfg* cfg, const ll_layer_weights* w
                               void* k_cache, void* v_cache, int64_t ctx,
                               void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Chunked prefill on a cache prefix (llama3 结构详解 §3.2: the new keys/values go to cache slots
+ * start_pos .. start_pos + seqlen - 1 and attention reads slots 0 .. start_pos + seqlen - 1; CSDN answer
+ * "#### 5.": for start_pos > 0 the causal mask gains start_pos leading zero columns).
+ * Same arguments and layout as llama_layer_forward; k_cache and v_cache are required. The rotated K
+ * and V of token (b, s) are stored at slot position_ids[b, s]; then query (b, s) attends over cache
+ * slots 0 .. position_ids[b, s] (slots not written by this call are used as stored, i.e. the prefix
+ * written by earlier calls). With position_ids[b, s] = s it equals llama_layer_forward with caches.
+ * Positions of one sequence must be distinct and in [0, ctx). Workspace as llama_layer_workspace_bytes
+ * for (B, S) with ctx = 0. */
+ll_status llama_layer_forward_chunk(const ll_layer_cfg* cfg, const ll_layer_weights* w,
+                                    const void* hidden, const int64_t* position_ids,
+                                    int64_t B, int64_t S, int64_t kv_seq_len,
+                                    void* k_cache, void* v_cache, int64_t ctx,
+                                    void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* RMSNorm over rows (llama3 结构详解 §3.1; NJU lecture 5 "编码实现RMSNorm"):
  *   y[r, i] = x[r, i] / sqrt(mean_i x[r, i]^2 + eps) * gain[i], fp32 accumulation.
  * x, y [rows, hidden] (y may equal x); gain [hidden]. */
@@ -138,6 +153,19 @@ ll_status gqa_attn_prefill(const void* qkv, const ll_rope* rope, const int64_t* 
                            int64_t kv_seq_len, void* o, void* k_cache, void* v_cache, int64_t ctx,
                            int64_t B, int64_t S, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
                            int32_t dtype, void* stream);
+
+/* Attention step of chunked prefill on a cache prefix (llama3 结构详解 §3.2 cache_k[:, start_pos :
+ * start_pos + seqlen] = xk, keys = cache_k[:, : start_pos + seqlen]; CSDN answer "#### 5." mask with
+ * start_pos zero columns):
+ *   k_cache[b, p] = k_{b,s}, v_cache[b, p] = v_{b,s} with p = position_ids[b, s], then
+ *   o[b, s, h*d:(h+1)*d] = sum_{j <= p} softmax_j(q_{b,s,h} . k_cache[b,j,c] / sqrt(d)) v_cache[b,j,c].
+ * qkv packed [B, S, (n_heads + 2 n_kv_heads) d] with q and k already rotated, read only;
+ * position_ids [B, S] int64, distinct per sequence, in [0, ctx); k_cache, v_cache [B, ctx, n_kv_heads, d]
+ * (required; slots outside this chunk are read as stored); o [B, S, n_heads d]. */
+ll_status gqa_attn_prefill_chunk(const void* qkv, const int64_t* position_ids, void* o,
+                                 void* k_cache, void* v_cache, int64_t ctx,
+                                 int64_t B, int64_t S, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+                                 int32_t dtype, void* stream);
 
 /* Bytes of workspace gqa_attn_decode needs. */
 size_t gqa_attn_decode_workspace_bytes(int64_t B, int64_t n_heads, int64_t head_dim, int64_t ctx);

@@ -238,3 +238,57 @@ def test_attn_decode(case, with_rope):
         keep[p] = False
         np.testing.assert_array_equal(gk[b, keep], K0[b, keep])
         np.testing.assert_array_equal(gv[b, keep], V0[b, keep])
+
+
+# ------------------------------------------------------------------ chunked prefill on a cache prefix
+CHUNK = [
+    # dtype, B, S, nh, nkv, d, ctx, starts, order
+    ("bf16", 2, 130, 8, 2, 128, 320, (0, 70), "up"),          # empty prefix and a prefix off a tile edge
+    ("bf16", 1, 64, 8, 2, 64, 200, (100,), "up"),
+    ("bf16", 2, 1, 8, 2, 128, 600, (500, 37), "up"),          # one-token chunks
+    ("bf16", 1, 200, 16, 2, 128, 1300, (1000,), "up"),        # long prefix, g = 8
+    ("bf16", 1, 257, 6, 2, 64, 400, (33,), "up"),             # g = 3 (one head per block)
+    ("bf16", 1, 100, 8, 2, 128, 200, (60,), "down"),          # positions in reverse order
+    ("bf16", 1, 50, 4, 2, 96, 120, (20,), "up"),              # generic kernel (d = 96)
+    ("f32", 2, 20, 4, 2, 16, 48, (3, 11), "up"),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK, ids=lambda c: "-".join(map(str, c)))
+def test_attn_prefill_chunk(case):
+    """gqa_attn_prefill_chunk against the oracle's attention_chunk: the chunk's K/V land at their slots
+    (bit for bit), other slots stay as they were, and each query attends over slots 0 .. its position."""
+    require_gpu()
+    dtype, B, S, nh, nkv, d, ctx, starts, order = case
+    qkv = normal(7, 150, (B, S, (nh + 2 * nkv) * d), dtype)
+    kc = normal(7, 151, (B, ctx, nkv, d), dtype)
+    vc = normal(7, 152, (B, ctx, nkv, d), dtype)
+    pos = np.stack([np.arange(P, P + S) if order == "up" else np.arange(P + S - 1, P - 1, -1) for P in starts])
+    pos = pos.astype(np.int64)
+    x = bits_to_f64(qkv, dtype)
+    q, k, v = ref.split_qkv(x, nh, nkv, d)
+    K0, V0 = bits_to_f64(kc, dtype), bits_to_f64(vc, dtype)
+    want, WK, WV = ref.attention_chunk(q, k, v, pos, K0, V0)
+    tk, tv = to_dev(kc, dtype), to_dev(vc, dtype)
+    o = L.gqa_attn_prefill_chunk(to_dev(qkv, dtype), torch.from_numpy(pos).to(DEV), tk, tv, nh, nkv, d)
+    got = to_f64(o)
+    assert got.shape == (B, S, nh * d)
+    assert ref.max_rel_err(got, want) <= tol(dtype)
+    np.testing.assert_array_equal(to_f64(tk), WK)
+    np.testing.assert_array_equal(to_f64(tv), WV)
+
+
+def test_attn_prefill_chunk_empty_prefix_equals_prefill():
+    """With positions 0..S-1 the chunked path computes the one-call prefill (same inputs, same cache
+    writes); both are bf16 kernels, so they agree to bf16 rounding."""
+    require_gpu()
+    B, S, nh, nkv, d, ctx = 2, 190, 8, 2, 128, 256
+    qkv = to_dev(normal(8, 153, (B, S, (nh + 2 * nkv) * d), "bf16"), "bf16")
+    pos = torch.arange(S, device=DEV, dtype=torch.int64).expand(B, S).contiguous()
+    k1 = torch.zeros((B, ctx, nkv, d), device=DEV, dtype=torch.bfloat16)
+    v1, k2, v2 = k1.clone(), k1.clone(), k1.clone()
+    o1 = L.gqa_attn_prefill(qkv, pos, nh, nkv, d, kv_seq_len=ctx, k_cache=k1, v_cache=v1)
+    o2 = L.gqa_attn_prefill_chunk(qkv, pos, k2, v2, nh, nkv, d)
+    torch.cuda.synchronize()
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    assert ref.max_rel_err(to_f64(o2), to_f64(o1)) <= 1e-2

@@ -14,7 +14,7 @@ import torch
 import transformer_layer_forward_amd as L
 from oracle import ref
 from synth_inputs import (CONFIGS, RopeCfg, make_cache, make_cache_row, make_decode_positions, make_hidden,
-                          make_prefill_positions, make_weights, scaled, to_f64 as bits_to_f64)
+                          make_prefill_positions, make_weights, normal, scaled, to_f64 as bits_to_f64)
 from tests.gpu_util import DEV, require_gpu, tol, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -163,6 +163,71 @@ def test_layer_decode_matches_prefill_row():
     torch.cuda.synchronize()
     a, b = to_f64(step)[:, 0], to_f64(full)[:, P]
     xb = to_f64(x)[:, P]
+    assert ref.max_rel_err(a, b) <= 2e-2
+    assert ref.max_rel_err(a - xb, b - xb) <= 3e-2
+
+
+# ------------------------------------------------------------------ chunked prefill on a cache prefix
+CHUNK_LAYER = [
+    # config, chunk length S, prefix length per sequence, ctx
+    (scaled(CONFIGS["llama3_8b_prefill"], B=2, S=90), (0, 130), 256),
+    (scaled(CONFIGS["llama32_1b_prefill"], B=1, S=70), (200,), 300),
+    (scaled(CONFIGS["tiny_f32"], B=2, S=9), (5, 20), 40),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_LAYER, ids=lambda c: f"{c[0].name}-S{c[0].S}-P{'_'.join(map(str, c[1]))}")
+def test_layer_chunk_small(case):
+    """llama_layer_forward_chunk against the oracle's layer_prefill_chunk: a chunk at positions
+    P..P+S-1 over seeded caches whose slots below P stand for an earlier prefix."""
+    require_gpu()
+    cfg, starts, ctx = case
+    W = make_weights(cfg, seed=2)
+    x = make_hidden(cfg, seed=2)
+    pos = np.stack([np.arange(P, P + cfg.S) for P in starts]).astype(np.int64)
+    kc = normal_cache(cfg, ctx, 160)
+    vc = normal_cache(cfg, ctx, 161)
+    x64 = bits_to_f64(x, cfg.dtype)
+    K0, V0 = bits_to_f64(kc, cfg.dtype), bits_to_f64(vc, cfg.dtype)
+    want = ref.layer_prefill_chunk(cfg, w64(W, cfg.dtype), x64, pos, ctx, K0, V0)
+    tk, tv = to_dev(kc, cfg.dtype), to_dev(vc, cfg.dtype)
+    out = L.llama_layer_forward_chunk(layer_cfg(cfg), dev_weights(W, cfg.dtype), to_dev(x, cfg.dtype),
+                                      torch.from_numpy(pos).to(DEV), tk, tv, kv_seq_len=ctx)
+    got = to_f64(out)
+    check(got, x64, want["out"], want["attn_proj"] + want["mlp_out"], cfg.dtype, cfg.name)
+    gk, gv = to_f64(tk), to_f64(tv)
+    for b, P in enumerate(starts):
+        assert ref.max_rel_err(gk[b, P:P + cfg.S], want["cache_k"][b, P:P + cfg.S]) <= tol(cfg.dtype)
+        assert ref.max_rel_err(gv[b, P:P + cfg.S], want["cache_v"][b, P:P + cfg.S]) <= tol(cfg.dtype)
+        np.testing.assert_array_equal(gk[b, :P], K0[b, :P])
+        np.testing.assert_array_equal(gv[b, P + cfg.S:], V0[b, P + cfg.S:])
+
+
+def normal_cache(cfg, ctx, k):
+    return normal(2, k, (cfg.B, ctx, cfg.n_kv_heads, cfg.head_dim), cfg.dtype)
+
+
+def test_layer_chunk_matches_one_shot():
+    """Prefill of tokens 0..P-1 into the caches, then a chunk of tokens P..P+S-1, reproduces rows P.. of
+    one prefill over all P+S tokens (llama3 结构详解 §3.2 start_pos; CSDN answer "#### 5.")."""
+    require_gpu()
+    P, S = 150, 100
+    cfg = scaled(CONFIGS["llama3_8b_prefill"], B=2, S=P + S)
+    W = dev_weights(make_weights(cfg, seed=5), cfg.dtype)
+    x = to_dev(make_hidden(cfg, seed=5), cfg.dtype)
+    lc = layer_cfg(cfg)
+    ctx = 320
+    pos = torch.from_numpy(make_prefill_positions(cfg)).to(DEV)
+    full = L.llama_layer_forward(lc, W, x, pos, kv_seq_len=ctx)
+    kc = torch.zeros((2, ctx, cfg.n_kv_heads, cfg.head_dim), device=DEV, dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    L.llama_layer_forward(lc, W, x[:, :P].contiguous(), pos[:, :P].contiguous(), kv_seq_len=ctx, k_cache=kc,
+                          v_cache=vc)
+    chunk = L.llama_layer_forward_chunk(lc, W, x[:, P:].contiguous(), pos[:, P:].contiguous(), kc, vc,
+                                        kv_seq_len=ctx)
+    torch.cuda.synchronize()
+    a, b = to_f64(chunk), to_f64(full)[:, P:]
+    xb = to_f64(x)[:, P:]
     assert ref.max_rel_err(a, b) <= 2e-2
     assert ref.max_rel_err(a - xb, b - xb) <= 3e-2
 

@@ -8,9 +8,11 @@ from ._lib import (  # noqa: F401
     Rope,
     gqa_attn_decode,
     gqa_attn_prefill,
+    gqa_attn_prefill_chunk,
     layer_workspace_bytes,
     last_error,
     llama_layer_forward,
+    llama_layer_forward_chunk,
     load,
     profile_begin,
     profile_end,

@@ -22,7 +22,8 @@ ROPE_TYPES = {"default": 0, "linear": 1, "dynamic_ntk": 2, "llama3": 3}
 STATUS_NAMES = {0: "LL_OK", 1: "LL_EINVAL", 2: "LL_EUNSUPPORTED", 3: "LL_EHIP", 4: "LL_ENOMEM"}
 
 EXPORTED = (
-    "llama_layer_workspace_bytes", "llama_layer_forward", "rmsnorm", "rope_apply", "gqa_attn_prefill",
+    "llama_layer_workspace_bytes", "llama_layer_forward", "llama_layer_forward_chunk", "rmsnorm", "rope_apply",
+    "gqa_attn_prefill", "gqa_attn_prefill_chunk",
     "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "swiglu_mlp_workspace_bytes", "swiglu_mlp",
     "ll_last_error", "ll_release_caches", "ll_profile_begin", "ll_profile_end", "ll_profile_stage_name",
     "ll_version",
@@ -104,11 +105,15 @@ def load() -> ctypes.CDLL:
         "llama_layer_workspace_bytes": (c_sz, [ctypes.POINTER(LLLayerCfg), c_i64, c_i64, c_i64]),
         "llama_layer_forward": (c_i32, [ctypes.POINTER(LLLayerCfg), ctypes.POINTER(LLLayerWeights), c_vp, c_vp, c_i64,
                                         c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_sz, c_vp]),
+        "llama_layer_forward_chunk": (c_i32, [ctypes.POINTER(LLLayerCfg), ctypes.POINTER(LLLayerWeights), c_vp, c_vp,
+                                              c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_sz, c_vp]),
         "rmsnorm": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_d, c_i32, c_vp]),
         "rope_apply": (c_i32, [ctypes.POINTER(LLRope), c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i32,
                                c_vp]),
         "gqa_attn_prefill": (c_i32, [c_vp, ctypes.POINTER(LLRope), c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
                                      c_i64, c_i64, c_i64, c_i32, c_vp]),
+        "gqa_attn_prefill_chunk": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64,
+                                           c_i32, c_vp]),
         "gqa_attn_decode_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i64]),
         "gqa_attn_decode": (c_i32, [c_vp, ctypes.POINTER(LLRope), c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64,
                                     c_i64, c_i64, c_i32, c_vp, c_sz, c_vp]),
@@ -206,6 +211,20 @@ def gqa_attn_prefill(qkv: torch.Tensor, position_ids: Optional[torch.Tensor], n_
     return o
 
 
+def gqa_attn_prefill_chunk(qkv: torch.Tensor, position_ids: torch.Tensor, k_cache: torch.Tensor,
+                           v_cache: torch.Tensor, n_heads: int, n_kv_heads: int, head_dim: int,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """qkv [B, S, (n_h + 2 n_kv) d] with q, k rotated; stores K/V at slots position_ids[b, s], then each
+    query attends over cache slots 0 .. its position -> o [B, S, n_h d]."""
+    lib = load()
+    B, S = qkv.shape[0], qkv.shape[1]
+    o = out if out is not None else torch.empty((B, S, n_heads * head_dim), dtype=qkv.dtype, device=qkv.device)
+    _check(lib.gqa_attn_prefill_chunk(_ptr(qkv), _ptr(position_ids), _ptr(o), _ptr(k_cache), _ptr(v_cache),
+                                      k_cache.shape[1], B, S, n_heads, n_kv_heads, head_dim, _dtype_code(qkv.dtype),
+                                      _stream(qkv)), "gqa_attn_prefill_chunk")
+    return o
+
+
 def gqa_attn_decode(qkv: torch.Tensor, pos: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, n_heads: int,
                     n_kv_heads: int, head_dim: int, rope: Optional[Rope] = None, kv_seq_len: int = 0,
                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -271,6 +290,33 @@ def llama_layer_forward(cfg: LayerConfig, weights: dict, hidden: torch.Tensor, p
     _check(lib.llama_layer_forward(ctypes.byref(c), ctypes.byref(w), _ptr(hidden), _ptr(position_ids), B, S,
                                    int(kv_seq_len), _ptr(k_cache), _ptr(v_cache), ctx, _ptr(y), _ptr(ws), ws.numel(),
                                    _stream(hidden)), "llama_layer_forward")
+    return y
+
+
+def llama_layer_forward_chunk(cfg: LayerConfig, weights: dict, hidden: torch.Tensor, position_ids: torch.Tensor,
+                              k_cache: torch.Tensor, v_cache: torch.Tensor, kv_seq_len: Optional[int] = None,
+                              out: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Chunked prefill on a cache prefix: hidden [B, S, H] at positions position_ids [B, S]; the chunk's
+    K/V are stored in the caches and attention reads cache slots 0 .. each token's position.
+    kv_seq_len defaults to the cache length."""
+    lib = load()
+    B, S = hidden.shape[0], hidden.shape[1]
+    ctx = k_cache.shape[1]
+    if kv_seq_len is None:
+        kv_seq_len = ctx
+    c = cfg.to_c()
+    w = LLLayerWeights(*(weights[k].data_ptr() for k in ("w_qkv", "w_o", "w_gate_up", "w_down", "g_attn", "g_mlp")))
+    for k in ("w_qkv", "w_o", "w_gate_up", "w_down", "g_attn", "g_mlp"):
+        _ptr(weights[k])
+    need = lib.llama_layer_workspace_bytes(ctypes.byref(c), B, S, 0)
+    if need == 0:
+        raise ValueError(f"invalid layer configuration: {last_error()}")
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=hidden.device)
+    y = out if out is not None else torch.empty_like(hidden)
+    _check(lib.llama_layer_forward_chunk(ctypes.byref(c), ctypes.byref(w), _ptr(hidden), _ptr(position_ids), B, S,
+                                         int(kv_seq_len), _ptr(k_cache), _ptr(v_cache), ctx, _ptr(y), _ptr(ws),
+                                         ws.numel(), _stream(hidden)), "llama_layer_forward_chunk")
     return y
 
 

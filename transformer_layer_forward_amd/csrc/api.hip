@@ -421,6 +421,22 @@ ll_status gqa_attn_prefill(const void* qkv, const ll_rope* rope, const int64_t* 
     return LL_OK;
 }
 
+ll_status gqa_attn_prefill_chunk(const void* qkv, const int64_t* position_ids, void* o, void* k_cache, void* v_cache,
+                                 int64_t ctx, int64_t B, int64_t S, int64_t n_heads, int64_t n_kv_heads,
+                                 int64_t head_dim, int32_t dtype, void* stream) {
+    if (!k_cache || !v_cache) return fail(LL_EINVAL, "chunked prefill needs k_cache and v_cache");
+    ll_status st = check_attn_common(qkv, nullptr, position_ids, 0, o, k_cache, v_cache, ctx, B, S, n_heads,
+                                     n_kv_heads, head_dim, dtype);
+    if (st != LL_OK || B * S == 0) return st;
+    if (ctx > kIntMax) return fail(LL_EUNSUPPORTED, "ctx exceeds 2^31-1");
+    hipError_t e = launch_attn_prefill_chunk(dtype, qkv, position_ids, o, k_cache, v_cache, ctx, static_cast<int>(B),
+                                             static_cast<int>(S), static_cast<int>(n_heads),
+                                             static_cast<int>(n_kv_heads), static_cast<int>(head_dim),
+                                             as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "gqa_attn_prefill_chunk launch");
+    return LL_OK;
+}
+
 size_t gqa_attn_decode_workspace_bytes(int64_t B, int64_t n_heads, int64_t head_dim, int64_t ctx) {
     if (B < 0 || n_heads <= 0 || head_dim <= 0 || ctx <= 0) return 0;
     return attn_decode_workspace_bytes(B, n_heads, head_dim, ctx);
@@ -493,10 +509,10 @@ size_t llama_layer_workspace_bytes(const ll_layer_cfg* cfg, int64_t B, int64_t S
     return layer_ws(cfg, B, S, (S == 1 && ctx > 0) ? ctx : 0).total;
 }
 
-ll_status llama_layer_forward(const ll_layer_cfg* cfg, const ll_layer_weights* w, const void* hidden,
-                              const int64_t* position_ids, int64_t B, int64_t S, int64_t kv_seq_len, void* k_cache,
-                              void* v_cache, int64_t ctx, void* out, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+static ll_status layer_forward_impl(const ll_layer_cfg* cfg, const ll_layer_weights* w, const void* hidden,
+                                    const int64_t* position_ids, int64_t B, int64_t S, int64_t kv_seq_len,
+                                    void* k_cache, void* v_cache, int64_t ctx, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream, bool chunk) {
     ll_status st = check_cfg(cfg);
     if (st != LL_OK) return st;
     if (!w) return fail(LL_EINVAL, "weights is NULL");
@@ -514,7 +530,8 @@ ll_status llama_layer_forward(const ll_layer_cfg* cfg, const ll_layer_weights* w
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(LL_EINVAL, "pointers must be 16-byte aligned");
     if (k_cache && (!aligned16(k_cache) || !aligned16(v_cache))) return fail(LL_EINVAL, "pointers must be 16-byte aligned");
-    const bool decode = (S == 1 && k_cache != nullptr);
+    if (chunk && !k_cache) return fail(LL_EINVAL, "chunked prefill needs k_cache and v_cache");
+    const bool decode = !chunk && (S == 1 && k_cache != nullptr);
     const LayerWs lw = layer_ws(cfg, B, S, decode ? ctx : 0);
     if (!workspace || workspace_bytes < lw.total)
         return fail(LL_EINVAL, "workspace too small: %zu < %zu", workspace_bytes, lw.total);
@@ -578,7 +595,11 @@ ll_status llama_layer_forward(const ll_layer_cfg* cfg, const ll_layer_weights* w
     }
     LL_CHECK_HIP(mark(), "hipEventRecord");
     // 3. attention on rotated q and k
-    if (decode) {
+    if (chunk) {
+        e = launch_attn_prefill_chunk(dt, qkv, position_ids, o, k_cache, v_cache, ctx, static_cast<int>(B),
+                                      static_cast<int>(S), static_cast<int>(s.nh), static_cast<int>(s.nkv),
+                                      static_cast<int>(s.d), stream_h);
+    } else if (decode) {
         e = launch_attn_decode(dt, qkv, position_ids, nullptr, 0, k_cache, v_cache, ctx, o, static_cast<int>(B),
                                static_cast<int>(s.nh), static_cast<int>(s.nkv), static_cast<int>(s.d), dws, dbytes,
                                stream_h);
@@ -606,6 +627,22 @@ ll_status llama_layer_forward(const ll_layer_cfg* cfg, const ll_layer_weights* w
     if (e != hipSuccess) return hip_fail(e, "down launch");
     LL_CHECK_HIP(mark(), "hipEventRecord");
     return LL_OK;
+}
+
+ll_status llama_layer_forward(const ll_layer_cfg* cfg, const ll_layer_weights* w, const void* hidden,
+                              const int64_t* position_ids, int64_t B, int64_t S, int64_t kv_seq_len, void* k_cache,
+                              void* v_cache, int64_t ctx, void* out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    return layer_forward_impl(cfg, w, hidden, position_ids, B, S, kv_seq_len, k_cache, v_cache, ctx, out, workspace,
+                              workspace_bytes, stream, false);
+}
+
+ll_status llama_layer_forward_chunk(const ll_layer_cfg* cfg, const ll_layer_weights* w, const void* hidden,
+                                    const int64_t* position_ids, int64_t B, int64_t S, int64_t kv_seq_len,
+                                    void* k_cache, void* v_cache, int64_t ctx, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    return layer_forward_impl(cfg, w, hidden, position_ids, B, S, kv_seq_len, k_cache, v_cache, ctx, out, workspace,
+                              workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -420,7 +420,7 @@ __device__ __forceinline__ int vt_phys(int r, int c) {
     else return c ^ (2 * ((r >> 1) & 1)) ^ (4 * ((r >> 2) & 1));
 }
 
-template <int D, int HPB>
+template <int D, int HPB, bool CACHED>
 __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, bf16_t* __restrict__ out, bf16_t* __restrict__ kc,
     bf16_t* __restrict__ vc, int64_t ctx, int B, int S, int nh, int nkv, float scale_log2) {
@@ -455,6 +455,36 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     const bf16_t* qkv_b = qkv + static_cast<int64_t>(b) * S * rs;
     const int q0 = qb * C::BQ + (wave & 1) * 32;
 
+    // ---- visibility: query i sees keys 0 .. lim(i). Over the call's own tokens lim(i) = i; over a
+    // cache (chunked prefill on a prefix) the keys are cache slots and lim(i) = position_ids[b, i]
+    // (clamped to the cache). The block's smallest and largest limits give the key tiles it visits
+    // (0 .. hi / 64) and the first one that needs the mask.
+    const int64_t* pos_b = CACHED ? pos + static_cast<int64_t>(b) * S : nullptr;
+    auto lim_of = [&](int qi) -> int {
+        if constexpr (CACHED) return static_cast<int>(clamp_pos(pos_b[qi], ctx));
+        else return qi;
+    };
+    int lo, hi;
+    {
+        const int qi = qb * C::BQ + lane;
+        const int qv = qi < S ? qi : S - 1;
+        int l = lim_of(qv);
+        int m = l;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            l = min(l, __shfl_xor(l, o, 64));
+            m = max(m, __shfl_xor(m, o, 64));
+        }
+        lo = __builtin_amdgcn_readfirstlane(l);
+        hi = __builtin_amdgcn_readfirstlane(m);
+    }
+    int qlim[2];
+#pragma unroll
+    for (int qf = 0; qf < 2; ++qf) {
+        const int qi = q0 + qf * 16 + lrow;
+        qlim[qf] = lim_of(qi < S ? qi : S - 1);
+    }
+
     // ---- Q fragments (B operand of S^T = K Q^T): lane holds query q0 + qf*16 + lrow, dims k*32 + lgrp*8 ..
     bf16x8 qfr[2][C::KC32];
 #pragma unroll
@@ -481,15 +511,16 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     // (MUBUF) loads based at this kv head's first K and V element, with 32-bit byte offsets (the
     // caller checks S * row stride fits); unlike the flat-segment form they let the compiler wait for
     // individual LDS reads rather than all of them.
-    const bf16_t* kbase = qkv_b + static_cast<int64_t>(nh + c) * D;
-    const bf16_t* vbase = qkv_b + static_cast<int64_t>(nh + nkv + c) * D;
-    const uint32_t rs_bytes = static_cast<uint32_t>(rs) * 2u;
+    const int64_t cache_b = (static_cast<int64_t>(b) * ctx * nkv + c) * D;
+    const bf16_t* kbase = CACHED ? kc + cache_b : qkv_b + static_cast<int64_t>(nh + c) * D;
+    const bf16_t* vbase = CACHED ? vc + cache_b : qkv_b + static_cast<int64_t>(nh + nkv + c) * D;
+    const uint32_t rs_bytes = static_cast<uint32_t>(CACHED ? static_cast<int64_t>(nkv) * D : rs) * 2u;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kbase), (short)0, -1, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vbase), (short)0, -1, 0x00020000);
 
     // ---- cache append: the first head chunk of each query block copies the block's own keys and
     // values (its diagonal tile) to their slots, so every token is written exactly once
-    if (kc != nullptr && hc == 0) {
+    if (!CACHED && kc != nullptr && hc == 0) {
         const int64_t* pos_b = pos + static_cast<int64_t>(b) * S;
         for (int job = tid; job < 2 * C::BKV * CH; job += NT) {
             const bool isv = job >= C::BKV * CH;
@@ -510,7 +541,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
             const int q = wave * LPW + i;
             const bool isv = q >= LOADS;
             const int r = (q % LOADS) * RPI + lane / CH, pc = lane % CH;
-            const int key = min((isv ? vtile : ktile) * C::BKV + r, S - 1);
+            const int key = min((isv ? vtile : ktile) * C::BKV + r, hi);
             const int lc = isv ? vt_phys<D>(r, pc) : k_phys<D>(r, pc);
             const uint32_t off = static_cast<uint32_t>(key) * rs_bytes + static_cast<uint32_t>(lc) * 16u;
             bf16_t* dst = isv ? &sV[vbuf][(q % LOADS) * RPI * D] : &sK[kbuf][(q % LOADS) * RPI * D];
@@ -524,7 +555,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
             const int q = wave * LPW + i;
             if (q < LOADS) {
                 const int r = q * RPI + lane / CH, pc = lane % CH;
-                const int key = min(ktile * C::BKV + r, S - 1);
+                const int key = min(ktile * C::BKV + r, hi);
                 const uint32_t off = static_cast<uint32_t>(key) * rs_bytes + static_cast<uint32_t>(k_phys<D>(r, pc)) * 16u;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)&sK[kbuf][q * RPI * D],
                                                          16, off, 0, 0, 0);
@@ -580,7 +611,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     float mbA[2] = {0.f, 0.f}, mbB[2] = {0.f, 0.f};   // reference max each accumulator set started from
     bf16x8 pfr[2][2];
 
-    const int nkt = qb + 1;
+    const int nkt = hi / C::BKV + 1;
     issue_tiles(0, 0, 0, 0);
     issue_k_only(1, 1);
     __syncthreads();
@@ -599,13 +630,12 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
         /* K(j+2) into the buffer K(j) used, V(j+1) into the buffer V(j-1) used: both free since the */    \
         /* barrier that ended the previous iteration                                                 */    \
         issue_tiles(j + 2, j & 1, j + 1, (j + 1) & 1);                                                     \
-        if (j == nkt - 1) {                                                                                \
+        if ((j + 1) * C::BKV - 1 > lo) {                                                                   \
             _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                             \
-                const int qi = q0 + qf * 16 + lrow;                                                        \
                 _Pragma("unroll") for (int kf = 0; kf < 4; ++kf)                                           \
                     _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                        \
                         const int key = j * C::BKV + kf * 16 + 4 * lgrp + r;                               \
-                        if (key > qi || key >= S) SC[kf][qf][r] = -INFINITY;                               \
+                        if (key > qlim[qf]) SC[kf][qf][r] = -INFINITY;                                     \
                     }                                                                                      \
             }                                                                                              \
         }                                                                                                  \
@@ -814,18 +844,19 @@ __global__ __launch_bounds__(256) void attn_decode_generic_kernel(const T* __res
                                                                   const float2* __restrict__ cs, int64_t rope_rows,
                                                                   int il, const T* __restrict__ kc,
                                                                   const T* __restrict__ vc, int64_t ctx,
-                                                                  T* __restrict__ out, int B, int nh, int nkv, int d,
-                                                                  float scale) {
+                                                                  T* __restrict__ out, int B, int S, int nh, int nkv,
+                                                                  int d, float scale) {
     const int lane = threadIdx.x & 63;
     const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (w >= static_cast<int64_t>(B) * nh) return;
+    if (w >= static_cast<int64_t>(B) * S * nh) return;
     const int h = static_cast<int>(w % nh);
-    const int b = static_cast<int>(w / nh);
+    const int64_t t = w / nh;            // token b * S + s
+    const int b = static_cast<int>(t / S);
     const int c = h / (nh / nkv);
     const int64_t rs = static_cast<int64_t>(nh + 2 * nkv) * d;
-    const int64_t p = clamp_pos(pos[b], ctx);
+    const int64_t p = clamp_pos(pos[t], ctx);
     float q[GEN_DPL], acc[GEN_DPL] = {0.f, 0.f, 0.f, 0.f};
-    gen_load_head<T>(qkv + b * rs + static_cast<int64_t>(h) * d, d, lane, cs, rope_rows, pos[b], il, q);
+    gen_load_head<T>(qkv + t * rs + static_cast<int64_t>(h) * d, d, lane, cs, rope_rows, pos[t], il, q);
     float m = -INFINITY, l = 0.f;
     for (int64_t j = 0; j <= p; ++j) {
         const T* kp = kc + ((static_cast<int64_t>(b) * ctx + j) * nkv + c) * d;
@@ -847,7 +878,7 @@ __global__ __launch_bounds__(256) void attn_decode_generic_kernel(const T* __res
         }
         m = mn;
     }
-    T* op = out + static_cast<int64_t>(b) * nh * d + static_cast<int64_t>(h) * d;
+    T* op = out + t * nh * d + static_cast<int64_t>(h) * d;
 #pragma unroll
     for (int e = 0; e < GEN_DPL; ++e) {
         const int dd = lane + 64 * e;
@@ -1137,7 +1168,7 @@ static hipError_t prefill_go(const void* qkv, const int64_t* pos, const RopeTab*
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
     const bool offsets_ok = static_cast<int64_t>(S) * (nh + 2 * nkv) * D * 2 < (int64_t(1) << 32);
     if (!ROPE && offsets_ok)
-        hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB>), dim3(blocks), dim3(128 * HPB), 0, st,
+        hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, false>), dim3(blocks), dim3(128 * HPB), 0, st,
                            static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
                            static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2);
     else
@@ -1270,11 +1301,67 @@ hipError_t launch_attn_decode(int dtype, const void* qkv, const int64_t* pos, co
     if (dtype == LL_BF16)
         hipLaunchKernelGGL(attn_decode_generic_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st,
                            static_cast<const bf16_t*>(qkv), pos, cs, rows, il, static_cast<const bf16_t*>(kc),
-                           static_cast<const bf16_t*>(vc), ctx, static_cast<bf16_t*>(o), B, nh, nkv, d, scale);
+                           static_cast<const bf16_t*>(vc), ctx, static_cast<bf16_t*>(o), B, 1, nh, nkv, d, scale);
     else
         hipLaunchKernelGGL(attn_decode_generic_kernel<float>, dim3(blocks), dim3(256), 0, st,
                            static_cast<const float*>(qkv), pos, cs, rows, il, static_cast<const float*>(kc),
-                           static_cast<const float*>(vc), ctx, static_cast<float*>(o), B, nh, nkv, d, scale);
+                           static_cast<const float*>(vc), ctx, static_cast<float*>(o), B, 1, nh, nkv, d, scale);
+    return hipGetLastError();
+}
+
+// Chunked prefill on a cache prefix: store the chunk's (already rotated) keys and values at their
+// slots, then every query attends over cache slots 0 .. its position.
+template <int D, int HPB>
+static hipError_t chunk_go(const void* qkv, const int64_t* pos, void* o, void* kc, void* vc, int64_t ctx, int B,
+                           int S, int nh, int nkv, hipStream_t st) {
+    const int g = nh / nkv;
+    const int nqb = (S + 63) / 64;
+    const unsigned blocks = static_cast<unsigned>(nqb) * B * nkv * (g / HPB);
+    const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
+    hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, true>), dim3(blocks), dim3(128 * HPB), 0, st,
+                       static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
+                       static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t chunk_hpb_sel(const void* qkv, const int64_t* pos, void* o, void* kc, void* vc, int64_t ctx, int B,
+                                int S, int nh, int nkv, hipStream_t st) {
+    const int g = nh / nkv;
+    if (g % 4 == 0) return chunk_go<D, 4>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, st);
+    if (g % 2 == 0) return chunk_go<D, 2>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, st);
+    return chunk_go<D, 1>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, st);
+}
+
+hipError_t launch_attn_prefill_chunk(int dtype, const void* qkv, const int64_t* pos, void* o, void* kc, void* vc,
+                                     int64_t ctx, int B, int S, int nh, int nkv, int d, hipStream_t st) {
+    if (B == 0 || S == 0) return hipSuccess;
+    // 1) append the chunk's keys and values at slots pos[b, s]
+    const unsigned kb = static_cast<unsigned>((static_cast<int64_t>(B) * S * nkv + 3) / 4);
+    if (dtype == LL_BF16)
+        hipLaunchKernelGGL(kv_store_kernel<bf16_t>, dim3(kb), dim3(256), 0, st, static_cast<const bf16_t*>(qkv), pos,
+                           nullptr, 1, 0, static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, d);
+    else
+        hipLaunchKernelGGL(kv_store_kernel<float>, dim3(kb), dim3(256), 0, st, static_cast<const float*>(qkv), pos,
+                           nullptr, 1, 0, static_cast<float*>(kc), static_cast<float*>(vc), ctx, B, S, nh, nkv, d);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // 2) attention over slots 0 .. pos[b, s]
+    const bool offsets_ok = ctx * nkv * d * 2 < (int64_t(1) << 32);
+    if (attn_mfma_supported(dtype, d, nh, nkv) && offsets_ok) {
+        if (d == 128) return chunk_hpb_sel<128>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, st);
+        return chunk_hpb_sel<64>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, st);
+    }
+    const unsigned blocks = static_cast<unsigned>((static_cast<int64_t>(B) * S * nh + 3) / 4);
+    const float scale = 1.f / sqrtf(static_cast<float>(d));
+    if (dtype == LL_BF16)
+        hipLaunchKernelGGL(attn_decode_generic_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st,
+                           static_cast<const bf16_t*>(qkv), pos, nullptr, 1, 0, static_cast<const bf16_t*>(kc),
+                           static_cast<const bf16_t*>(vc), ctx, static_cast<bf16_t*>(o), B, S, nh, nkv, d, scale);
+    else
+        hipLaunchKernelGGL(attn_decode_generic_kernel<float>, dim3(blocks), dim3(256), 0, st,
+                           static_cast<const float*>(qkv), pos, nullptr, 1, 0, static_cast<const float*>(kc),
+                           static_cast<const float*>(vc), ctx, static_cast<float*>(o), B, S, nh, nkv, d, scale);
     return hipGetLastError();
 }
 

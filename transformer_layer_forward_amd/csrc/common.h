@@ -91,6 +91,10 @@ bool gemm_rope_fusable(int dtype, int64_t M, int d);
 hipError_t launch_attn_prefill(int dtype, const void* qkv, const int64_t* pos, const RopeTab* tab, int interleaved,
                                void* o, void* kc, void* vc, int64_t ctx, int B, int S, int nh, int nkv, int d,
                                hipStream_t st);
+// chunked prefill on a cache prefix: q and k already rotated; stores the chunk's K/V at slots pos[b, s],
+// then query (b, s) attends over cache slots 0 .. pos[b, s]
+hipError_t launch_attn_prefill_chunk(int dtype, const void* qkv, const int64_t* pos, void* o, void* kc, void* vc,
+                                     int64_t ctx, int B, int S, int nh, int nkv, int d, hipStream_t st);
 size_t attn_decode_workspace_bytes(int64_t B, int64_t nh, int64_t d, int64_t ctx);
 hipError_t launch_attn_decode(int dtype, const void* qkv, const int64_t* pos, const RopeTab* tab, int interleaved,
                               void* kc, void* vc, int64_t ctx, void* o, int B, int nh, int nkv, int d, void* ws,
