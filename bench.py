@@ -34,7 +34,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=WORKLOAD,
-                    choices=[WORKLOAD, "llama32_1b_prefill", "llama3_8b_long_llama3rope", "llama3_8b_decode"],
+                    choices=[WORKLOAD, "llama32_1b_prefill", "llama3_8b_long_llama3rope", "llama3_8b_decode",
+                             CHUNK_WORKLOAD],
                     help="the headline line is the 8B prefill; the others print the same record for that workload")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the cache-cold decode measurement that the headline run adds as \"decode\"")
@@ -210,6 +211,42 @@ def run_prefill(L, torch, np, cfg, W, args):
     return wall * 1e3 / args.steps, stages, x_bits
 
 
+CHUNK_WORKLOAD = "llama3_8b_chunk"
+CHUNK_START, CHUNK_CTX = 6144, 8192
+
+
+def run_chunk(L, torch, np, cfg, W, args):
+    """Chunked prefill on a cache prefix: each sequence's S new tokens sit at positions
+    CHUNK_START .. CHUNK_START + S - 1 of CHUNK_CTX-slot caches whose earlier slots (the prefix) hold
+    N(0,1) values from torch's seeded device generator. Every call rewrites the same slots with the same
+    values, so calls are idempotent. Returns (ms_per_step, stages)."""
+    from synth_inputs import make_hidden
+    dev = "cuda:0"
+    x = torch.from_numpy(np.ascontiguousarray(make_hidden(cfg, seed=0)).view(np.int16)).to(dev).view(torch.bfloat16)
+    pos = (torch.arange(cfg.S, device=dev, dtype=torch.int64) + CHUNK_START).expand(cfg.B, cfg.S).contiguous()
+    g = torch.Generator(device=dev)
+    shape = (cfg.B, CHUNK_CTX, cfg.n_kv_heads, cfg.head_dim)
+    g.manual_seed(8)
+    kc = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    g.manual_seed(9)
+    vc = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    lc = lib_config(L, cfg, torch)
+    ws = torch.empty(L.layer_workspace_bytes(lc, cfg.B, cfg.S), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+    for _ in range(args.warmup):
+        L.llama_layer_forward_chunk(lc, W, x, pos, kc, vc, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    L.profile_begin(args.steps)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        L.llama_layer_forward_chunk(lc, W, x, pos, kc, vc, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = L.profile_end()
+    assert torch.isfinite(out.float()).all().item()
+    return wall * 1e3 / args.steps, stages
+
+
 def decode_inputs(L, torch, np, cfg, W):
     """Decode step inputs on the device: hidden [B,1,H], positions [B] integer-uniform on [1024, ctx),
     and K/V caches [B, ctx, n_kv, d] of N(0,1) values drawn by torch's seeded device generator (the
@@ -320,7 +357,12 @@ def main():
     import transformer_layer_forward_amd as L
     from synth_inputs import CONFIGS, make_weights
 
-    cfg = CONFIGS[args.workload]
+    chunk = args.workload == CHUNK_WORKLOAD
+    if chunk:
+        from synth_inputs import scaled
+        cfg = scaled(CONFIGS[WORKLOAD], name=CHUNK_WORKLOAD, S=2048)
+    else:
+        cfg = CONFIGS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
     W_bits = make_weights(cfg, seed=0)
@@ -355,13 +397,19 @@ def main():
         print(json.dumps(rec), flush=True)
         return
 
-    ms_per_step, stages, x_bits = run_prefill(L, torch, np, cfg, W, args)
+    if chunk:
+        ms_per_step, stages = run_chunk(L, torch, np, cfg, W, args)
+        x_bits = None
+    else:
+        ms_per_step, stages, x_bits = run_prefill(L, torch, np, cfg, W, args)
     tokens = cfg.B * cfg.S
     value = tokens / (ms_per_step / 1e3)
     M = cfg.M
     gate_up_flops = 2.0 * M * (2 * I) * H
     achieved = gate_up_flops / (stage_ms(stages, "gate_up_silu") / 1e3) / 1e12
-    attn_flops = 4.0 * cfg.B * cfg.n_heads * d * (cfg.S * (cfg.S + 1) / 2)   # QK^T and PV over visible pairs
+    start = CHUNK_START if chunk else 0
+    # QK^T and PV over the visible (query, key) pairs: query s sees keys 0 .. start + s
+    attn_flops = 4.0 * cfg.B * cfg.n_heads * d * (cfg.S * start + cfg.S * (cfg.S + 1) / 2)
     gemm_flops = gemm_flops_per_token(cfg) * M
     gemm_ms = sum(stage_ms(stages, k) for k in ("qkv_proj", "o_proj_residual", "gate_up_silu", "down_residual"))
     norm_bytes = 2 * (2 * M * H * 2 + H * 2)
@@ -369,7 +417,9 @@ def main():
     name = {"llama3_8b_prefill": "Llama-3-8B-shaped decoder layer, bf16 prefill, causal",
             "llama32_1b_prefill": "Llama-3.2-1B-shaped decoder layer, bf16 prefill, causal",
             "llama3_8b_long_llama3rope": "Llama-3-8B-shaped decoder layer, bf16 32k prefill, causal, "
-                                         "Llama3 RoPE scaling"}[args.workload]
+                                         "Llama3 RoPE scaling",
+            CHUNK_WORKLOAD: f"Llama-3-8B-shaped decoder layer, bf16 chunked prefill: {cfg.S} new tokens per "
+                            f"sequence on a {CHUNK_START}-token cached prefix ({CHUNK_CTX}-slot KV cache)"}[args.workload]
     metric = ("decoder-layer tokens/s (Llama-3-8B shape, bf16) + attention MFMA util %"
               if args.workload == WORKLOAD else f"decoder-layer tokens/s ({name})")
     rec = {
@@ -378,8 +428,10 @@ def main():
         "unit": "tokens/s",
         **common,
         "ms_per_step": round(ms_per_step, 4),
-        "data": "synthetic (seeded N(0,1) hidden, N(0,0.02) weights, 1+N(0,0.1) gains)",
-        "config": {"workload": name, "B": cfg.B, "S": cfg.S, **shape, "tokens_per_step": tokens},
+        "data": ("synthetic (seeded N(0,1) hidden" + (" and cache prefix" if chunk else "")
+                 + ", N(0,0.02) weights, 1+N(0,0.1) gains)"),
+        "config": {"workload": name, "B": cfg.B, "S": cfg.S, **shape, "tokens_per_step": tokens,
+                   **({"prefix": CHUNK_START, "ctx": CHUNK_CTX} if chunk else {})},
         "attention_mfma_util_pct": round(100.0 * attn_flops / (stage_ms(stages, "attention") / 1e3) / 1e12
                                          / MI355X_BF16_DENSE_TFLOPS, 2),
         "gemm_mfma_util_pct": round(100.0 * gemm_flops / (gemm_ms / 1e3) / 1e12 / MI355X_BF16_DENSE_TFLOPS, 2),
