@@ -232,6 +232,24 @@ def attention_chunk(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, positio
     return o, K, V
 
 
+def attention_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens) -> np.ndarray:
+    """Padding-free (packed) causal attention ([verl] §3 ParallelLlamaAttentionRmPad:
+    flash_attn_varlen_func with cu_seqlens_q = cu_seqlens_k = cu_seqlens, causal=True).
+
+    q [T,n_h,d], k/v [T,n_kv,d] hold the tokens of several sequences back to back; sequence i is tokens
+    cu_seqlens[i] .. cu_seqlens[i+1]-1. Each token attends causally to the earlier tokens of its own
+    sequence only. Returns o [T, n_h*d].
+    """
+    T, nh, d = q.shape
+    out = np.empty((T, nh * d), dtype=F64)
+    cu = [int(c) for c in cu_seqlens]
+    for i in range(len(cu) - 1):
+        a, b = cu[i], cu[i + 1]
+        if b > a:
+            out[a:b] = attention_prefill(q[None, a:b], k[None, a:b], v[None, a:b])[0]
+    return out
+
+
 # ---------------------------------------------------------------- MLP
 def silu(z: np.ndarray) -> np.ndarray:
     """silu(z) = z * sigmoid(z) = z / (1 + e^-z) ([nju] "SwiGLU模块")."""
@@ -339,6 +357,25 @@ def layer_prefill_chunk(cfg, W: dict, x: np.ndarray, position_ids: np.ndarray, k
     mlp_out = linear(act, W["w_down"])
     return {"o": o, "attn_proj": attn_proj, "h": h, "act": act, "mlp_out": mlp_out, "out": h + mlp_out,
             "k_rot": kr, "v": v, "cache_k": K, "cache_v": V}
+
+
+def layer_prefill_varlen(cfg, W: dict, x: np.ndarray, position_ids: np.ndarray, cu_seqlens, kv_seq_len: int) -> dict:
+    """The decoder layer over packed tokens ([verl] §3 ParallelLlamaAttentionRmPad): x [T,H] holds several
+    sequences back to back (boundaries cu_seqlens); the projections, norms and MLP act per token, RoPE
+    rotates token t at position_ids[t] (the rmpad path rotates by the index within the sequence, which
+    is what callers pass), and attention is attention_varlen."""
+    x = np.asarray(x, dtype=F64)
+    xn = rmsnorm(x, W["g_attn"], cfg.eps)
+    qkv = linear(xn, W["w_qkv"])
+    q, k, v = split_qkv(qkv, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim)
+    qr, kr = _rope_qk(cfg, q, k, np.asarray(position_ids), kv_seq_len)
+    o = attention_varlen(qr, kr, v, cu_seqlens)
+    attn_proj = linear(o, W["w_o"])
+    h = np.add(x, attn_proj)
+    hn = rmsnorm(h, g=W["g_mlp"], eps=cfg.eps)
+    act = swiglu_act(hn, W["w_gate_up"], cfg.intermediate)
+    mlp_out = linear(act, W["w_down"])
+    return {"o": o, "attn_proj": attn_proj, "h": h, "act": act, "mlp_out": mlp_out, "out": mlp_out + h}
 
 
 def layer_decode(cfg, W: dict, x: np.ndarray, pos: np.ndarray, kv_seq_len: int, cache_row_k, cache_row_v,

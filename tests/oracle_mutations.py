@@ -47,6 +47,10 @@ MUTS = [
     ("chunk layer unrotated k", "o, K, V = attention_chunk(qr, kr, v, np.asarray(position_ids), cache_k, cache_v)", "o, K, V = attention_chunk(qr, k, v, np.asarray(position_ids), cache_k, cache_v)"),
     ("chunk attn residual dropped", "    h = attn_proj + x\n", "    h = attn_proj\n"),
     ("chunk second norm uses g_attn", "hn = rmsnorm(h, W[\"g_mlp\"], eps=cfg.eps)", "hn = rmsnorm(h, W[\"g_attn\"], eps=cfg.eps)"),
+    ("varlen ignores boundaries", "out[a:b] = attention_prefill(q[None, a:b], k[None, a:b], v[None, a:b])[0]", "out[a:b] = attention_prefill(q[None, :b], k[None, :b], v[None, :b])[0][a:b]"),
+    ("varlen layer mlp residual", "\"out\": mlp_out + h}", "\"out\": mlp_out + x}"),
+    ("varlen attn residual dropped", "h = np.add(x, attn_proj)", "h = np.add(0.0, attn_proj)"),
+    ("varlen second norm uses g_attn", "hn = rmsnorm(h, g=W[\"g_mlp\"], eps=cfg.eps)", "hn = rmsnorm(h, g=W[\"g_attn\"], eps=cfg.eps)"),
     ("rows path second norm eps", "hn = rmsnorm(h, W[\"g_mlp\"], cfg.eps)\n            act", "hn = rmsnorm(h, W[\"g_mlp\"], 0.1)\n            act"),
 ]
 results = []

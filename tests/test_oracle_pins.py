@@ -447,6 +447,48 @@ def test_layer_chunk_continues_one_shot_prefill():
     np.testing.assert_allclose(ch["cache_k"][:, P:P + S], full["k_rot"][:, P:], rtol=1e-13, atol=1e-14)
 
 
+# ------------------------------------------------------------------ varlen packed prefill
+def test_attention_varlen_equals_per_sequence_prefill():
+    """parallel_attention.py §3: flash_attn_varlen_func(cu_seqlens, causal=True) over packed tokens is
+    causal attention within each sequence; it equals attention_prefill run on each sequence alone, and
+    tokens of one sequence cannot change another's rows."""
+    lens = [5, 1, 0, 9, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, nh, nkv, d = int(cu[-1]), 4, 2, 16
+    q, k, v = RNG.standard_normal((T, nh, d)), RNG.standard_normal((T, nkv, d)), RNG.standard_normal((T, nkv, d))
+    o = ref.attention_varlen(q, k, v, cu)
+    for i in range(len(lens)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b > a:
+            want = ref.attention_prefill(q[None, a:b], k[None, a:b], v[None, a:b])[0]
+            np.testing.assert_array_equal(o[a:b], want)
+    k2, v2 = k.copy(), v.copy()
+    k2[cu[3]:cu[4]] += 2.0
+    v2[cu[3]:cu[4]] -= 4.0
+    o2 = ref.attention_varlen(q, k2, v2, cu)
+    np.testing.assert_array_equal(o2[:cu[3]], o[:cu[3]])
+    np.testing.assert_array_equal(o2[cu[4]:], o[cu[4]:])
+    assert not np.array_equal(o2[cu[3]:cu[4]], o[cu[3]:cu[4]])
+
+
+def test_layer_varlen_equals_per_sequence_layer():
+    """The packed layer with in-sequence positions (the rmpad RoPE convention) equals the one-call layer
+    run on each sequence separately."""
+    base = CONFIGS["tiny_f32"]
+    lens = [7, 12, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    cfg = scaled(base, B=1, S=T)
+    W = _w64(cfg)
+    x = to_f64(make_hidden(cfg), cfg.dtype)[0]
+    pos = np.concatenate([np.arange(n) for n in lens]).astype(np.int64)
+    got = ref.layer_prefill_varlen(cfg, W, x, pos, cu, 64)
+    for i, n in enumerate(lens):
+        a, b = int(cu[i]), int(cu[i + 1])
+        one = ref.layer_prefill(scaled(base, B=1, S=n), W, x[None, a:b], pos[None, a:b], 64)
+        np.testing.assert_allclose(got["out"][a:b], one["out"][0], rtol=1e-13, atol=1e-13)
+
+
 # ------------------------------------------------------------------ shapes
 def test_layer_shapes_match_lecture_printout():
     """Golden: the Llama-3.2-1B layer dump on NJU lecture 5 fixes the projection shapes of the
