@@ -126,6 +126,21 @@ ll_status llama_layer_forward_chunk(const ll_layer_cfg* cfg, const ll_layer_weig
                                     void* k_cache, void* v_cache, int64_t ctx,
                                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decoder layer over packed (padding-free) sequences (parallel_attention.py §3 ParallelLlamaAttentionRmPad:
+ * tokens of all sequences back to back, boundaries cu_seqlens, causal attention within each sequence).
+ *   hidden, out   [total_tokens, H] (out may equal hidden);
+ *   position_ids  [total_tokens] int64 RoPE positions (§4 apply_rotary_pos_emb_rmpad_flash rotates each
+ *                 token by its index within its sequence: pass t - cu_seqlens[i] for that convention);
+ *   cu_seqlens    [n_seqs + 1] int32 on the device: 0 = cu[0] <= cu[1] <= ... <= cu[n_seqs] = total_tokens;
+ *   max_seqlen    host value >= every cu[i+1] - cu[i] (sizes the launch; longer sequences are cut there).
+ * Entries out of order or out of range are clamped (no out-of-bounds access) but then give unspecified
+ * results. No KV cache. Workspace as llama_layer_workspace_bytes(cfg, 1, total_tokens, 0). */
+ll_status llama_layer_forward_varlen(const ll_layer_cfg* cfg, const ll_layer_weights* w,
+                                     const void* hidden, const int64_t* position_ids,
+                                     const int32_t* cu_seqlens, int64_t n_seqs, int64_t max_seqlen,
+                                     int64_t total_tokens, int64_t kv_seq_len,
+                                     void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* RMSNorm over rows (llama3 结构详解 §3.1; NJU lecture 5 "编码实现RMSNorm"):
  *   y[r, i] = x[r, i] / sqrt(mean_i x[r, i]^2 + eps) * gain[i], fp32 accumulation.
  * x, y [rows, hidden] (y may equal x); gain [hidden]. */
@@ -166,6 +181,17 @@ ll_status gqa_attn_prefill_chunk(const void* qkv, const int64_t* position_ids, v
                                  void* k_cache, void* v_cache, int64_t ctx,
                                  int64_t B, int64_t S, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
                                  int32_t dtype, void* stream);
+
+/* Padding-free causal attention over packed sequences (parallel_attention.py §3: flash_attn_varlen_func
+ * with cu_seqlens_q = cu_seqlens_k = cu_seqlens, max_seqlen, causal=True):
+ *   o[t, h*d:(h+1)*d] = sum_{cu[i] <= j <= t} softmax_j(q_{t,h} . k_{j,c} / sqrt(d)) v_{j,c},
+ *   for the sequence i with cu[i] <= t < cu[i+1].
+ * qkv packed [total_tokens, (n_heads + 2 n_kv_heads) d] with q and k already rotated (read only);
+ * cu_seqlens, max_seqlen as in llama_layer_forward_varlen; o [total_tokens, n_heads d]. */
+ll_status gqa_attn_prefill_varlen(const void* qkv, const int32_t* cu_seqlens, int64_t n_seqs,
+                                  int64_t max_seqlen, int64_t total_tokens, void* o,
+                                  int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+                                  int32_t dtype, void* stream);
 
 /* Bytes of workspace gqa_attn_decode needs. */
 size_t gqa_attn_decode_workspace_bytes(int64_t B, int64_t n_heads, int64_t head_dim, int64_t ctx);

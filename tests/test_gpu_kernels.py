@@ -292,3 +292,30 @@ def test_attn_prefill_chunk_empty_prefix_equals_prefill():
     torch.cuda.synchronize()
     assert torch.equal(k1, k2) and torch.equal(v1, v2)
     assert ref.max_rel_err(to_f64(o2), to_f64(o1)) <= 1e-2
+
+
+# ------------------------------------------------------------------ varlen packed prefill
+VARLEN = [
+    # dtype, sequence lengths, nh, nkv, d
+    ("bf16", (130, 1, 0, 64, 200), 8, 2, 128),    # one-token and empty sequences, exact and ragged tiles
+    ("bf16", (70, 257), 6, 2, 64),                # g = 3
+    ("bf16", (33, 100), 16, 2, 128),              # g = 8
+    ("bf16", (10, 50), 4, 2, 96),                 # generic kernel
+    ("f32", (5, 20, 1), 4, 2, 16),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: f"{c[0]}-{'_'.join(map(str, c[1]))}-{c[2]}-{c[3]}-{c[4]}")
+def test_attn_prefill_varlen(case):
+    """gqa_attn_prefill_varlen against the oracle's attention_varlen (causal within each packed sequence)."""
+    require_gpu()
+    dtype, lens, nh, nkv, d = case
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    qkv = normal(9, 170, (T, (nh + 2 * nkv) * d), dtype)
+    q, k, v = ref.split_qkv(bits_to_f64(qkv, dtype), nh, nkv, d)
+    want = ref.attention_varlen(q, k, v, cu)
+    o = L.gqa_attn_prefill_varlen(to_dev(qkv, dtype), torch.from_numpy(cu).to(DEV), max(lens), nh, nkv, d)
+    got = to_f64(o)
+    assert got.shape == (T, nh * d)
+    assert ref.max_rel_err(got, want) <= tol(dtype)

@@ -232,6 +232,56 @@ def test_layer_chunk_matches_one_shot():
     assert ref.max_rel_err(a - xb, b - xb) <= 3e-2
 
 
+# ------------------------------------------------------------------ varlen packed prefill
+VARLEN_LAYER = [
+    (scaled(CONFIGS["llama3_8b_prefill"], B=1, S=1), (90, 130, 1)),
+    (scaled(CONFIGS["llama32_1b_prefill"], B=1, S=1), (64, 100)),
+    (scaled(CONFIGS["tiny_f32"], B=1, S=1), (7, 12, 1)),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_LAYER, ids=lambda c: f"{c[0].name}-{'_'.join(map(str, c[1]))}")
+def test_layer_varlen_small(case):
+    """llama_layer_forward_varlen against the oracle's layer_prefill_varlen, RoPE at in-sequence positions
+    (the rmpad convention of parallel_attention.py §4)."""
+    require_gpu()
+    base, lens = case
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    cfg = scaled(base, B=1, S=T)
+    W = make_weights(cfg, seed=3)
+    x = make_hidden(cfg, seed=3)[0]
+    pos = np.concatenate([np.arange(n) for n in lens]).astype(np.int64)
+    kv = max(lens)
+    x64 = bits_to_f64(x, cfg.dtype)
+    want = ref.layer_prefill_varlen(cfg, w64(W, cfg.dtype), x64, pos, cu, kv)
+    out = L.llama_layer_forward_varlen(layer_cfg(cfg), dev_weights(W, cfg.dtype), to_dev(x, cfg.dtype),
+                                       torch.from_numpy(pos).to(DEV), torch.from_numpy(cu).to(DEV), max(lens),
+                                       kv_seq_len=kv)
+    check(to_f64(out), x64, want["out"], want["attn_proj"] + want["mlp_out"], cfg.dtype, cfg.name)
+
+
+def test_layer_varlen_equals_separate_calls():
+    """Packing changes nothing per token: the varlen layer equals one llama_layer_forward per sequence,
+    bit for bit (every sequence longer than 64 tokens, so both runs use the same GEMM kernels)."""
+    require_gpu()
+    lens = (130, 257, 65)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    cfg = scaled(CONFIGS["llama3_8b_prefill"], B=1, S=T)
+    W = dev_weights(make_weights(cfg, seed=6), cfg.dtype)
+    x = to_dev(make_hidden(cfg, seed=6), cfg.dtype)[0]
+    pos = torch.from_numpy(np.concatenate([np.arange(n) for n in lens]).astype(np.int64)).to(DEV)
+    lc = layer_cfg(cfg)
+    kv = max(lens)
+    packed = L.llama_layer_forward_varlen(lc, W, x, pos, torch.from_numpy(cu).to(DEV), kv, kv_seq_len=kv)
+    for i, n in enumerate(lens):
+        a, b = int(cu[i]), int(cu[i + 1])
+        one = L.llama_layer_forward(lc, W, x[None, a:b].contiguous(), pos[None, a:b].contiguous(), kv_seq_len=kv)
+        torch.cuda.synchronize()
+        assert torch.equal(packed[a:b], one[0]), i
+
+
 # ------------------------------------------------------------------ full-size workloads, sampled rows
 def _sample_rows(cfg, n, seed=7):
     rng = np.random.default_rng([seed, 99])

@@ -9,10 +9,12 @@ from ._lib import (  # noqa: F401
     gqa_attn_decode,
     gqa_attn_prefill,
     gqa_attn_prefill_chunk,
+    gqa_attn_prefill_varlen,
     layer_workspace_bytes,
     last_error,
     llama_layer_forward,
     llama_layer_forward_chunk,
+    llama_layer_forward_varlen,
     load,
     profile_begin,
     profile_end,

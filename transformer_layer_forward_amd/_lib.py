@@ -22,8 +22,8 @@ ROPE_TYPES = {"default": 0, "linear": 1, "dynamic_ntk": 2, "llama3": 3}
 STATUS_NAMES = {0: "LL_OK", 1: "LL_EINVAL", 2: "LL_EUNSUPPORTED", 3: "LL_EHIP", 4: "LL_ENOMEM"}
 
 EXPORTED = (
-    "llama_layer_workspace_bytes", "llama_layer_forward", "llama_layer_forward_chunk", "rmsnorm", "rope_apply",
-    "gqa_attn_prefill", "gqa_attn_prefill_chunk",
+    "llama_layer_workspace_bytes", "llama_layer_forward", "llama_layer_forward_chunk", "llama_layer_forward_varlen",
+    "rmsnorm", "rope_apply", "gqa_attn_prefill", "gqa_attn_prefill_chunk", "gqa_attn_prefill_varlen",
     "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "swiglu_mlp_workspace_bytes", "swiglu_mlp",
     "ll_last_error", "ll_release_caches", "ll_profile_begin", "ll_profile_end", "ll_profile_stage_name",
     "ll_version",
@@ -107,6 +107,8 @@ def load() -> ctypes.CDLL:
                                         c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_sz, c_vp]),
         "llama_layer_forward_chunk": (c_i32, [ctypes.POINTER(LLLayerCfg), ctypes.POINTER(LLLayerWeights), c_vp, c_vp,
                                               c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_sz, c_vp]),
+        "llama_layer_forward_varlen": (c_i32, [ctypes.POINTER(LLLayerCfg), ctypes.POINTER(LLLayerWeights), c_vp,
+                                               c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
         "rmsnorm": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_d, c_i32, c_vp]),
         "rope_apply": (c_i32, [ctypes.POINTER(LLRope), c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i32,
                                c_vp]),
@@ -114,6 +116,7 @@ def load() -> ctypes.CDLL:
                                      c_i64, c_i64, c_i64, c_i32, c_vp]),
         "gqa_attn_prefill_chunk": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64,
                                            c_i32, c_vp]),
+        "gqa_attn_prefill_varlen": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp]),
         "gqa_attn_decode_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i64]),
         "gqa_attn_decode": (c_i32, [c_vp, ctypes.POINTER(LLRope), c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64,
                                     c_i64, c_i64, c_i32, c_vp, c_sz, c_vp]),
@@ -225,6 +228,21 @@ def gqa_attn_prefill_chunk(qkv: torch.Tensor, position_ids: torch.Tensor, k_cach
     return o
 
 
+def gqa_attn_prefill_varlen(qkv: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, n_heads: int,
+                            n_kv_heads: int, head_dim: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed qkv [T, (n_h + 2 n_kv) d] (q, k rotated), cu_seqlens [n+1] int32 -> o [T, n_h d], causal
+    within each sequence."""
+    lib = load()
+    T = qkv.shape[0]
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    o = out if out is not None else torch.empty((T, n_heads * head_dim), dtype=qkv.dtype, device=qkv.device)
+    _check(lib.gqa_attn_prefill_varlen(_ptr(qkv), _ptr(cu_seqlens), cu_seqlens.numel() - 1, int(max_seqlen), T,
+                                       _ptr(o), n_heads, n_kv_heads, head_dim, _dtype_code(qkv.dtype), _stream(qkv)),
+           "gqa_attn_prefill_varlen")
+    return o
+
+
 def gqa_attn_decode(qkv: torch.Tensor, pos: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, n_heads: int,
                     n_kv_heads: int, head_dim: int, rope: Optional[Rope] = None, kv_seq_len: int = 0,
                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -290,6 +308,34 @@ def llama_layer_forward(cfg: LayerConfig, weights: dict, hidden: torch.Tensor, p
     _check(lib.llama_layer_forward(ctypes.byref(c), ctypes.byref(w), _ptr(hidden), _ptr(position_ids), B, S,
                                    int(kv_seq_len), _ptr(k_cache), _ptr(v_cache), ctx, _ptr(y), _ptr(ws), ws.numel(),
                                    _stream(hidden)), "llama_layer_forward")
+    return y
+
+
+def llama_layer_forward_varlen(cfg: LayerConfig, weights: dict, hidden: torch.Tensor, position_ids: torch.Tensor,
+                               cu_seqlens: torch.Tensor, max_seqlen: int, kv_seq_len: Optional[int] = None,
+                               out: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed sequences: hidden [T, H], position_ids [T] int64, cu_seqlens [n+1] int32 (device);
+    kv_seq_len (RoPE table length) defaults to max_seqlen."""
+    lib = load()
+    T = hidden.shape[0]
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if kv_seq_len is None:
+        kv_seq_len = max(int(max_seqlen), 1)
+    c = cfg.to_c()
+    w = LLLayerWeights(*(weights[k].data_ptr() for k in ("w_qkv", "w_o", "w_gate_up", "w_down", "g_attn", "g_mlp")))
+    for k in ("w_qkv", "w_o", "w_gate_up", "w_down", "g_attn", "g_mlp"):
+        _ptr(weights[k])
+    need = lib.llama_layer_workspace_bytes(ctypes.byref(c), 1, T, 0)
+    if need == 0:
+        raise ValueError(f"invalid layer configuration: {last_error()}")
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=hidden.device)
+    y = out if out is not None else torch.empty_like(hidden)
+    _check(lib.llama_layer_forward_varlen(ctypes.byref(c), ctypes.byref(w), _ptr(hidden), _ptr(position_ids),
+                                          _ptr(cu_seqlens), cu_seqlens.numel() - 1, int(max_seqlen), T,
+                                          int(kv_seq_len), _ptr(y), _ptr(ws), ws.numel(), _stream(hidden)),
+           "llama_layer_forward_varlen")
     return y
 
 

@@ -437,6 +437,25 @@ ll_status gqa_attn_prefill_chunk(const void* qkv, const int64_t* position_ids, v
     return LL_OK;
 }
 
+ll_status gqa_attn_prefill_varlen(const void* qkv, const int32_t* cu_seqlens, int64_t n_seqs, int64_t max_seqlen,
+                                  int64_t total_tokens, void* o, int64_t n_heads, int64_t n_kv_heads,
+                                  int64_t head_dim, int32_t dtype, void* stream) {
+    ll_status st = check_attn_common(qkv, nullptr, nullptr, 0, o, nullptr, nullptr, 0, 1, total_tokens, n_heads,
+                                     n_kv_heads, head_dim, dtype);
+    if (st != LL_OK) return st;
+    if (n_seqs < 0 || max_seqlen < 0) return fail(LL_EINVAL, "n_seqs and max_seqlen must be >= 0");
+    if (n_seqs > kIntMax || max_seqlen > kIntMax) return fail(LL_EUNSUPPORTED, "n_seqs or max_seqlen exceeds 2^31-1");
+    if (max_seqlen > total_tokens) return fail(LL_EINVAL, "max_seqlen > total_tokens");
+    if (total_tokens == 0 || n_seqs == 0) return LL_OK;
+    if (!cu_seqlens) return fail(LL_EINVAL, "cu_seqlens is NULL");
+    hipError_t e = launch_attn_prefill_varlen(dtype, qkv, cu_seqlens, static_cast<int>(n_seqs),
+                                              static_cast<int>(max_seqlen), static_cast<int>(total_tokens), o,
+                                              static_cast<int>(n_heads), static_cast<int>(n_kv_heads),
+                                              static_cast<int>(head_dim), as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "gqa_attn_prefill_varlen launch");
+    return LL_OK;
+}
+
 size_t gqa_attn_decode_workspace_bytes(int64_t B, int64_t n_heads, int64_t head_dim, int64_t ctx) {
     if (B < 0 || n_heads <= 0 || head_dim <= 0 || ctx <= 0) return 0;
     return attn_decode_workspace_bytes(B, n_heads, head_dim, ctx);
@@ -509,10 +528,16 @@ size_t llama_layer_workspace_bytes(const ll_layer_cfg* cfg, int64_t B, int64_t S
     return layer_ws(cfg, B, S, (S == 1 && ctx > 0) ? ctx : 0).total;
 }
 
+struct Varlen {
+    const int32_t* cu;
+    int64_t nseq, max_seqlen;
+};
+
 static ll_status layer_forward_impl(const ll_layer_cfg* cfg, const ll_layer_weights* w, const void* hidden,
                                     const int64_t* position_ids, int64_t B, int64_t S, int64_t kv_seq_len,
                                     void* k_cache, void* v_cache, int64_t ctx, void* out, void* workspace,
-                                    size_t workspace_bytes, void* stream, bool chunk) {
+                                    size_t workspace_bytes, void* stream, bool chunk,
+                                    const Varlen* vl = nullptr) {
     ll_status st = check_cfg(cfg);
     if (st != LL_OK) return st;
     if (!w) return fail(LL_EINVAL, "weights is NULL");
@@ -595,7 +620,11 @@ static ll_status layer_forward_impl(const ll_layer_cfg* cfg, const ll_layer_weig
     }
     LL_CHECK_HIP(mark(), "hipEventRecord");
     // 3. attention on rotated q and k
-    if (chunk) {
+    if (vl) {
+        e = launch_attn_prefill_varlen(dt, qkv, vl->cu, static_cast<int>(vl->nseq), static_cast<int>(vl->max_seqlen),
+                                       static_cast<int>(S), o, static_cast<int>(s.nh), static_cast<int>(s.nkv),
+                                       static_cast<int>(s.d), stream_h);
+    } else if (chunk) {
         e = launch_attn_prefill_chunk(dt, qkv, position_ids, o, k_cache, v_cache, ctx, static_cast<int>(B),
                                       static_cast<int>(S), static_cast<int>(s.nh), static_cast<int>(s.nkv),
                                       static_cast<int>(s.d), stream_h);
@@ -635,6 +664,19 @@ ll_status llama_layer_forward(const ll_layer_cfg* cfg, const ll_layer_weights* w
                               void* stream) {
     return layer_forward_impl(cfg, w, hidden, position_ids, B, S, kv_seq_len, k_cache, v_cache, ctx, out, workspace,
                               workspace_bytes, stream, false);
+}
+
+ll_status llama_layer_forward_varlen(const ll_layer_cfg* cfg, const ll_layer_weights* w, const void* hidden,
+                                     const int64_t* position_ids, const int32_t* cu_seqlens, int64_t n_seqs,
+                                     int64_t max_seqlen, int64_t total_tokens, int64_t kv_seq_len, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (n_seqs < 0 || max_seqlen < 0 || total_tokens < 0) return fail(LL_EINVAL, "n_seqs, max_seqlen, total_tokens must be >= 0");
+    if (n_seqs > kIntMax || max_seqlen > kIntMax) return fail(LL_EUNSUPPORTED, "n_seqs or max_seqlen exceeds 2^31-1");
+    if (max_seqlen > total_tokens) return fail(LL_EINVAL, "max_seqlen > total_tokens");
+    if (total_tokens > 0 && n_seqs > 0 && !cu_seqlens) return fail(LL_EINVAL, "cu_seqlens is NULL");
+    const Varlen vl{cu_seqlens, n_seqs, max_seqlen};
+    return layer_forward_impl(cfg, w, hidden, position_ids, 1, total_tokens, kv_seq_len, nullptr, nullptr, 0, out,
+                              workspace, workspace_bytes, stream, false, &vl);
 }
 
 ll_status llama_layer_forward_chunk(const ll_layer_cfg* cfg, const ll_layer_weights* w, const void* hidden,

@@ -423,7 +423,8 @@ __device__ __forceinline__ int vt_phys(int r, int c) {
 template <int D, int HPB, bool CACHED>
 __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, bf16_t* __restrict__ out, bf16_t* __restrict__ kc,
-    bf16_t* __restrict__ vc, int64_t ctx, int B, int S, int nh, int nkv, float scale_log2) {
+    bf16_t* __restrict__ vc, int64_t ctx, int B, int S_max, int nh, int nkv, float scale_log2,
+    const int* __restrict__ cu, int total) {
     using C = PrefillCfg<D>;
     constexpr int NT = 128 * HPB, NW = NT / 64;
     constexpr int CH = D / 8;                        // 16-byte chunks per row
@@ -438,7 +439,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
 
     const int g = nh / nkv;
     const int hchunks = g / HPB;
-    const int nqb = (S + C::BQ - 1) / C::BQ;
+    const int nqb = (S_max + C::BQ - 1) / C::BQ;
     const int per_qb = B * nkv * hchunks;
     const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / per_qb;
     int rem = static_cast<int>(blockIdx.x) % per_qb;
@@ -447,19 +448,34 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     const int c = rem % nkv;
     const int b = rem / nkv;
 
+    // ---- the sequence: B sequences of S_max tokens, or (packed, cu given) sequence b = tokens
+    // cu[b] .. cu[b+1]-1 of `total`, clamped into range so any cu contents stay in bounds. Query blocks
+    // past the sequence's end have nothing to do.
+    int seq0, S;
+    if (cu != nullptr) {
+        const int a0 = min(max(cu[b], 0), total);
+        const int a1 = min(max(cu[b + 1], a0), total);
+        seq0 = a0;
+        S = min(a1 - a0, S_max);
+    } else {
+        seq0 = b * S_max;
+        S = S_max;
+    }
+    if (qb * C::BQ >= S) return;
+
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar descriptor choice
     const int lrow = lane & 15, lgrp = lane >> 4;
     const int h = c * g + hc * HPB + (wave >> 1);
     const int64_t rs = static_cast<int64_t>(nh + 2 * nkv) * D;  // packed row stride
-    const bf16_t* qkv_b = qkv + static_cast<int64_t>(b) * S * rs;
+    const bf16_t* qkv_b = qkv + static_cast<int64_t>(seq0) * rs;
     const int q0 = qb * C::BQ + (wave & 1) * 32;
 
     // ---- visibility: query i sees keys 0 .. lim(i). Over the call's own tokens lim(i) = i; over a
     // cache (chunked prefill on a prefix) the keys are cache slots and lim(i) = position_ids[b, i]
     // (clamped to the cache). The block's smallest and largest limits give the key tiles it visits
     // (0 .. hi / 64) and the first one that needs the mask.
-    const int64_t* pos_b = CACHED ? pos + static_cast<int64_t>(b) * S : nullptr;
+    const int64_t* pos_b = CACHED ? pos + seq0 : nullptr;
     auto lim_of = [&](int qi) -> int {
         if constexpr (CACHED) return static_cast<int>(clamp_pos(pos_b[qi], ctx));
         else return qi;
@@ -521,7 +537,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     // ---- cache append: the first head chunk of each query block copies the block's own keys and
     // values (its diagonal tile) to their slots, so every token is written exactly once
     if (!CACHED && kc != nullptr && hc == 0) {
-        const int64_t* pos_b = pos + static_cast<int64_t>(b) * S;
+        const int64_t* pos_b = pos + seq0;
         for (int job = tid; job < 2 * C::BKV * CH; job += NT) {
             const bool isv = job >= C::BKV * CH;
             const int jj = isv ? job - C::BKV * CH : job;
@@ -703,7 +719,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
         const float inv = 1.f / rows_sum(l_i[qf]);
         const int qi = q0 + qf * 16 + lrow;
         if (qi >= S) continue;
-        bf16_t* op = out + (static_cast<int64_t>(b) * S + qi) * nh * D + static_cast<int64_t>(h) * D;
+        bf16_t* op = out + (static_cast<int64_t>(seq0) + qi) * nh * D + static_cast<int64_t>(h) * D;
 #pragma unroll
         for (int a = 0; a < C::DF; ++a) {
             const f32x4 v = oacc[a][qf];
@@ -762,7 +778,8 @@ __global__ __launch_bounds__(256) void attn_prefill_generic_kernel(const T* __re
                                                                    const int64_t* __restrict__ pos,
                                                                    const float2* __restrict__ cs, int64_t rope_rows,
                                                                    int il, T* __restrict__ out, int B, int S, int nh,
-                                                                   int nkv, int d, float scale) {
+                                                                   int nkv, int d, float scale,
+                                                                   const int* __restrict__ cu, int nseq) {
     const int lane = threadIdx.x & 63;
     const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (w >= static_cast<int64_t>(B) * S * nh) return;
@@ -774,11 +791,24 @@ __global__ __launch_bounds__(256) void attn_prefill_generic_kernel(const T* __re
     const int64_t rs = static_cast<int64_t>(nh + 2 * nkv) * d;
     const T* base = qkv + static_cast<int64_t>(b) * S * rs;
     const int64_t* pb = pos ? pos + static_cast<int64_t>(b) * S : nullptr;
+    // packed sequences (cu given, B = 1, S = all tokens): token i attends from the first token of its
+    // own sequence, the largest cu[k] <= i (binary search; cu entries clamped into [0, S])
+    int start = 0;
+    if (cu != nullptr) {
+        auto cuc = [&](int k_) { return min(max(cu[k_], 0), S); };
+        int lo_ = 0, hi_ = nseq;
+        while (lo_ < hi_) {
+            const int mid = (lo_ + hi_ + 1) >> 1;
+            if (cuc(mid) <= i) lo_ = mid;
+            else hi_ = mid - 1;
+        }
+        start = min(cuc(lo_), i);
+    }
     float q[GEN_DPL], acc[GEN_DPL] = {0.f, 0.f, 0.f, 0.f};
     gen_load_head<T>(base + static_cast<int64_t>(i) * rs + static_cast<int64_t>(h) * d, d, lane, cs, rope_rows,
                      cs ? pb[i] : 0, il, q);
     float m = -INFINITY, l = 0.f;
-    for (int j = 0; j <= i; ++j) {
+    for (int j = start; j <= i; ++j) {
         float k[GEN_DPL];
         const T* kp = base + static_cast<int64_t>(j) * rs + static_cast<int64_t>(nh + c) * d;
         gen_load_head<T>(kp, d, lane, cs, rope_rows, cs ? pb[j] : 0, il, k);
@@ -1170,7 +1200,7 @@ static hipError_t prefill_go(const void* qkv, const int64_t* pos, const RopeTab*
     if (!ROPE && offsets_ok)
         hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, false>), dim3(blocks), dim3(128 * HPB), 0, st,
                            static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
-                           static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2);
+                           static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2, nullptr, 0);
     else
         hipLaunchKernelGGL((attn_prefill_mfma_kernel<D, HPB, ROPE, IL>), dim3(blocks), dim3(128 * HPB), 0, st,
                            static_cast<const bf16_t*>(qkv), pos, tab ? tab->cs : nullptr, tab ? tab->rows : 1,
@@ -1212,11 +1242,11 @@ hipError_t launch_attn_prefill(int dtype, const void* qkv, const int64_t* pos, c
     if (dtype == LL_BF16)
         hipLaunchKernelGGL(attn_prefill_generic_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st,
                            static_cast<const bf16_t*>(qkv), pos, cs, rows, il, static_cast<bf16_t*>(o), B, S, nh, nkv,
-                           d, scale);
+                           d, scale, nullptr, 0);
     else
         hipLaunchKernelGGL(attn_prefill_generic_kernel<float>, dim3(blocks), dim3(256), 0, st,
                            static_cast<const float*>(qkv), pos, cs, rows, il, static_cast<float*>(o), B, S, nh, nkv, d,
-                           scale);
+                           scale, nullptr, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || kc == nullptr) return e;
     const int64_t kw = static_cast<int64_t>(B) * S * nkv;
@@ -1320,7 +1350,7 @@ static hipError_t chunk_go(const void* qkv, const int64_t* pos, void* o, void* k
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
     hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, true>), dim3(blocks), dim3(128 * HPB), 0, st,
                        static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
-                       static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2);
+                       static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2, nullptr, 0);
     return hipGetLastError();
 }
 
@@ -1362,6 +1392,51 @@ hipError_t launch_attn_prefill_chunk(int dtype, const void* qkv, const int64_t* 
         hipLaunchKernelGGL(attn_decode_generic_kernel<float>, dim3(blocks), dim3(256), 0, st,
                            static_cast<const float*>(qkv), pos, nullptr, 1, 0, static_cast<const float*>(kc),
                            static_cast<const float*>(vc), ctx, static_cast<float*>(o), B, S, nh, nkv, d, scale);
+    return hipGetLastError();
+}
+
+// Packed (varlen) prefill: sequence i is tokens cu[i] .. cu[i+1]-1 of `total`; causal attention within
+// each sequence; q and k already rotated.
+template <int D, int HPB>
+static hipError_t varlen_go(const void* qkv, const int* cu, int nseq, int max_seqlen, int total, void* o, int nh,
+                            int nkv, hipStream_t st) {
+    const int g = nh / nkv;
+    const int nqb = (max_seqlen + 63) / 64;
+    const unsigned blocks = static_cast<unsigned>(nqb) * nseq * nkv * (g / HPB);
+    const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
+    hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, false>), dim3(blocks), dim3(128 * HPB), 0, st,
+                       static_cast<const bf16_t*>(qkv), nullptr, static_cast<bf16_t*>(o), nullptr, nullptr, 1, nseq,
+                       max_seqlen, nh, nkv, scale_log2, cu, total);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t varlen_hpb_sel(const void* qkv, const int* cu, int nseq, int max_seqlen, int total, void* o, int nh,
+                                 int nkv, hipStream_t st) {
+    const int g = nh / nkv;
+    if (g % 4 == 0) return varlen_go<D, 4>(qkv, cu, nseq, max_seqlen, total, o, nh, nkv, st);
+    if (g % 2 == 0) return varlen_go<D, 2>(qkv, cu, nseq, max_seqlen, total, o, nh, nkv, st);
+    return varlen_go<D, 1>(qkv, cu, nseq, max_seqlen, total, o, nh, nkv, st);
+}
+
+hipError_t launch_attn_prefill_varlen(int dtype, const void* qkv, const int* cu, int nseq, int max_seqlen, int total,
+                                      void* o, int nh, int nkv, int d, hipStream_t st) {
+    if (nseq == 0 || total == 0 || max_seqlen == 0) return hipSuccess;
+    const bool offsets_ok = static_cast<int64_t>(max_seqlen) * (nh + 2 * nkv) * d * 2 < (int64_t(1) << 32);
+    if (attn_mfma_supported(dtype, d, nh, nkv) && offsets_ok) {
+        if (d == 128) return varlen_hpb_sel<128>(qkv, cu, nseq, max_seqlen, total, o, nh, nkv, st);
+        return varlen_hpb_sel<64>(qkv, cu, nseq, max_seqlen, total, o, nh, nkv, st);
+    }
+    const unsigned blocks = static_cast<unsigned>((static_cast<int64_t>(total) * nh + 3) / 4);
+    const float scale = 1.f / sqrtf(static_cast<float>(d));
+    if (dtype == LL_BF16)
+        hipLaunchKernelGGL(attn_prefill_generic_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st,
+                           static_cast<const bf16_t*>(qkv), nullptr, nullptr, 1, 0, static_cast<bf16_t*>(o), 1, total,
+                           nh, nkv, d, scale, cu, nseq);
+    else
+        hipLaunchKernelGGL(attn_prefill_generic_kernel<float>, dim3(blocks), dim3(256), 0, st,
+                           static_cast<const float*>(qkv), nullptr, nullptr, 1, 0, static_cast<float*>(o), 1, total,
+                           nh, nkv, d, scale, cu, nseq);
     return hipGetLastError();
 }
 

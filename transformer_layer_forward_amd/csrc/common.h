@@ -95,6 +95,9 @@ hipError_t launch_attn_prefill(int dtype, const void* qkv, const int64_t* pos, c
 // then query (b, s) attends over cache slots 0 .. pos[b, s]
 hipError_t launch_attn_prefill_chunk(int dtype, const void* qkv, const int64_t* pos, void* o, void* kc, void* vc,
                                      int64_t ctx, int B, int S, int nh, int nkv, int d, hipStream_t st);
+// packed (varlen) prefill: q and k already rotated; sequence i is tokens cu[i] .. cu[i+1]-1 of `total`
+hipError_t launch_attn_prefill_varlen(int dtype, const void* qkv, const int* cu, int nseq, int max_seqlen, int total,
+                                      void* o, int nh, int nkv, int d, hipStream_t st);
 size_t attn_decode_workspace_bytes(int64_t B, int64_t nh, int64_t d, int64_t ctx);
 hipError_t launch_attn_decode(int dtype, const void* qkv, const int64_t* pos, const RopeTab* tab, int interleaved,
                               void* kc, void* vc, int64_t ctx, void* o, int B, int nh, int nkv, int d, void* ws,
