@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=[WORKLOAD, "llama32_1b_prefill", "llama3_8b_long_llama3rope", "llama3_8b_decode",
-                             CHUNK_WORKLOAD],
+                             CHUNK_WORKLOAD, VARLEN_WORKLOAD],
                     help="the headline line is the 8B prefill; the others print the same record for that workload")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the cache-cold decode measurement that the headline run adds as \"decode\"")
@@ -247,6 +247,49 @@ def run_chunk(L, torch, np, cfg, W, args):
     return wall * 1e3 / args.steps, stages
 
 
+VARLEN_WORKLOAD = "llama3_8b_varlen"
+VARLEN_TOKENS = 8192
+
+
+def varlen_lengths(np):
+    """Seeded ragged length mix for the packed workload: lengths integer-uniform on [64, 2048] drawn
+    until VARLEN_TOKENS tokens are reached (the last one shortened to fit)."""
+    rng = np.random.default_rng([0, 20])
+    lens, tot = [], 0
+    while tot < VARLEN_TOKENS:
+        n = int(min(rng.integers(64, 2049), VARLEN_TOKENS - tot))
+        lens.append(n)
+        tot += n
+    return lens
+
+
+def run_varlen(L, torch, np, cfg, W, args, lens):
+    """Packed prefill of the sequences `lens` (total VARLEN_TOKENS) through llama_layer_forward_varlen,
+    RoPE at in-sequence positions. Returns (ms_per_step, stages)."""
+    from synth_inputs import make_hidden
+    dev = "cuda:0"
+    x = torch.from_numpy(np.ascontiguousarray(make_hidden(cfg, seed=0)[0]).view(np.int16)).to(dev).view(torch.bfloat16)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    pos = torch.from_numpy(np.concatenate([np.arange(n) for n in lens]).astype(np.int64)).to(dev)
+    lc = lib_config(L, cfg, torch)
+    T = sum(lens)
+    ws = torch.empty(L.layer_workspace_bytes(lc, 1, T), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+    mx = max(lens)
+    for _ in range(args.warmup):
+        L.llama_layer_forward_varlen(lc, W, x, pos, cu, mx, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    L.profile_begin(args.steps)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        L.llama_layer_forward_varlen(lc, W, x, pos, cu, mx, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = L.profile_end()
+    assert torch.isfinite(out.float()).all().item()
+    return wall * 1e3 / args.steps, stages
+
+
 def decode_inputs(L, torch, np, cfg, W):
     """Decode step inputs on the device: hidden [B,1,H], positions [B] integer-uniform on [1024, ctx),
     and K/V caches [B, ctx, n_kv, d] of N(0,1) values drawn by torch's seeded device generator (the
@@ -358,9 +401,15 @@ def main():
     from synth_inputs import CONFIGS, make_weights
 
     chunk = args.workload == CHUNK_WORKLOAD
+    varlen = args.workload == VARLEN_WORKLOAD
+    lens = None
     if chunk:
         from synth_inputs import scaled
         cfg = scaled(CONFIGS[WORKLOAD], name=CHUNK_WORKLOAD, S=2048)
+    elif varlen:
+        from synth_inputs import scaled
+        lens = varlen_lengths(np)
+        cfg = scaled(CONFIGS[WORKLOAD], name=VARLEN_WORKLOAD, B=1, S=sum(lens))
     else:
         cfg = CONFIGS[args.workload]
     dev = "cuda:0"
@@ -400,6 +449,9 @@ def main():
     if chunk:
         ms_per_step, stages = run_chunk(L, torch, np, cfg, W, args)
         x_bits = None
+    elif varlen:
+        ms_per_step, stages = run_varlen(L, torch, np, cfg, W, args, lens)
+        x_bits = None
     else:
         ms_per_step, stages, x_bits = run_prefill(L, torch, np, cfg, W, args)
     tokens = cfg.B * cfg.S
@@ -409,7 +461,10 @@ def main():
     achieved = gate_up_flops / (stage_ms(stages, "gate_up_silu") / 1e3) / 1e12
     start = CHUNK_START if chunk else 0
     # QK^T and PV over the visible (query, key) pairs: query s sees keys 0 .. start + s
-    attn_flops = 4.0 * cfg.B * cfg.n_heads * d * (cfg.S * start + cfg.S * (cfg.S + 1) / 2)
+    if varlen:
+        attn_flops = 4.0 * cfg.n_heads * d * sum(n * (n + 1) / 2 for n in lens)
+    else:
+        attn_flops = 4.0 * cfg.B * cfg.n_heads * d * (cfg.S * start + cfg.S * (cfg.S + 1) / 2)
     gemm_flops = gemm_flops_per_token(cfg) * M
     gemm_ms = sum(stage_ms(stages, k) for k in ("qkv_proj", "o_proj_residual", "gate_up_silu", "down_residual"))
     norm_bytes = 2 * (2 * M * H * 2 + H * 2)
@@ -419,7 +474,10 @@ def main():
             "llama3_8b_long_llama3rope": "Llama-3-8B-shaped decoder layer, bf16 32k prefill, causal, "
                                          "Llama3 RoPE scaling",
             CHUNK_WORKLOAD: f"Llama-3-8B-shaped decoder layer, bf16 chunked prefill: {cfg.S} new tokens per "
-                            f"sequence on a {CHUNK_START}-token cached prefix ({CHUNK_CTX}-slot KV cache)"}[args.workload]
+                            f"sequence on a {CHUNK_START}-token cached prefix ({CHUNK_CTX}-slot KV cache)",
+            VARLEN_WORKLOAD: f"Llama-3-8B-shaped decoder layer, bf16 varlen packed prefill: {len(lens or [])} "
+                             f"sequences of 64-2048 tokens packed into {cfg.S} tokens, causal within each"
+            }[args.workload]
     metric = ("decoder-layer tokens/s (Llama-3-8B shape, bf16) + attention MFMA util %"
               if args.workload == WORKLOAD else f"decoder-layer tokens/s ({name})")
     rec = {
@@ -431,7 +489,8 @@ def main():
         "data": ("synthetic (seeded N(0,1) hidden" + (" and cache prefix" if chunk else "")
                  + ", N(0,0.02) weights, 1+N(0,0.1) gains)"),
         "config": {"workload": name, "B": cfg.B, "S": cfg.S, **shape, "tokens_per_step": tokens,
-                   **({"prefix": CHUNK_START, "ctx": CHUNK_CTX} if chunk else {})},
+                   **({"prefix": CHUNK_START, "ctx": CHUNK_CTX} if chunk else {}),
+                   **({"seq_lens": lens} if varlen else {})},
         "attention_mfma_util_pct": round(100.0 * attn_flops / (stage_ms(stages, "attention") / 1e3) / 1e12
                                          / MI355X_BF16_DENSE_TFLOPS, 2),
         "gemm_mfma_util_pct": round(100.0 * gemm_flops / (gemm_ms / 1e3) / 1e12 / MI355X_BF16_DENSE_TFLOPS, 2),
