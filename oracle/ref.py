@@ -418,6 +418,24 @@ def layer_decode(cfg, W: dict, x: np.ndarray, pos: np.ndarray, kv_seq_len: int, 
     return {k: np.stack(v) for k, v in outs.items()}
 
 
+# ---------------------------------------------------------------- the model stack
+def embedding(table: np.ndarray, tokens: np.ndarray) -> np.ndarray:
+    """nn.Embedding lookup ([meta-qa] #### 5 tok_embeddings(tokens)): row tokens[b, s] of table [vocab, H]."""
+    return np.asarray(table, dtype=F64)[np.asarray(tokens)]
+
+
+def model_prefill(cfg, M: dict, tokens: np.ndarray, position_ids: np.ndarray, kv_seq_len: int) -> dict:
+    """The model driver of [meta-qa] #### 5 (Transformer.forward at start_pos = 0): token embeddings,
+    the decoder layers in order, the final RMSNorm, then the output projection to vocabulary logits
+    (output(norm(h)), no bias). M holds fp64 "layers" (list of layer weight dicts), "tok_embeddings"
+    [vocab, H], "g_final" [H] and "lm_head" [vocab, H]. Returns the last hidden state and the logits."""
+    h = embedding(M["tok_embeddings"], tokens)
+    for W in M["layers"]:
+        h = layer_prefill(cfg, W, h, position_ids, kv_seq_len)["out"]
+    hn = rmsnorm(h, M["g_final"], cfg.eps)
+    return {"h": h, "logits": linear(hn, M["lm_head"])}
+
+
 # ---------------------------------------------------------------- comparison metric
 def max_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     """Normwise max relative error: max|got - ref| / max|ref| (the reading of "max relative

@@ -24,6 +24,7 @@ import numpy as np
 
 # tensor stream ids
 K_HIDDEN, K_WQKV, K_WO, K_WGU, K_WDOWN, K_GATTN, K_GMLP, K_POS, K_KCACHE, K_VCACHE = range(10)
+K_EMB, K_GFINAL, K_LMHEAD, K_TOKENS = 30, 31, 32, 33
 
 
 @dataclasses.dataclass(frozen=True)
@@ -128,6 +129,25 @@ def make_weights(cfg: LayerCfg, seed: int = 0) -> dict:
         "g_attn": _draw(seed, K_GATTN, (cfg.hidden,), 0.1, 1.0, d),
         "g_mlp": _draw(seed, K_GMLP, (cfg.hidden,), 0.1, 1.0, d),
     }
+
+
+def make_model_weights(cfg: LayerCfg, n_layers: int, vocab: int, seed: int = 0) -> dict:
+    """A synthetic model stack: layer l gets make_weights(cfg, seed * 1000 + l); token embeddings
+    [vocab, H] ~ N(0,1) (the hidden-state distribution of the layer workloads), final RMSNorm gain
+    1+N(0,0.1), output projection [vocab, H] ~ N(0,0.02)."""
+    d = cfg.dtype
+    return {
+        "layers": [make_weights(cfg, seed * 1000 + l) for l in range(n_layers)],
+        "tok_embeddings": _draw(seed, K_EMB, (vocab, cfg.hidden), 1.0, 0.0, d),
+        "g_final": _draw(seed, K_GFINAL, (cfg.hidden,), 0.1, 1.0, d),
+        "lm_head": _draw(seed, K_LMHEAD, (vocab, cfg.hidden), 0.02, 0.0, d),
+    }
+
+
+def make_tokens(cfg: LayerCfg, vocab: int, seed: int = 0) -> np.ndarray:
+    """Token ids [B, S] integer-uniform on [0, vocab) (int64)."""
+    rng = np.random.default_rng([seed, K_TOKENS])
+    return rng.integers(0, vocab, size=(cfg.B, cfg.S), dtype=np.int64)
 
 
 def make_hidden(cfg: LayerCfg, seed: int = 0) -> np.ndarray:

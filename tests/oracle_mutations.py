@@ -51,6 +51,9 @@ MUTS = [
     ("varlen layer mlp residual", "\"out\": mlp_out + h}", "\"out\": mlp_out + x}"),
     ("varlen attn residual dropped", "h = np.add(x, attn_proj)", "h = np.add(0.0, attn_proj)"),
     ("varlen second norm uses g_attn", "hn = rmsnorm(h, g=W[\"g_mlp\"], eps=cfg.eps)", "hn = rmsnorm(h, g=W[\"g_attn\"], eps=cfg.eps)"),
+    ("embedding row off by one", "return np.asarray(table, dtype=F64)[np.asarray(tokens)]", "return np.asarray(table, dtype=F64)[np.asarray(tokens) - 1]"),
+    ("model final norm dropped", "hn = rmsnorm(h, M[\"g_final\"], cfg.eps)", "hn = h"),
+    ("model layers reversed", "for W in M[\"layers\"]:", "for W in M[\"layers\"][::-1]:"),
     ("rows path second norm eps", "hn = rmsnorm(h, W[\"g_mlp\"], cfg.eps)\n            act", "hn = rmsnorm(h, W[\"g_mlp\"], 0.1)\n            act"),
 ]
 results = []

@@ -489,6 +489,66 @@ def test_layer_varlen_equals_per_sequence_layer():
         np.testing.assert_allclose(got["out"][a:b], one["out"][0], rtol=1e-13, atol=1e-13)
 
 
+# ------------------------------------------------------------------ model stack
+def test_embedding_is_one_hot_product():
+    """nn.Embedding(vocab, dim)(tokens) equals one_hot(tokens) @ table (the lookup as a matrix product)."""
+    table = RNG.standard_normal((11, 6))
+    tok = np.array([[3, 0, 10], [7, 7, 1]])
+    one_hot = np.eye(11)[tok]
+    np.testing.assert_array_equal(ref.embedding(table, tok), one_hot @ table)
+
+
+def _model64(cfg, n_layers, vocab, seed=0):
+    from synth_inputs import make_model_weights
+    M = make_model_weights(cfg, n_layers, vocab, seed)
+    return {"layers": [{k: to_f64(v, cfg.dtype) for k, v in W.items()} for W in M["layers"]],
+            "tok_embeddings": to_f64(M["tok_embeddings"], cfg.dtype), "g_final": to_f64(M["g_final"], cfg.dtype),
+            "lm_head": to_f64(M["lm_head"], cfg.dtype)}
+
+
+def test_model_without_layers_is_head_of_embeddings():
+    """With no decoder layers the driver is output(norm(tok_embeddings(tokens))) ([meta-qa] #### 5)."""
+    cfg = scaled(CONFIGS["tiny_f32"], B=2, S=5)
+    M = _model64(cfg, 0, 23)
+    tok = np.array([[1, 22, 0, 5, 5], [9, 3, 3, 17, 2]])
+    pos = make_prefill_positions(cfg)
+    got = ref.model_prefill(cfg, M, tok, pos, 16)["logits"]
+    x = M["tok_embeddings"][tok]
+    want = (x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + cfg.eps) * M["g_final"]) @ M["lm_head"].T
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13)
+    assert got.shape == (2, 5, 23)
+
+
+def test_model_stack_causality_and_layer_order():
+    """Logits of token i depend only on tokens 0..i (bitwise), and the layers apply in order (swapping two
+    different layers changes the result)."""
+    cfg = scaled(CONFIGS["tiny_f32"], B=1, S=9)
+    M = _model64(cfg, 2, 31)
+    pos = make_prefill_positions(cfg)
+    tok = np.array([[4, 8, 15, 16, 23, 30, 2, 7, 1]])
+    a = ref.model_prefill(cfg, M, tok, pos, 16)["logits"]
+    tok2 = tok.copy()
+    tok2[0, 6:] = [0, 0, 0]
+    b = ref.model_prefill(cfg, M, tok2, pos, 16)["logits"]
+    np.testing.assert_array_equal(a[:, :6], b[:, :6])
+    assert not np.array_equal(a[:, 6:], b[:, 6:])
+    M2 = dict(M, layers=M["layers"][::-1])
+    assert not np.allclose(ref.model_prefill(cfg, M2, tok, pos, 16)["logits"], a)
+
+
+def test_model_applies_layers_in_list_order():
+    """for layer in self.layers: h = layer(h, ...) ([meta-qa] #### 5): the stack equals applying the
+    layer forward to the embeddings, first layer first."""
+    cfg = scaled(CONFIGS["tiny_f32"], B=1, S=7)
+    M = _model64(cfg, 2, 19)
+    pos = make_prefill_positions(cfg)
+    tok = np.array([[3, 1, 4, 1, 5, 9, 2]])
+    h = M["tok_embeddings"][tok]
+    for W in M["layers"]:
+        h = ref.layer_prefill(cfg, W, h, pos, 16)["out"]
+    np.testing.assert_array_equal(ref.model_prefill(cfg, M, tok, pos, 16)["h"], h)
+
+
 # ------------------------------------------------------------------ shapes
 def test_layer_shapes_match_lecture_printout():
     """Golden: the Llama-3.2-1B layer dump on NJU lecture 5 fixes the projection shapes of the
