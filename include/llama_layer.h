@@ -141,6 +141,23 @@ ll_status llama_layer_forward_varlen(const ll_layer_cfg* cfg, const ll_layer_wei
                                      int64_t total_tokens, int64_t kv_seq_len,
                                      void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace llama_model_forward needs for B sequences of S tokens. 0 for invalid input. */
+size_t llama_model_workspace_bytes(const ll_layer_cfg* cfg, int64_t vocab, int64_t B, int64_t S);
+
+/* The model stack at prefill (CSDN answer "#### 5." Transformer.forward with start_pos = 0: h =
+ * tok_embeddings(tokens); for layer in layers: h = layer(h); return output(norm(h))):
+ *   layers          host array of n_layers weight sets (device pointers), applied in order;
+ *   tok_embeddings  [vocab, H]; final_norm_gain [H] (the final RMSNorm, eps = cfg->eps);
+ *   lm_head         [vocab, H] output projection, logits = norm(h) lm_head^T (no bias);
+ *   tokens          [B, S] int64 ids (ids outside [0, vocab) are clamped); position_ids [B, S] as in
+ *                   llama_layer_forward; logits [B, S, vocab] in cfg->dtype.
+ * No KV cache (prefill only). workspace: at least llama_model_workspace_bytes bytes, scratch. */
+ll_status llama_model_forward(const ll_layer_cfg* cfg, int64_t n_layers, const ll_layer_weights* layers,
+                              const void* tok_embeddings, const void* final_norm_gain, const void* lm_head,
+                              int64_t vocab, const int64_t* tokens, const int64_t* position_ids,
+                              int64_t B, int64_t S, int64_t kv_seq_len, void* logits,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* RMSNorm over rows (llama3 结构详解 §3.1; NJU lecture 5 "编码实现RMSNorm"):
  *   y[r, i] = x[r, i] / sqrt(mean_i x[r, i]^2 + eps) * gain[i], fp32 accumulation.
  * x, y [rows, hidden] (y may equal x); gain [hidden]. */

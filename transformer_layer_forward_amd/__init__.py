@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     llama_layer_forward,
     llama_layer_forward_chunk,
     llama_layer_forward_varlen,
+    llama_model_forward,
     load,
     profile_begin,
     profile_end,

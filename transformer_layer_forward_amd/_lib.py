@@ -23,6 +23,7 @@ STATUS_NAMES = {0: "LL_OK", 1: "LL_EINVAL", 2: "LL_EUNSUPPORTED", 3: "LL_EHIP", 
 
 EXPORTED = (
     "llama_layer_workspace_bytes", "llama_layer_forward", "llama_layer_forward_chunk", "llama_layer_forward_varlen",
+    "llama_model_workspace_bytes", "llama_model_forward",
     "rmsnorm", "rope_apply", "gqa_attn_prefill", "gqa_attn_prefill_chunk", "gqa_attn_prefill_varlen",
     "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "swiglu_mlp_workspace_bytes", "swiglu_mlp",
     "ll_last_error", "ll_release_caches", "ll_profile_begin", "ll_profile_end", "ll_profile_stage_name",
@@ -109,6 +110,9 @@ def load() -> ctypes.CDLL:
                                               c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_sz, c_vp]),
         "llama_layer_forward_varlen": (c_i32, [ctypes.POINTER(LLLayerCfg), ctypes.POINTER(LLLayerWeights), c_vp,
                                                c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
+        "llama_model_workspace_bytes": (c_sz, [ctypes.POINTER(LLLayerCfg), c_i64, c_i64, c_i64]),
+        "llama_model_forward": (c_i32, [ctypes.POINTER(LLLayerCfg), c_i64, ctypes.POINTER(LLLayerWeights), c_vp, c_vp,
+                                        c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
         "rmsnorm": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_d, c_i32, c_vp]),
         "rope_apply": (c_i32, [ctypes.POINTER(LLRope), c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i32,
                                c_vp]),
@@ -363,6 +367,34 @@ def llama_layer_forward_chunk(cfg: LayerConfig, weights: dict, hidden: torch.Ten
     _check(lib.llama_layer_forward_chunk(ctypes.byref(c), ctypes.byref(w), _ptr(hidden), _ptr(position_ids), B, S,
                                          int(kv_seq_len), _ptr(k_cache), _ptr(v_cache), ctx, _ptr(y), _ptr(ws),
                                          ws.numel(), _stream(hidden)), "llama_layer_forward_chunk")
+    return y
+
+
+def llama_model_forward(cfg: LayerConfig, model: dict, tokens: torch.Tensor, position_ids: torch.Tensor,
+                        kv_seq_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """model: "layers" (list of layer weight dicts), "tok_embeddings" [vocab, H], "g_final" [H],
+    "lm_head" [vocab, H]; tokens, position_ids [B, S] int64 -> logits [B, S, vocab]."""
+    lib = load()
+    B, S = tokens.shape
+    vocab = model["lm_head"].shape[0]
+    if kv_seq_len is None:
+        kv_seq_len = S
+    c = cfg.to_c()
+    names = ("w_qkv", "w_o", "w_gate_up", "w_down", "g_attn", "g_mlp")
+    n = len(model["layers"])
+    arr = (LLLayerWeights * max(n, 1))()
+    for i, W in enumerate(model["layers"]):
+        arr[i] = LLLayerWeights(*(_ptr(W[k]) for k in names))
+    need = lib.llama_model_workspace_bytes(ctypes.byref(c), vocab, B, S)
+    if need == 0:
+        raise ValueError(f"invalid model configuration: {last_error()}")
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=tokens.device)
+    y = out if out is not None else torch.empty((B, S, vocab), dtype=model["lm_head"].dtype, device=tokens.device)
+    _check(lib.llama_model_forward(ctypes.byref(c), n, arr, _ptr(model["tok_embeddings"]), _ptr(model["g_final"]),
+                                   _ptr(model["lm_head"]), vocab, _ptr(tokens), _ptr(position_ids), B, S,
+                                   int(kv_seq_len), _ptr(y), _ptr(ws), ws.numel(), _stream(tokens)),
+           "llama_model_forward")
     return y
 
 

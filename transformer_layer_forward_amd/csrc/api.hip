@@ -666,6 +666,64 @@ ll_status llama_layer_forward(const ll_layer_cfg* cfg, const ll_layer_weights* w
                               workspace_bytes, stream, false);
 }
 
+size_t llama_model_workspace_bytes(const ll_layer_cfg* cfg, int64_t vocab, int64_t B, int64_t S) {
+    if (!cfg || vocab <= 0 || B < 0 || S < 0) return 0;
+    if (check_cfg(cfg) != LL_OK) return 0;
+    const Shapes s = shapes_of(cfg, B, S);
+    const size_t act = round_up(static_cast<size_t>(s.M * s.H) * s.es);
+    return 2 * act + round_up(gemm_workspace_bytes(cfg->dtype, s.M, vocab, s.H, EPI_STORE)) +
+           layer_ws(cfg, B, S, 0).total;
+}
+
+ll_status llama_model_forward(const ll_layer_cfg* cfg, int64_t n_layers, const ll_layer_weights* layers,
+                              const void* tok_embeddings, const void* final_norm_gain, const void* lm_head,
+                              int64_t vocab, const int64_t* tokens, const int64_t* position_ids, int64_t B,
+                              int64_t S, int64_t kv_seq_len, void* logits, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    ll_status st = check_cfg(cfg);
+    if (st != LL_OK) return st;
+    if (n_layers < 0) return fail(LL_EINVAL, "n_layers must be >= 0");
+    if (n_layers > 0 && !layers) return fail(LL_EINVAL, "layers is NULL");
+    if (vocab <= 0) return fail(LL_EINVAL, "vocab must be > 0");
+    if (vocab > kIntMax) return fail(LL_EUNSUPPORTED, "vocab exceeds 2^31-1");
+    if (B < 0 || S < 0) return fail(LL_EINVAL, "B and S must be >= 0");
+    if (B > kIntMax || S > kIntMax || B * S > kIntMax) return fail(LL_EUNSUPPORTED, "B*S exceeds 2^31-1");
+    if (kv_seq_len <= 0) return fail(LL_EINVAL, "kv_seq_len must be > 0");
+    if (B * S == 0) return LL_OK;
+    if (!tok_embeddings || !final_norm_gain || !lm_head || !tokens || !position_ids || !logits)
+        return fail(LL_EINVAL, "NULL tensor pointer");
+    const void* ptrs[] = {tok_embeddings, final_norm_gain, lm_head, logits, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(LL_EINVAL, "pointers must be 16-byte aligned");
+    const Shapes s = shapes_of(cfg, B, S);
+    const size_t act = round_up(static_cast<size_t>(s.M * s.H) * s.es);
+    const size_t gws = round_up(gemm_workspace_bytes(cfg->dtype, s.M, vocab, s.H, EPI_STORE));
+    const size_t lws = layer_ws(cfg, B, S, 0).total;
+    const size_t need = 2 * act + gws + lws;
+    if (!workspace || workspace_bytes < need)
+        return fail(LL_EINVAL, "workspace too small: %zu < %zu", workspace_bytes, need);
+    char* ws = static_cast<char*>(workspace);
+    void* h = ws;
+    void* hn = ws + act;
+    void* g = ws + 2 * act;
+    void* lw = ws + 2 * act + gws;
+    hipStream_t stream_h = as_stream(stream);
+    // h = tok_embeddings(tokens); every layer runs in place on h
+    hipError_t e = launch_embedding(cfg->dtype, tok_embeddings, tokens, h, s.M, s.H, vocab, stream_h);
+    if (e != hipSuccess) return hip_fail(e, "embedding launch");
+    for (int64_t l = 0; l < n_layers; ++l) {
+        st = layer_forward_impl(cfg, &layers[l], h, position_ids, B, S, kv_seq_len, nullptr, nullptr, 0, h, lw, lws,
+                                stream, false);
+        if (st != LL_OK) return st;
+    }
+    // logits = output(norm(h))
+    e = launch_rmsnorm(cfg->dtype, h, final_norm_gain, hn, s.M, s.H, static_cast<float>(cfg->eps), stream_h);
+    if (e != hipSuccess) return hip_fail(e, "final rmsnorm launch");
+    e = launch_gemm(cfg->dtype, EPI_STORE, hn, lm_head, logits, nullptr, s.M, vocab, s.H, g, gws, stream_h);
+    if (e != hipSuccess) return hip_fail(e, "lm_head launch");
+    return LL_OK;
+}
+
 ll_status llama_layer_forward_varlen(const ll_layer_cfg* cfg, const ll_layer_weights* w, const void* hidden,
                                      const int64_t* position_ids, const int32_t* cu_seqlens, int64_t n_seqs,
                                      int64_t max_seqlen, int64_t total_tokens, int64_t kv_seq_len, void* out,

@@ -80,6 +80,9 @@ struct RopeEpi {
 // ---- launchers (host) ----
 hipError_t launch_rmsnorm(int dtype, const void* x, const void* g, void* y, int64_t rows, int64_t H, float eps,
                           hipStream_t st);
+// out[r, :] = table[clamp(tokens[r], 0, vocab-1), :] for r < rows
+hipError_t launch_embedding(int dtype, const void* table, const int64_t* tokens, void* out, int64_t rows, int64_t H,
+                            int64_t vocab, hipStream_t st);
 hipError_t launch_rope_apply(int dtype, void* qkv, const int64_t* pos, RopeTab tab, int64_t tokens, int nh, int nkv,
                              int d, int interleaved, hipStream_t st);
 // C[M, ldc] (epi) = X[M, K] . W^T; W has N rows (EPI_SILU: 2*inter rows, N = inter output columns).

@@ -5,6 +5,9 @@
 // reduces across the wave with shuffles and across the 4 waves through LDS, then writes
 // x * rsqrt(mean + eps) * g rounded once. HBM-bound: 2 * H * sizeof(T) bytes per row plus the gain.
 //
+// Token embedding (CSDN answer "#### 5." tok_embeddings(tokens), nn.Embedding): one row per workgroup,
+// copied from the table with 16-byte vectors; ids outside [0, vocab) are clamped (no out-of-bounds read).
+//
 // RoPE apply (verl "parallel_attention.py" §1 rotary_emb/apply_rotary_pos_emb; NJU lecture 5
 // "RoPE高效实现" rotate_half): one lane per (token, head, pair), in place on packed qkv, reading
 // (cos, sin) from the fp32 table built from fp64 angles.
@@ -173,6 +176,47 @@ hipError_t launch_rope_apply(int dtype, void* qkv, const int64_t* pos, RopeTab t
     else
         hipLaunchKernelGGL(rope_apply_kernel<float>, dim3(blocks), dim3(256), 0, st, static_cast<float*>(qkv), pos,
                            tab.cs, tab.rows, tokens, nh, nkv, d, interleaved);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ token embedding
+__global__ __launch_bounds__(256) void embedding_vec_kernel(const uint4* __restrict__ table,
+                                                            const int64_t* __restrict__ tokens,
+                                                            uint4* __restrict__ out, int64_t vecs_per_row,
+                                                            int64_t vocab) {
+    const int64_t row = blockIdx.x;
+    int64_t id = tokens[row];
+    id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+    const uint4* src = table + id * vecs_per_row;
+    uint4* dst = out + row * vecs_per_row;
+    for (int64_t i = threadIdx.x; i < vecs_per_row; i += 256) dst[i] = src[i];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void embedding_scalar_kernel(const T* __restrict__ table,
+                                                               const int64_t* __restrict__ tokens,
+                                                               T* __restrict__ out, int64_t H, int64_t vocab) {
+    const int64_t row = blockIdx.x;
+    int64_t id = tokens[row];
+    id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+    for (int64_t i = threadIdx.x; i < H; i += 256) out[row * H + i] = table[id * H + i];
+}
+
+hipError_t launch_embedding(int dtype, const void* table, const int64_t* tokens, void* out, int64_t rows, int64_t H,
+                            int64_t vocab, hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    const int64_t row_bytes = H * (dtype == LL_BF16 ? 2 : 4);
+    const bool vec = row_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(table) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+    if (vec)
+        hipLaunchKernelGGL(embedding_vec_kernel, dim3(static_cast<unsigned>(rows)), dim3(256), 0, st,
+                           static_cast<const uint4*>(table), tokens, static_cast<uint4*>(out), row_bytes / 16, vocab);
+    else if (dtype == LL_BF16)
+        hipLaunchKernelGGL(embedding_scalar_kernel<bf16_t>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, st,
+                           static_cast<const bf16_t*>(table), tokens, static_cast<bf16_t*>(out), H, vocab);
+    else
+        hipLaunchKernelGGL(embedding_scalar_kernel<float>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, st,
+                           static_cast<const float*>(table), tokens, static_cast<float*>(out), H, vocab);
     return hipGetLastError();
 }
 
