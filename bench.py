@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=[WORKLOAD, "llama32_1b_prefill", "llama3_8b_long_llama3rope", "llama3_8b_decode",
-                             CHUNK_WORKLOAD, VARLEN_WORKLOAD],
+                             CHUNK_WORKLOAD, VARLEN_WORKLOAD, MODEL_WORKLOAD],
                     help="the headline line is the 8B prefill; the others print the same record for that workload")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the cache-cold decode measurement that the headline run adds as \"decode\"")
@@ -290,6 +290,91 @@ def run_varlen(L, torch, np, cfg, W, args, lens):
     return wall * 1e3 / args.steps, stages
 
 
+MODEL_WORKLOAD = "llama32_1b_model"
+MODEL_LAYERS, MODEL_VOCAB = 16, 128256
+
+
+def run_model(L, torch, np, cfg, args):
+    """The Llama-3.2-1B-shaped stack (16 decoder layers, 128256-token vocabulary, the layer dump on the
+    NJU lecture page) over B x S token ids. Weights come from torch's seeded device generator (N(0,0.02)
+    projections, 1+N(0,0.1) gains, N(0,1) embeddings; their values do not change the work); token ids
+    integer-uniform on the vocabulary. Returns (ms_per_step, stages)."""
+    dev = "cuda:0"
+    g = torch.Generator(device=dev)
+
+    def draw(shape, std, mean, seed):
+        g.manual_seed(seed)
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std + mean).to(torch.bfloat16)
+
+    H, I = cfg.hidden, cfg.intermediate
+    layers = []
+    for l in range(MODEL_LAYERS):
+        s = 1000 + 10 * l
+        layers.append({"w_qkv": draw((cfg.qkv_dim, H), 0.02, 0.0, s), "w_o": draw((H, cfg.n_heads * cfg.head_dim), 0.02, 0.0, s + 1),
+                       "w_gate_up": draw((2 * I, H), 0.02, 0.0, s + 2), "w_down": draw((H, I), 0.02, 0.0, s + 3),
+                       "g_attn": draw((H,), 0.1, 1.0, s + 4), "g_mlp": draw((H,), 0.1, 1.0, s + 5)})
+    model = {"layers": layers, "tok_embeddings": draw((MODEL_VOCAB, H), 1.0, 0.0, 1), "g_final": draw((H,), 0.1, 1.0, 2),
+             "lm_head": draw((MODEL_VOCAB, H), 0.02, 0.0, 3)}
+    g.manual_seed(4)
+    tok = torch.randint(0, MODEL_VOCAB, (cfg.B, cfg.S), generator=g, device=dev, dtype=torch.int64)
+    pos = torch.arange(cfg.S, device=dev, dtype=torch.int64).expand(cfg.B, cfg.S).contiguous()
+    lc = lib_config(L, cfg, torch)
+    logits = torch.empty((cfg.B, cfg.S, MODEL_VOCAB), device=dev, dtype=torch.bfloat16)
+    import ctypes
+    c = lc.to_c()
+    ws = torch.empty(L.load().llama_model_workspace_bytes(ctypes.byref(c), MODEL_VOCAB, cfg.B, cfg.S),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        L.llama_model_forward(lc, model, tok, pos, out=logits, workspace=ws)
+    torch.cuda.synchronize()
+    L.profile_begin(args.steps * MODEL_LAYERS)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        L.llama_model_forward(lc, model, tok, pos, out=logits, workspace=ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = L.profile_end()
+    assert torch.isfinite(logits[:, -1].float()).all().item()
+    return wall * 1e3 / args.steps, stages
+
+
+def run_model_record(args):
+    import torch
+
+    import transformer_layer_forward_amd as L
+    from synth_inputs import CONFIGS
+    torch.cuda.set_device(0)
+    cfg = CONFIGS["llama32_1b_prefill"]
+    ms, stages = run_model(L, torch, None, cfg, args)
+    per_layer = {k: v[0] / v[1] for k, v in stages.items()}
+    layers_ms = MODEL_LAYERS * sum(per_layer.values())
+    M, H, I, d = cfg.M, cfg.hidden, cfg.intermediate, cfg.head_dim
+    gate_up_ms = per_layer["gate_up_silu"]
+    achieved = 2.0 * M * (2 * I) * H / (gate_up_ms / 1e3) / 1e12
+    flops = (MODEL_LAYERS * (gemm_flops_per_token(cfg) * M + 4.0 * cfg.B * cfg.n_heads * d * cfg.S * (cfg.S + 1) / 2)
+             + 2.0 * M * MODEL_VOCAB * H)
+    rec = {
+        "metric": f"model tokens/s (Llama-3.2-1B-shaped stack: embeddings, {MODEL_LAYERS} decoder layers, final "
+                  f"RMSNorm, {H}->{MODEL_VOCAB} output projection; bf16 prefill)",
+        "value": round(M / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "ms_per_step": round(ms, 4),
+        "data": "synthetic (weights and token ids from torch's seeded device generator)",
+        "config": {"workload": f"Llama-3.2-1B-shaped model stack, {MODEL_LAYERS} layers, vocab {MODEL_VOCAB}",
+                   "B": cfg.B, "S": cfg.S, "hidden": H, "n_heads": cfg.n_heads, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": d, "intermediate": I, "layers": MODEL_LAYERS, "vocab": MODEL_VOCAB},
+        "model_tflops": round(flops / (ms / 1e3) / 1e12, 1),
+        "layers_ms": round(layers_ms, 4),
+        "embedding_norm_head_ms": round(ms - layers_ms, 4),
+        "per_layer_stages_ms": {k: round(v, 4) for k, v in per_layer.items()},
+        "roofline": {"kernel": "gemm_bf16_mfma32_kernel<EPI_SILU> (fused gate_up + silu*up), per layer",
+                     "bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_BF16_DENSE_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def decode_inputs(L, torch, np, cfg, W):
     """Decode step inputs on the device: hidden [B,1,H], positions [B] integer-uniform on [1024, ctx),
     and K/V caches [B, ctx, n_kv, d] of N(0,1) values drawn by torch's seeded device generator (the
@@ -400,6 +485,9 @@ def main():
     import transformer_layer_forward_amd as L
     from synth_inputs import CONFIGS, make_weights
 
+    if args.workload == MODEL_WORKLOAD:
+        run_model_record(args)
+        return
     chunk = args.workload == CHUNK_WORKLOAD
     varlen = args.workload == VARLEN_WORKLOAD
     lens = None
