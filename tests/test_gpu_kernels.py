@@ -82,7 +82,8 @@ def test_rope_apply(rc, il, dtype, d):
 # ------------------------------------------------------------------ projections (via the MLP entry point)
 @pytest.mark.parametrize("dtype,M,H,I", [("bf16", 1, 256, 512), ("bf16", 37, 512, 1000), ("bf16", 64, 256, 384),
                                          ("bf16", 48, 1288, 2056), ("bf16", 65, 256, 384), ("bf16", 300, 1024, 2048),
-                                         ("bf16", 515, 512, 1032), ("f32", 32, 64, 176), ("f32", 45, 96, 200)])
+                                         ("bf16", 515, 512, 1032), ("bf16", 20, 200, 1000), ("bf16", 33, 520, 240),
+                                         ("f32", 32, 64, 176), ("f32", 45, 96, 200)])
 @pytest.mark.parametrize("with_residual", [False, True])
 def test_swiglu_mlp(dtype, M, H, I, with_residual):
     require_gpu()

@@ -554,102 +554,156 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
 }
 #undef MF_WAITVM0
 
-// ------------------------------------------------------------------ bf16, small M (split-K)
-// With M <= 64 tokens the product is bound by streaming W from HBM once. A workgroup of 8 waves
-// owns 128*FR weight rows and one 1024-wide K chunk. The 64 x 1024 activation chunk is staged in
-// LDS once (rows >= M and columns >= K are zero; 16-byte chunks XOR-swizzled by row so the 16 rows
-// of a B fragment read distinct banks); each wave then streams its own 16*FR weight rows through
-// a ring of SK_U 32-wide k steps of loads in flight and feeds the matrix cores with W as the A
-// operand. Chunk partials go to workspace; a reduce kernel sums them and applies the epilogue.
-constexpr int SK_MAXM = 64, SK_KC = 1024, SK_THREADS = 512, SK_U = 8;
-constexpr int SK_CPR = SK_KC / 8;                 // 16-byte chunks per staged activation row
-constexpr int SK_LDS_BYTES = 64 * SK_KC * 2;
+// ------------------------------------------------------------------ bf16, small M (decode)
+// With M <= 64 tokens a projection is bound by streaming W from HBM once. A workgroup of 8 waves
+// owns 128 weight rows (16 per wave; gate_up: 64 gate rows and the 64 matching up rows) over one K
+// range; its waves walk that range together in 256-wide sub-chunks. The 64 x 256 activation
+// sub-chunk sits in LDS (rows >= M and columns past the range are zero; 16-byte chunks XOR-swizzled
+// by row so the 16 rows of a B fragment read distinct banks), double-buffered and staged through
+// registers one sub-chunk ahead; each wave streams its 16 weight rows through a ring of SK_U 32-wide
+// k steps of loads in flight, straight into matrix-core A operands. The K ranges are sized so the
+// grid is about one workgroup per compute unit. With a single range the epilogue runs in the kernel
+// (gate_up: the up waves hand their sums to the gate waves through LDS); otherwise fp32 range
+// partials go to workspace and a reduce kernel sums them and applies the epilogue.
+constexpr int SK_MAXM = 64, SK_SC = 256, SK_WAVES = 8, SK_THREADS = 64 * SK_WAVES, SK_U = 4;
+constexpr int SK_CPR = SK_SC / 8;                  // 16-byte chunks per staged activation row (32)
+constexpr int SK_XPT = 64 * SK_CPR / SK_THREADS;   // chunks of one sub-chunk staged per lane (4)
+constexpr int SK_STEPS = SK_SC / 32;               // k steps per sub-chunk (8)
+constexpr int SK_WG_TARGET = 256;                  // workgroups aimed for (one per compute unit)
+static_assert(SK_XPT * SK_THREADS == 64 * SK_CPR && SK_STEPS % SK_U == 0, "skinny tiling");
 
-// The k steps of one chunk. TAIL: the chunk ends before SK_KC (k offsets are clamped to the last
-// valid 8-column group, whose re-read weights meet zero activations).
-template <int FR, bool TAIL>
-__device__ __forceinline__ void skinny_steps(uint4* __restrict__ sX, const bf16_t* __restrict__ X, int M, int K,
-                                             int k0, int kvalid, int tid, const bf16_t* const* wrow, int kofs0,
-                                             int kmax, int lrow, int lgrp, f32x4 (&acc)[FR][4]) {
-    constexpr int KS = SK_KC / 32;
-    auto kof = [&](int step) { const int k = kofs0 + 32 * step; return TAIL ? min(k, kmax) : k; };
-    // first SK_U steps of weights in flight before the activation chunk is staged
-    uint4 wr[SK_U][FR];
-#pragma unroll
-    for (int u = 0; u < SK_U; ++u)
-#pragma unroll
-        for (int f = 0; f < FR; ++f) wr[u][f] = *reinterpret_cast<const uint4*>(wrow[f] + kof(u));
-    for (int e = tid; e < 64 * SK_CPR; e += SK_THREADS) {
-        const int m = e / SK_CPR, c = e % SK_CPR;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (m < M && c * 8 < kvalid) v = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(m) * K + k0 + c * 8);
-        sX[m * SK_CPR + (c ^ (m & 15))] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
-        bf16x8 xb[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int m = 16 * b + lrow, c = 4 * st + lgrp;
-            xb[b] = __builtin_bit_cast(bf16x8, sX[m * SK_CPR + (c ^ (m & 15))]);
-        }
-        uint4 cur[FR];
-#pragma unroll
-        for (int f = 0; f < FR; ++f) cur[f] = wr[st % SK_U][f];
-        if (st + SK_U < KS) {
-#pragma unroll
-            for (int f = 0; f < FR; ++f) wr[st % SK_U][f] = *reinterpret_cast<const uint4*>(wrow[f] + kof(st + SK_U));
-        }
-#pragma unroll
-        for (int f = 0; f < FR; ++f)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur[f]), xb[b],
-                                                                    acc[f][b], 0, 0, 0);
-    }
-}
-
-template <int FR>
-__global__ __launch_bounds__(SK_THREADS) void gemm_bf16_skinny_kernel(const bf16_t* __restrict__ X,
-                                                                      const bf16_t* __restrict__ W,
-                                                                      float* __restrict__ P, int M, int Nw, int K,
-                                                                      int nrb) {
-    extern __shared__ uint4 sX[];                 // [64][SK_CPR]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// N = output columns (the weight has 2N rows for gate_up); P = partials [splits][M][Nw] (Nw = 2N
+// for gate_up) when direct == 0.
+template <int EPI>
+__global__ __launch_bounds__(SK_THREADS) void gemm_bf16_skinny_kernel(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, const bf16_t* __restrict__ R,
+    float* __restrict__ P, int M, int N, int K, int nrb, int kw, int direct) {
+    __shared__ uint4 sX[2][64 * SK_CPR];           // 2 x 32 KiB
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 15, lgrp = lane >> 4;
     const int rb = blockIdx.x % nrb, kc = blockIdx.x / nrb;
-    const int k0 = kc * SK_KC;
-    const int kvalid = min(SK_KC, K - k0);        // a multiple of 8
-    const int n0 = rb * (128 * FR) + wave * (16 * FR);
-    const bf16_t* wrow[FR];
+    const int kbeg = kc * kw, kend = min(K, kbeg + kw);
+    const int nsc = (kend - kbeg + SK_SC - 1) / SK_SC;
+    // first output column of this wave's 16-row block, and the weight row of that block's first row
+    int col0, wrow0;
+    if (EPI == EPI_SILU) {
+        col0 = rb * 64 + 16 * (wave & 3);
+        wrow0 = wave < 4 ? 0 : N;                 // gate rows [0, N), up rows [N, 2N)
+    } else {
+        col0 = rb * 128 + 16 * wave;
+        wrow0 = 0;
+    }
+    const bf16_t* wrow = W + static_cast<int64_t>(wrow0 + min(col0 + lrow, N - 1)) * K;
+    const int kmax = K - 8;
+    // k of this lane's 8 weights in global step g; steps past the range (the last sub-chunk of the last
+    // range) re-read columns K-8.. of the row, which meet zero activations
+    auto wk = [&](int g) { return min(kbeg + 32 * g + 8 * lgrp, kmax); };
+    auto xload = [&](int sc, uint4 (&r)[SK_XPT]) {
 #pragma unroll
-    for (int f = 0; f < FR; ++f) wrow[f] = W + static_cast<int64_t>(min(n0 + 16 * f + lrow, Nw - 1)) * K;
-    f32x4 acc[FR][4];
+        for (int i = 0; i < SK_XPT; ++i) {
+            const int e = tid + i * SK_THREADS, m = e / SK_CPR, c = e % SK_CPR;
+            const int k = kbeg + sc * SK_SC + c * 8;
+            r[i] = (m < M && k < kend) ? *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(m) * K + k)
+                                       : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto xstore = [&](int buf, const uint4 (&r)[SK_XPT]) {
 #pragma unroll
-    for (int f = 0; f < FR; ++f)
+        for (int i = 0; i < SK_XPT; ++i) {
+            const int e = tid + i * SK_THREADS, m = e / SK_CPR, c = e % SK_CPR;
+            sX[buf][m * SK_CPR + (c ^ (m & 15))] = r[i];
+        }
+    };
+    const int gsteps = nsc * SK_STEPS;
+    uint4 wr[SK_U];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (kvalid == SK_KC)
-        skinny_steps<FR, false>(sX, X, M, K, k0, kvalid, tid, wrow, k0 + lgrp * 8, K - 8, lrow, lgrp, acc);
-    else
-        skinny_steps<FR, true>(sX, X, M, K, k0, kvalid, tid, wrow, k0 + lgrp * 8, K - 8, lrow, lgrp, acc);
+    for (int u = 0; u < SK_U; ++u) wr[u] = *reinterpret_cast<const uint4*>(wrow + wk(u));
+    uint4 xr[SK_XPT];
+    xload(0, xr);
+    xstore(0, xr);
+    if (nsc > 1) xload(1, xr);
+    __syncthreads();
+    f32x4 acc[4];
 #pragma unroll
-    for (int f = 0; f < FR; ++f)
+    for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sc = 0; sc < nsc; ++sc) {
+        const uint4* sb = sX[sc & 1];
+#pragma unroll
+        for (int st = 0; st < SK_STEPS; ++st) {
+            const int g = sc * SK_STEPS + st;
+            bf16x8 xb[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int m = 16 * b + lrow, c = 4 * st + lgrp;
+                xb[b] = __builtin_bit_cast(bf16x8, sb[m * SK_CPR + (c ^ (m & 15))]);
+            }
+            const bf16x8 cur = __builtin_bit_cast(bf16x8, wr[st % SK_U]);
+            if (g + SK_U < gsteps) wr[st % SK_U] = *reinterpret_cast<const uint4*>(wrow + wk(g + SK_U));
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, xb[b], acc[b], 0, 0, 0);
+        }
+        // the buffer refilled here was last read in sub-chunk sc - 1, which the barrier below it closed
+        if (sc + 1 < nsc) {
+            xstore((sc + 1) & 1, xr);
+            if (sc + 2 < nsc) xload(sc + 2, xr);
+        }
+        __syncthreads();
+    }
+    // lane holds acc[b][r] = sum for token 16b + lrow and output column col0 + 4*lgrp + r
+    const int n = col0 + 4 * lgrp;
+    if (!direct) {
+        const int64_t Nw = EPI == EPI_SILU ? 2 * static_cast<int64_t>(N) : N;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int m = 16 * b + lrow;
-            const int n = n0 + 16 * f + 4 * lgrp;
             if (m >= M) continue;
-            float* prow = P + (static_cast<int64_t>(kc) * M + m) * Nw;
-            if (n + 4 <= Nw) {
-                *reinterpret_cast<f32x4*>(prow + n) = acc[f][b];
+            float* prow = P + (static_cast<int64_t>(kc) * M + m) * Nw + wrow0;
+            if (n + 4 <= N) {
+                *reinterpret_cast<f32x4*>(prow + n) = acc[b];
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (n + r < Nw) prow[n + r] = acc[f][b][r];
+                    if (n + r < N) prow[n + r] = acc[b][r];
             }
         }
+        return;
+    }
+    if (EPI == EPI_SILU) {
+        // the LDS buffers are free after the loop's last barrier: the up waves pass their sums over
+        f32x4* sU = reinterpret_cast<f32x4*>(&sX[0][0]);
+        if (wave >= 4) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) sU[((wave - 4) * 4 + b) * 64 + lane] = acc[b];
+        }
+        __syncthreads();
+        if (wave >= 4) return;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const f32x4 u = sU[(wave * 4 + b) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[b][r] = acc[b][r] / (1.f + __expf(-acc[b][r])) * u[r];
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int m = 16 * b + lrow;
+        if (m >= M) continue;
+        const int64_t o = static_cast<int64_t>(m) * N + n;
+        float v[4] = {acc[b][0], acc[b][1], acc[b][2], acc[b][3]};
+        if (n + 4 <= N) {
+            if (EPI == EPI_RESIDUAL) {
+                const uint2 rr = *reinterpret_cast<const uint2*>(R + o);
+                v[0] += __uint_as_float(rr.x << 16); v[1] += __uint_as_float(rr.x & 0xffff0000u);
+                v[2] += __uint_as_float(rr.y << 16); v[3] += __uint_as_float(rr.y & 0xffff0000u);
+            }
+            *reinterpret_cast<uint2*>(C + o) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n + r < N) C[o + r] = f2bf(EPI == EPI_RESIDUAL ? v[r] + bf2f(R[o + r]) : v[r]);
+        }
+    }
 }
 
 // Sum split partials P[splits][M][Nw] and apply the epilogue; N = output columns.
@@ -742,20 +796,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // ------------------------------------------------------------------ dispatch
 static bool use_skinny(int64_t M) { return M <= SK_MAXM; }
 
-// K chunks of SK_KC; 256-row workgroups (FR = 2) when that still gives ~192 or more workgroups,
-// 128-row ones otherwise.
-static void skinny_plan(int64_t Nw, int64_t K, int* fr, int* splits, int* nrb) {
-    *splits = static_cast<int>((K + SK_KC - 1) / SK_KC);
-    *fr = ((Nw + 255) / 256) * *splits >= 192 ? 2 : 1;
-    *nrb = static_cast<int>((Nw + 128 * *fr - 1) / (128 * *fr));
+// Decode plan: workgroups over 128 output columns (gate_up: 64) times K ranges of a multiple of
+// SK_SC columns, as many ranges as keep the grid near SK_WG_TARGET workgroups. A single range
+// applies the epilogue in the kernel, except RoPE, whose rotation partner lives in another wave.
+struct SkinnyPlan {
+    int nrb, splits, kw;
+    bool direct;
+};
+
+static SkinnyPlan skinny_plan(int epi, int64_t N, int64_t K) {
+    SkinnyPlan p;
+    p.nrb = static_cast<int>(epi == EPI_SILU ? (N + 63) / 64 : (N + 127) / 128);
+    const int64_t want = std::max<int64_t>(1, SK_WG_TARGET / p.nrb);
+    p.kw = static_cast<int>(((K + want - 1) / want + SK_SC - 1) / SK_SC * SK_SC);
+    p.splits = static_cast<int>((K + p.kw - 1) / p.kw);
+    p.direct = p.splits == 1 && epi != EPI_ROPE;
+    return p;
 }
 
 size_t gemm_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K, int epi) {
     if (dtype != LL_BF16 || !use_skinny(M)) return 0;
+    const SkinnyPlan p = skinny_plan(epi, N, K);
+    if (p.direct) return 0;
     const int64_t Nw = epi == EPI_SILU ? 2 * N : N;
-    int fr, splits, nrb;
-    skinny_plan(Nw, K, &fr, &splits, &nrb);
-    return static_cast<size_t>(splits) * M * Nw * sizeof(float);
+    return static_cast<size_t>(p.splits) * M * Nw * sizeof(float);
 }
 
 template <int EPI, bool DIRECT, int RD>
@@ -801,33 +865,21 @@ static hipError_t mfma32_launch(const void* X, const void* W, void* C, const voi
     return hipGetLastError();
 }
 
-template <int FR>
-static hipError_t skinny_gemm_t(const void* X, const void* W, void* P, int64_t M, int64_t Nw, int64_t K, int nrb,
-                                int splits, hipStream_t st) {
-    static bool attr = [] {
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_skinny_kernel<FR>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, SK_LDS_BYTES) == hipSuccess;
-    }();
-    if (!attr) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(gemm_bf16_skinny_kernel<FR>, dim3(static_cast<unsigned>(nrb) * splits), dim3(SK_THREADS),
-                       SK_LDS_BYTES, st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W),
-                       static_cast<float*>(P), static_cast<int>(M), static_cast<int>(Nw), static_cast<int>(K), nrb);
-    return hipGetLastError();
-}
-
 template <int EPI>
 static hipError_t skinny_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N, int64_t K,
                                 void* ws, hipStream_t st, const RopeEpi* re = nullptr) {
+    const SkinnyPlan p = skinny_plan(EPI, N, K);
     const int64_t Nw = EPI == EPI_SILU ? 2 * N : N;
-    int fr, splits, nrb;
-    skinny_plan(Nw, K, &fr, &splits, &nrb);
-    hipError_t e = fr == 2 ? skinny_gemm_t<2>(X, W, ws, M, Nw, K, nrb, splits, st)
-                           : skinny_gemm_t<1>(X, W, ws, M, Nw, K, nrb, splits, st);
-    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_bf16_skinny_kernel<EPI>, dim3(static_cast<unsigned>(p.nrb) * p.splits), dim3(SK_THREADS),
+                       0, st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), static_cast<bf16_t*>(C),
+                       static_cast<const bf16_t*>(R), static_cast<float*>(ws), static_cast<int>(M),
+                       static_cast<int>(N), static_cast<int>(K), p.nrb, p.kw, p.direct ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.direct) return e;
     const int64_t total = M * N;
     hipLaunchKernelGGL(gemm_splitk_reduce_kernel<EPI>, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
                        st, static_cast<const float*>(ws), static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R),
-                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(Nw), splits,
+                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(Nw), p.splits,
                        re ? re->pos : nullptr, re ? re->tab.cs : nullptr, re ? re->tab.rows : 1,
                        re ? re->rope_cols : 0, re ? re->d : 2, re ? re->interleaved : 0);
     return hipGetLastError();
