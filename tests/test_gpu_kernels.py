@@ -197,6 +197,8 @@ DECODE = [
     ("bf16", 3, 1100, 32, 8, 128),
     ("bf16", 12, 1300, 16, 2, 128),  # 8 query heads per kv head; positions at tile and chunk edges
     ("bf16", 12, 900, 4, 2, 64),
+    ("bf16", 48, 2000, 32, 8, 128),  # few key splits per sequence, several 128-key blocks each
+    ("bf16", 64, 1200, 32, 8, 64),
     ("bf16", 2, 300, 4, 2, 96),      # generic kernel
     ("f32", 2, 40, 4, 2, 16),
 ]

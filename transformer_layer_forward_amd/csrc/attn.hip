@@ -917,17 +917,22 @@ __global__ __launch_bounds__(256) void attn_decode_generic_kernel(const T* __res
 }
 
 // ------------------------------------------------------------------ decode, matrix cores
-// Workgroup = (sequence b, kv head c, 512-key chunk), 4 waves. Wave w takes the 32-key tiles
-// w, w+4, w+8, w+12 of the chunk, so in each step the 4 waves stream 128 consecutive cache slots.
-// Every lane loads its K fragments (MFMA A operand: key row l%16, 8 dims) and its V rows (8 dims of
-// one key) for the next tile before it computes the current one, so two tiles of K and V (32 KiB
-// per wave) are in flight while the matrix and vector units work; loads use clamped slot indices
-// and are masked afterwards. No workgroup barrier or memory fence sits inside the key loop.
-constexpr int DEC_CHUNK = 512;   // keys per workgroup
+// Workgroup = (sequence b, kv head c, key split), 4 waves. The sequence's visible slots 0..pos[b] are
+// cut into 128-key blocks and the blocks are shared out evenly among nsplit workgroups, so every
+// workgroup has work in proportion to the sequence's own length (no workgroup scans empty slots).
+// Within a block wave w takes the 32-key tile w. Each lane loads its K fragments (MFMA A operand: key
+// row l%16, 8 dims) and its V row pieces (8 dims of one key) for the next two tiles while it computes
+// the current one; loads use slot indices clamped to the workgroup's last slot. Both products run on
+// the matrix cores: S = K q (columns = the group's query heads, the rest zero), online softmax per head
+// in the log2 domain, then O^T += V^T P^T, where P^T is the lane's own probabilities (the B operand's
+// key order is that of the score accumulator) and V^T comes from the tile's rows written to the wave's
+// own LDS tile (XOR-swizzled) and read back with transposing reads. No workgroup barrier or fence sits
+// inside the key loop: LDS instructions of one wave execute in order.
 constexpr int DEC_TILE = 32;     // keys per wave step
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_THREADS = 64 * DEC_WAVES;
-constexpr int DEC_TPW = DEC_CHUNK / (DEC_TILE * DEC_WAVES);   // tiles per wave
+constexpr int DEC_BLOCK = DEC_TILE * DEC_WAVES;   // keys per workgroup step (128)
+constexpr int DEC_TARGET = 6144;                  // (workgroups x query heads) aimed for per call
 
 template <int D>
 struct DecTile {
@@ -957,118 +962,52 @@ __device__ __forceinline__ void dec_load(DecTile<D>& t, const bf16_t* __restrict
     }
 }
 
-// One 32-key tile: S = K q (matrix cores; column = query head, only the first G are real),
-// online softmax per head in the log2 domain, then o[h][8 dims] += p V on the vector ALUs.
-// P goes through this wave's private LDS rows; LDS instructions of one wave execute in order, so
-// the exchange needs only a compiler barrier.
-template <int D, int G>
-__device__ __forceinline__ void dec_compute(const DecTile<D>& t, const bf16x8* qfr, int64_t t0, int64_t L,
-                                            float scale_log2, float& m_w, float& l_w, float (&o)[G][8],
-                                            float (*sPw)[G], int lrow, int lgrp, int dch, int ksub) {
-    using TT = DecTile<D>;
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int k = 0; k < TT::KC32; ++k)
-#pragma unroll
-        for (int kf = 0; kf < 2; ++kf)
-            sacc[kf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[kf][k]), qfr[k],
-                                                                sacc[kf], 0, 0, 0);
-    float s[2][4], mx = -INFINITY;
-#pragma unroll
-    for (int kf = 0; kf < 2; ++kf)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t key = t0 + kf * 16 + 4 * lgrp + r;
-            const float v = key < L ? sacc[kf][r] * scale_log2 : -INFINITY;
-            s[kf][r] = v;
-            mx = fmaxf(mx, v);
-        }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(m_w, mx);
-    const float alpha = fast_exp2(m_w - mnew);
-    m_w = mnew;
-    float ls = 0.f;
-#pragma unroll
-    for (int kf = 0; kf < 2; ++kf)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float pr = fast_exp2(s[kf][r] - mnew);
-            ls += pr;
-            if (lrow < G) sPw[kf * 16 + 4 * lgrp + r][lrow] = pr;
-        }
-    l_w = l_w * alpha + ls;
-    // alpha of head h is the same in every lane of column h: move it to scalar registers
-    float al[G];
-    bool rescale = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        al[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
-        rescale |= al[h] != 1.f;
-    }
-    if (rescale) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[h][e] *= al[h];
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-#pragma unroll
-    for (int it = 0; it < TT::PV_IT; ++it) {
-        const int kr = it * TT::KPI + ksub;
-        float pv[G];
-        if constexpr (G % 4 == 0) {
-#pragma unroll
-            for (int h = 0; h < G; h += 4) {
-                const float4 q4 = *reinterpret_cast<const float4*>(&sPw[kr][h]);
-                pv[h] = q4.x; pv[h + 1] = q4.y; pv[h + 2] = q4.z; pv[h + 3] = q4.w;
-            }
-        } else {
-#pragma unroll
-            for (int h = 0; h < G; ++h) pv[h] = sPw[kr][h];
-        }
-        float vf[8];
-        unpack8(t.v[it], vf);
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[h][e] += pv[h] * vf[e];
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+// number of key splits per (sequence, kv head) for a call: enough workgroups to fill the chip, at most
+// one per 128-key block of the cache
+static int dec_nsplit(int64_t B, int64_t nh, int64_t ctx) {
+    const int64_t want = (DEC_TARGET + B * nh - 1) / (B * nh > 0 ? B * nh : 1);
+    const int64_t cap = (ctx + DEC_BLOCK - 1) / DEC_BLOCK;
+    return static_cast<int>(std::max<int64_t>(1, std::min(want, cap)));
 }
 
-// partial record per (b, h, chunk): [0] = max (log2 domain), [1] = sum, [2..2+d) = unnormalised o
+// blocks [j0, j1) of split s among nsplit over nblk blocks; empty when j0 == j1
+__device__ __forceinline__ int dec_split_begin(int s, int nblk, int nsplit) {
+    return static_cast<int>(static_cast<int64_t>(s) * nblk / nsplit);
+}
+
+// partial record per (b, h, split): [0] = max (log2 domain), [1] = sum, [2..2+d) = unnormalised o
 template <int D, int G, bool ROPE, bool IL>
 __global__ __launch_bounds__(DEC_THREADS) void attn_decode_split_kernel(
     const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, const float2* __restrict__ cs, int64_t rope_rows,
-    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, int64_t ctx, float* __restrict__ part, int nchunks,
+    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, int64_t ctx, float* __restrict__ part, int nsplit,
     int nh, int nkv, float scale_log2) {
     using TT = DecTile<D>;
-    __shared__ __align__(16) float sP[DEC_WAVES][DEC_TILE][G];
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    constexpr int DF = D / 16;                     // 16-dim blocks of the output
+    __shared__ __align__(16) bf16_t sV[DEC_WAVES][DEC_TILE * D];
     __shared__ float sM[DEC_WAVES][G], sL[DEC_WAVES][G];
     __shared__ float sO[DEC_WAVES][G][D];
 
-    // the kv heads of one (b, chunk) are adjacent block ids: they read adjacent 256-byte pieces of
-    // the same cache rows
+    // the kv heads of one (b, split) are adjacent block ids: they read adjacent pieces of the same rows
     const int blk = blockIdx.x;
     const int c = blk % nkv;
-    const int chunk = (blk / nkv) % nchunks;
-    const int b = blk / (nkv * nchunks);
+    const int split = (blk / nkv) % nsplit;
+    const int b = blk / (nkv * nsplit);
     const int64_t L = clamp_pos(pos[b], ctx) + 1;
-    const int64_t k0 = static_cast<int64_t>(chunk) * DEC_CHUNK;
-    if (k0 >= L) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nblk = static_cast<int>((L + DEC_BLOCK - 1) / DEC_BLOCK);
+    const int j0 = dec_split_begin(split, nblk, nsplit), j1 = dec_split_begin(split + 1, nblk, nsplit);
+    if (j0 >= j1) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 15, lgrp = lane >> 4;
     const int dch = lane % TT::DL, ksub = lane / TT::DL;
     const int64_t kstride = static_cast<int64_t>(nkv) * D;
     const bf16_t* kb = kc + (static_cast<int64_t>(b) * ctx * nkv + c) * D;
     const bf16_t* vb = vc + (static_cast<int64_t>(b) * ctx * nkv + c) * D;
-    const int64_t last = L - 1;
-    const int64_t base = k0 + static_cast<int64_t>(wave) * DEC_TILE;
-    constexpr int64_t STEP = static_cast<int64_t>(DEC_WAVES) * DEC_TILE;
+    const int64_t lastw = std::min<int64_t>(L, static_cast<int64_t>(j1) * DEC_BLOCK) - 1;
+    const int64_t base = static_cast<int64_t>(j0) * DEC_BLOCK + wave * DEC_TILE;
 
     // B operand of S = K q: column lrow = query head c*G + lrow (zero for lrow >= G), k = dims.
-    // Loaded before the first K/V tile and without branches, so no wait on it holds back the tiles.
     bf16x8 qfr[TT::KC32];
     {
         const int64_t rs = static_cast<int64_t>(nh + 2 * nkv) * D;
@@ -1096,50 +1035,105 @@ __global__ __launch_bounds__(DEC_THREADS) void attn_decode_split_kernel(
         }
     }
 
-    // two tiles in flight from the start; tile loads are unconditional (slot indices are clamped to
-    // the last valid slot), only the compute of a tile past the end is skipped
-    DecTile<D> ta, tb;
-    dec_load<D>(ta, kb, vb, kstride, base, last, lrow, lgrp, dch, ksub);
-    dec_load<D>(tb, kb, vb, kstride, base + STEP, last, lrow, lgrp, dch, ksub);
-
     float m_w = -INFINITY, l_w = 0.f;   // per lane: stats of head column lrow
-    float o[G][8];
+    f32x4 oacc[DF];                     // O^T: dims 16a + 4*lgrp + r, head column lrow
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+    for (int a = 0; a < DF; ++a) oacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16_t* sVw = sV[wave];
 
+    auto compute = [&](const DecTile<D>& t, int64_t t0) {
+        // the tile's V rows into the wave's LDS tile; the previous tile's transposing reads were
+        // consumed by its matrix ops, and one wave's LDS instructions execute in order
 #pragma unroll
-    for (int i = 0; i < DEC_TPW; i += 2) {
-        const int64_t t0 = base + i * STEP, t1 = t0 + STEP;
-        if (t0 < L) dec_compute<D, G>(ta, qfr, t0, L, scale_log2, m_w, l_w, o, sP[wave], lrow, lgrp, dch, ksub);
-        if (i + 2 < DEC_TPW) dec_load<D>(ta, kb, vb, kstride, t0 + 2 * STEP, last, lrow, lgrp, dch, ksub);
-        if (t1 < L) dec_compute<D, G>(tb, qfr, t1, L, scale_log2, m_w, l_w, o, sP[wave], lrow, lgrp, dch, ksub);
-        if (i + 3 < DEC_TPW) dec_load<D>(tb, kb, vb, kstride, t0 + 3 * STEP, last, lrow, lgrp, dch, ksub);
+        for (int it = 0; it < TT::PV_IT; ++it) {
+            const int r = it * TT::KPI + ksub;
+            *reinterpret_cast<uint4*>(&sVw[r * D + vt_phys<D>(r, dch) * 8]) = t.v[it];
+        }
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int k = 0; k < TT::KC32; ++k)
+#pragma unroll
+            for (int kf = 0; kf < 2; ++kf)
+                sacc[kf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[kf][k]), qfr[k],
+                                                                    sacc[kf], 0, 0, 0);
+        // lane holds scores of keys t0 + 16 kf + 4 lgrp + r for head column lrow
+        float s[2][4], mx = -INFINITY;
+#pragma unroll
+        for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t key = t0 + kf * 16 + 4 * lgrp + r;
+                const float v = key < L ? sacc[kf][r] * scale_log2 : -INFINITY;
+                s[kf][r] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = rows_max(mx);
+        const float mnew = fmaxf(m_w, mx);
+        const float alpha = fast_exp2(m_w - mnew);
+        m_w = mnew;
+        float p[2][4], ls = 0.f;
+#pragma unroll
+        for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[kf][r] = fast_exp2(s[kf][r] - mnew);
+                ls += p[kf][r];
+            }
+        l_w = l_w * alpha + ls;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int a = 0; a < DF; ++a) oacc[a] *= alpha;
+        }
+        uint4 pu;
+        pu.x = pack_bf16x2(p[0][0], p[0][1]);
+        pu.y = pack_bf16x2(p[0][2], p[0][3]);
+        pu.z = pack_bf16x2(p[1][0], p[1][1]);
+        pu.w = pack_bf16x2(p[1][2], p[1][3]);
+        const bf16x8 pfr = __builtin_bit_cast(bf16x8, pu);
+        // A operand V^T (dims 16a + lrow, the lane group's 8 keys in the order of pfr) by two
+        // transposing reads of 4 keys each
+#pragma unroll
+        for (int a = 0; a < DF; ++a) {
+            s16x4 h[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r = 16 * u + 4 * lgrp + (lrow >> 2);
+                const int cc = 2 * a + ((lrow & 3) >> 1);
+                h[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
+                    &sVw[r * D + vt_phys<D>(r, cc) * 8 + (lrow & 1) * 4]));
+            }
+            const bf16x8 vfr = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, pfr, oacc[a], 0, 0, 0);
+        }
+    };
+
+    // two tiles in flight; loads are unconditional (slots clamped to the workgroup's last one) so the
+    // waits on them are exact, only the compute of a tile past the end is skipped
+    DecTile<D> ta, tb;
+    dec_load<D>(ta, kb, vb, kstride, base, lastw, lrow, lgrp, dch, ksub);
+    dec_load<D>(tb, kb, vb, kstride, base + DEC_BLOCK, lastw, lrow, lgrp, dch, ksub);
+    const int nt = j1 - j0;
+    for (int i = 0; i < nt; i += 2) {
+        const int64_t t0 = base + static_cast<int64_t>(i) * DEC_BLOCK, t1 = t0 + DEC_BLOCK;
+        if (t0 < L) compute(ta, t0);
+        dec_load<D>(ta, kb, vb, kstride, t0 + 2 * DEC_BLOCK, lastw, lrow, lgrp, dch, ksub);
+        if (i + 1 < nt && t1 < L) compute(tb, t1);
+        dec_load<D>(tb, kb, vb, kstride, t0 + 3 * DEC_BLOCK, lastw, lrow, lgrp, dch, ksub);
     }
 
-    // reduce o over the KPI key groups of the wave, l over the 4 row groups
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int off = TT::DL; off < 64; off <<= 1) o[h][e] += __shfl_xor(o[h][e], off, 64);
-    float lt = l_w;
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = rows_sum(l_w);
     if (lgrp == 0 && lrow < G) {
         sM[wave][lrow] = m_w;      // -inf for a wave that saw no key
         sL[wave][lrow] = lt;
     }
-    if (lane < TT::DL) {
+    if (lrow < G) {
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int a = 0; a < DF; ++a)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sO[wave][h][lane * 8 + e] = o[h][e];
+            for (int r = 0; r < 4; ++r) sO[wave][lrow][16 * a + 4 * lgrp + r] = oacc[a][r];
     }
     __syncthreads();
-    // merge the waves (wave 0 always saw key k0, so M is finite) and write the chunk partial
+    // merge the waves (wave 0 always saw key 128*j0, so M is finite) and write the split's record
     for (int e = tid; e < G * (D + 2); e += DEC_THREADS) {
         const int h = e / (D + 2), k = e % (D + 2);
         float M = -INFINITY;
@@ -1153,33 +1147,35 @@ __global__ __launch_bounds__(DEC_THREADS) void attn_decode_split_kernel(
             else if (k >= 2) v += sO[w][h][k - 2] * sc;
         }
         if (k == 0) v = M;
-        part[((static_cast<int64_t>(b) * nh + c * G + h) * nchunks + chunk) * (D + 2) + k] = v;
+        part[((static_cast<int64_t>(b) * nh + c * G + h) * nsplit + split) * (D + 2) + k] = v;
     }
 }
 
-// One wave per (b, h): log-sum-exp merge of the chunk partials. The chunk loop is unrolled so the
-// partial rows of several chunks are loaded together.
+// One wave per (b, h): log-sum-exp merge of the records of the splits that had keys.
 template <typename T>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(const float* __restrict__ part,
                                                                  const int64_t* __restrict__ pos, int64_t ctx,
-                                                                 T* __restrict__ out, int nh, int d, int nchunks) {
+                                                                 T* __restrict__ out, int nh, int d, int nsplit) {
     const int bh = blockIdx.x, lane = threadIdx.x;
     const int b = bh / nh;
     const int64_t L = clamp_pos(pos[b], ctx) + 1;
-    const int nc = static_cast<int>((L + DEC_CHUNK - 1) / DEC_CHUNK);
+    const int nblk = static_cast<int>((L + DEC_BLOCK - 1) / DEC_BLOCK);
     const int64_t rec = d + 2;
-    const float* pr = part + static_cast<int64_t>(bh) * nchunks * rec;
+    const float* pr = part + static_cast<int64_t>(bh) * nsplit * rec;
+    auto live = [&](int k) { return dec_split_begin(k, nblk, nsplit) < dec_split_begin(k + 1, nblk, nsplit); };
     float M = -INFINITY;
-    for (int k = lane; k < nc; k += 64) M = fmaxf(M, pr[k * rec]);
+    for (int k = lane; k < nsplit; k += 64)
+        if (live(k)) M = fmaxf(M, pr[k * rec]);
     M = wave_max(M);
     float den = 0.f;
-    for (int k = lane; k < nc; k += 64) den += pr[k * rec + 1] * exp2f(pr[k * rec] - M);
+    for (int k = lane; k < nsplit; k += 64)
+        if (live(k)) den += pr[k * rec + 1] * exp2f(pr[k * rec] - M);
     den = wave_sum(den);
     const float inv = 1.f / den;
     for (int dd = lane; dd < d; dd += 64) {
         float num = 0.f;
-#pragma unroll 8
-        for (int k = 0; k < nc; ++k) num += pr[k * rec + 2 + dd] * exp2f(pr[k * rec] - M);
+        for (int k = 0; k < nsplit; ++k)
+            if (live(k)) num += pr[k * rec + 2 + dd] * exp2f(pr[k * rec] - M);
         stf<T>(out + static_cast<int64_t>(bh) * d + dd, num * inv);
     }
 }
@@ -1261,24 +1257,23 @@ hipError_t launch_attn_prefill(int dtype, const void* qkv, const int64_t* pos, c
 }
 
 size_t attn_decode_workspace_bytes(int64_t B, int64_t nh, int64_t d, int64_t ctx) {
-    const int64_t nchunks = (ctx + DEC_CHUNK - 1) / DEC_CHUNK;
-    return static_cast<size_t>(B * nh * nchunks * (d + 2)) * sizeof(float);
+    return static_cast<size_t>(B * nh * dec_nsplit(B, nh, ctx) * (d + 2)) * sizeof(float);
 }
 
 template <int D, int G, bool ROPE, bool IL>
 static hipError_t decode_go(const void* qkv, const int64_t* pos, const RopeTab* tab, const void* kc, const void* vc,
                             int64_t ctx, void* o, int B, int nh, int nkv, void* ws, hipStream_t st) {
-    const int nchunks = static_cast<int>((ctx + DEC_CHUNK - 1) / DEC_CHUNK);
+    const int nsplit = dec_nsplit(B, nh, ctx);
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
-    const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(B) * nchunks * nkv);
+    const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(B) * nsplit * nkv);
     hipLaunchKernelGGL((attn_decode_split_kernel<D, G, ROPE, IL>), dim3(blocks), dim3(DEC_THREADS), 0, st,
                        static_cast<const bf16_t*>(qkv), pos, tab ? tab->cs : nullptr, tab ? tab->rows : 1,
                        static_cast<const bf16_t*>(kc), static_cast<const bf16_t*>(vc), ctx, static_cast<float*>(ws),
-                       nchunks, nh, nkv, scale_log2);
+                       nsplit, nh, nkv, scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_decode_combine_kernel<bf16_t>, dim3(B * nh), dim3(64), 0, st,
-                       static_cast<const float*>(ws), pos, ctx, static_cast<bf16_t*>(o), nh, D, nchunks);
+                       static_cast<const float*>(ws), pos, ctx, static_cast<bf16_t*>(o), nh, D, nsplit);
     return hipGetLastError();
 }
 
