@@ -23,12 +23,13 @@
 // that XCD's L2.
 //
 // Decode (bf16, d in {64, 128}, n_h/n_kv in {1, 2, 4, 8}): an append kernel writes the new key
-// (rotated) and value to slot pos[b]; the split kernel gives each workgroup (b, c, 512-key chunk)
-// 4 waves that step through 32-key tiles with the next tile's K and V already loading. Q K^T uses
-// the matrix cores with K streamed from HBM straight into operand registers (every K element is
-// used once); P V runs on the vector ALUs on V rows as stored, so V is never transposed. Waves
-// merge through LDS; each workgroup writes (max, sum, o) to workspace and a combine kernel merges
-// the chunks with the log-sum-exp rule.
+// (rotated) and value to slot pos[b]; the split kernel cuts each sequence's visible slots into
+// 128-key blocks shared out evenly over a fixed number of workgroups per (b, c), whose 4 waves step
+// through 32-key tiles with the next tiles' K and V already loading into registers. Q K^T uses the
+// matrix cores with K streamed from HBM straight into operand registers (every K element is used
+// once); P V runs on the matrix cores too, P^T straight from the score accumulators and V^T read
+// transposed from a wave-private LDS copy of the tile. Waves merge through LDS; each workgroup writes
+// (max, sum, o) to workspace and a combine kernel merges the splits with the log-sum-exp rule.
 //
 // Generic kernels (fp32, or any even d <= 256): one wave per query, lanes over d, exact two-level
 // online softmax; used for the fp32 configuration and for head sizes the matrix-core kernels
