@@ -26,6 +26,7 @@ MI355X_HBM_GBS = 8000.0
 WORKLOAD = "llama3_8b_prefill"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gate_up_silu_gemm_llama3_8b_prefill_pmc.json")
 GEMM_SRC = os.path.join(ROOT, "transformer_layer_forward_amd", "csrc", "gemm.hip")
+COMMON_H = os.path.join(ROOT, "transformer_layer_forward_amd", "csrc", "common.h")
 
 
 def parse():
@@ -99,7 +100,7 @@ def pmc_summary(fetch_db: str, write_db: str) -> None:
     kib = COPY_BYTES / 1024.0
     f_scale = kib / f_copy if f_copy else None
     w_scale = kib / w_copy if w_copy else None
-    rec = {"gemm_source_sha256_16": gemm_source_hash(), "fetch_kib_per_launch_raw": f_gu,
+    rec = {"kernel_source_sha256_16": gemm_source_hash(), "fetch_kib_per_launch_raw": f_gu,
            "write_kib_per_launch_raw": w_gu, "copy_fetch_kib_raw": f_copy, "copy_write_kib_raw": w_copy,
            "copy_bytes": COPY_BYTES, "fetch_scale": f_scale, "write_scale": w_scale}
     if None not in (f_gu, w_gu, f_scale, w_scale):
@@ -121,7 +122,16 @@ def rocpd_summary(db: str) -> None:
 
 
 def gemm_source_hash() -> str:
-    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the code the gate_up kernel is built from: the 32x32 section of gemm.hip, its launcher and the
+    shared header. Other GEMM paths (decode, fp32) may change without invalidating the counters."""
+    src = open(GEMM_SRC).read()
+    dash = "// " + "-" * 66
+    a = src.index(dash + " bf16, large M, 32x32 matrix ops")
+    b = src.index(dash + " bf16, small M (decode)")
+    la = src.index("static hipError_t mfma32_launch(")
+    lb = src.index("\n}\n", la)
+    text = src[a:b] + src[la:lb] + open(COMMON_H).read()
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def measured_traffic():
@@ -131,7 +141,7 @@ def measured_traffic():
         rec = json.load(open(PMC_SUMMARY))
     except (OSError, ValueError):
         return None
-    if rec.get("gemm_source_sha256_16") != gemm_source_hash():
+    if rec.get("kernel_source_sha256_16") != gemm_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
 

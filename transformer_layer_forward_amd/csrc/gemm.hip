@@ -19,9 +19,9 @@
 // columns, so the gate and up accumulators of one output sit in the same lane and
 // silu(g)*u is formed in registers; the [M, 2I] product is never stored.
 //
-// bf16 path, small M (decode): split-K over many workgroups that stream W straight from HBM into
-// matrix-core operands; fp32 partial sums go to workspace and a second kernel reduces them and
-// applies the epilogue.
+// bf16 path, small M (decode): workgroups stream W straight from HBM into matrix-core operands over
+// K ranges sized to fill the chip; with one range the epilogue runs in the kernel, otherwise fp32
+// partial sums go to workspace and a second kernel reduces them and applies the epilogue.
 //
 // fp32 path: a simple LDS-tiled FMA kernel (no bf16 or reduced-precision step anywhere).
 #include "common.h"
