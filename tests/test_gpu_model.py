@@ -19,6 +19,7 @@ MODEL = [
     (scaled(CONFIGS["tiny_f32"], B=2, S=17), 3, 97),
     (scaled(CONFIGS["llama32_1b_prefill"], B=1, S=100), 2, 1001),     # vocab not a multiple of 8
     (scaled(CONFIGS["llama3_8b_prefill"], B=2, S=70), 2, 512),
+    (scaled(CONFIGS["llama32_1b_prefill"], B=2, S=24), 2, 1001),      # 48 tokens: decode-sized projections
 ]
 
 
@@ -34,7 +35,7 @@ def _f64_model(M, dtype):
             "lm_head": bits_to_f64(M["lm_head"], dtype)}
 
 
-@pytest.mark.parametrize("case", MODEL, ids=lambda c: f"{c[0].name}-L{c[1]}-V{c[2]}")
+@pytest.mark.parametrize("case", MODEL, ids=lambda c: f"{c[0].name}-B{c[0].B}xS{c[0].S}-L{c[1]}-V{c[2]}")
 def test_model_prefill(case):
     require_gpu()
     cfg, n_layers, vocab = case
