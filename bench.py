@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=[WORKLOAD, "llama32_1b_prefill", "llama3_8b_long_llama3rope", "llama3_8b_decode",
-                             CHUNK_WORKLOAD, VARLEN_WORKLOAD, MODEL_WORKLOAD],
+                             CHUNK_WORKLOAD, CHUNK_SMALL_WORKLOAD, VARLEN_WORKLOAD, MODEL_WORKLOAD],
                     help="the headline line is the 8B prefill; the others print the same record for that workload")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the cache-cold decode measurement that the headline run adds as \"decode\"")
@@ -222,18 +222,22 @@ def run_prefill(L, torch, np, cfg, W, args):
 
 
 CHUNK_WORKLOAD = "llama3_8b_chunk"
-CHUNK_START, CHUNK_CTX = 6144, 8192
+CHUNK_SMALL_WORKLOAD = "llama3_8b_chunk_small"
+CHUNK_CTX = 8192
+# workload -> (sequences, new tokens per sequence, cached prefix length)
+CHUNK_SHAPES = {CHUNK_WORKLOAD: (None, 2048, 6144), CHUNK_SMALL_WORKLOAD: (1, 256, 7936)}
 
 
-def run_chunk(L, torch, np, cfg, W, args):
+def run_chunk(L, torch, np, cfg, W, args, start):
     """Chunked prefill on a cache prefix: each sequence's S new tokens sit at positions
-    CHUNK_START .. CHUNK_START + S - 1 of CHUNK_CTX-slot caches whose earlier slots (the prefix) hold
+    start .. start + S - 1 of CHUNK_CTX-slot caches whose earlier slots (the prefix) hold
     N(0,1) values from torch's seeded device generator. Every call rewrites the same slots with the same
-    values, so calls are idempotent. Returns (ms_per_step, stages)."""
+    values, so calls are idempotent. The workspace is sized for the cache length, so attention may split
+    a small chunk's keys over several workgroups. Returns (ms_per_step, stages)."""
     from synth_inputs import make_hidden
     dev = "cuda:0"
     x = torch.from_numpy(np.ascontiguousarray(make_hidden(cfg, seed=0)).view(np.int16)).to(dev).view(torch.bfloat16)
-    pos = (torch.arange(cfg.S, device=dev, dtype=torch.int64) + CHUNK_START).expand(cfg.B, cfg.S).contiguous()
+    pos = (torch.arange(cfg.S, device=dev, dtype=torch.int64) + start).expand(cfg.B, cfg.S).contiguous()
     g = torch.Generator(device=dev)
     shape = (cfg.B, CHUNK_CTX, cfg.n_kv_heads, cfg.head_dim)
     g.manual_seed(8)
@@ -241,7 +245,7 @@ def run_chunk(L, torch, np, cfg, W, args):
     g.manual_seed(9)
     vc = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     lc = lib_config(L, cfg, torch)
-    ws = torch.empty(L.layer_workspace_bytes(lc, cfg.B, cfg.S), dtype=torch.uint8, device=dev)
+    ws = torch.empty(L.layer_workspace_bytes(lc, cfg.B, cfg.S, CHUNK_CTX), dtype=torch.uint8, device=dev)
     out = torch.empty_like(x)
     for _ in range(args.warmup):
         L.llama_layer_forward_chunk(lc, W, x, pos, kc, vc, out=out, workspace=ws)
@@ -498,12 +502,13 @@ def main():
     if args.workload == MODEL_WORKLOAD:
         run_model_record(args)
         return
-    chunk = args.workload == CHUNK_WORKLOAD
+    chunk = args.workload in CHUNK_SHAPES
     varlen = args.workload == VARLEN_WORKLOAD
     lens = None
     if chunk:
         from synth_inputs import scaled
-        cfg = scaled(CONFIGS[WORKLOAD], name=CHUNK_WORKLOAD, S=2048)
+        nb, ns, chunk_start = CHUNK_SHAPES[args.workload]
+        cfg = scaled(CONFIGS[WORKLOAD], name=args.workload, S=ns, **({"B": nb} if nb else {}))
     elif varlen:
         from synth_inputs import scaled
         lens = varlen_lengths(np)
@@ -545,7 +550,7 @@ def main():
         return
 
     if chunk:
-        ms_per_step, stages = run_chunk(L, torch, np, cfg, W, args)
+        ms_per_step, stages = run_chunk(L, torch, np, cfg, W, args, chunk_start)
         x_bits = None
     elif varlen:
         ms_per_step, stages = run_varlen(L, torch, np, cfg, W, args, lens)
@@ -557,7 +562,7 @@ def main():
     M = cfg.M
     gate_up_flops = 2.0 * M * (2 * I) * H
     achieved = gate_up_flops / (stage_ms(stages, "gate_up_silu") / 1e3) / 1e12
-    start = CHUNK_START if chunk else 0
+    start = chunk_start if chunk else 0
     # QK^T and PV over the visible (query, key) pairs: query s sees keys 0 .. start + s
     if varlen:
         attn_flops = 4.0 * cfg.n_heads * d * sum(n * (n + 1) / 2 for n in lens)
@@ -571,8 +576,8 @@ def main():
             "llama32_1b_prefill": "Llama-3.2-1B-shaped decoder layer, bf16 prefill, causal",
             "llama3_8b_long_llama3rope": "Llama-3-8B-shaped decoder layer, bf16 32k prefill, causal, "
                                          "Llama3 RoPE scaling",
-            CHUNK_WORKLOAD: f"Llama-3-8B-shaped decoder layer, bf16 chunked prefill: {cfg.S} new tokens per "
-                            f"sequence on a {CHUNK_START}-token cached prefix ({CHUNK_CTX}-slot KV cache)",
+            **{w: f"Llama-3-8B-shaped decoder layer, bf16 chunked prefill: {cfg.S} new tokens per "
+                  f"sequence on a {start}-token cached prefix ({CHUNK_CTX}-slot KV cache)" for w in CHUNK_SHAPES},
             VARLEN_WORKLOAD: f"Llama-3-8B-shaped decoder layer, bf16 varlen packed prefill: {len(lens or [])} "
                              f"sequences of 64-2048 tokens packed into {cfg.S} tokens, causal within each"
             }[args.workload]
@@ -587,7 +592,7 @@ def main():
         "data": ("synthetic (seeded N(0,1) hidden" + (" and cache prefix" if chunk else "")
                  + ", N(0,0.02) weights, 1+N(0,0.1) gains)"),
         "config": {"workload": name, "B": cfg.B, "S": cfg.S, **shape, "tokens_per_step": tokens,
-                   **({"prefix": CHUNK_START, "ctx": CHUNK_CTX} if chunk else {}),
+                   **({"prefix": start, "ctx": CHUNK_CTX} if chunk else {}),
                    **({"seq_lens": lens} if varlen else {})},
         "attention_mfma_util_pct": round(100.0 * attn_flops / (stage_ms(stages, "attention") / 1e3) / 1e12
                                          / MI355X_BF16_DENSE_TFLOPS, 2),

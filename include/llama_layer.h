@@ -193,11 +193,17 @@ ll_status gqa_attn_prefill(const void* qkv, const ll_rope* rope, const int64_t* 
  *   o[b, s, h*d:(h+1)*d] = sum_{j <= p} softmax_j(q_{b,s,h} . k_cache[b,j,c] / sqrt(d)) v_cache[b,j,c].
  * qkv packed [B, S, (n_heads + 2 n_kv_heads) d] with q and k already rotated, read only;
  * position_ids [B, S] int64, distinct per sequence, in [0, ctx); k_cache, v_cache [B, ctx, n_kv_heads, d]
- * (required; slots outside this chunk are read as stored); o [B, S, n_heads d]. */
+ * (required; slots outside this chunk are read as stored); o [B, S, n_heads d].
+ * workspace: device scratch owned by the caller, or NULL. With at least
+ * gqa_attn_prefill_chunk_workspace_bytes bytes a small chunk shares each query block's keys out over
+ * several workgroups (partial softmax records merged by a combine pass); with less, or NULL, every query
+ * block is one workgroup (same results up to fp32 rounding order, slower for small chunks). */
+size_t gqa_attn_prefill_chunk_workspace_bytes(int64_t B, int64_t S, int64_t n_heads, int64_t n_kv_heads,
+                                              int64_t head_dim, int64_t ctx, int32_t dtype);
 ll_status gqa_attn_prefill_chunk(const void* qkv, const int64_t* position_ids, void* o,
                                  void* k_cache, void* v_cache, int64_t ctx,
                                  int64_t B, int64_t S, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
-                                 int32_t dtype, void* stream);
+                                 int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Padding-free causal attention over packed sequences (parallel_attention.py §3: flash_attn_varlen_func
  * with cu_seqlens_q = cu_seqlens_k = cu_seqlens, max_seqlen, causal=True):

@@ -252,6 +252,9 @@ CHUNK = [
     ("bf16", 1, 200, 16, 2, 128, 1300, (1000,), "up"),        # long prefix, g = 8
     ("bf16", 1, 257, 6, 2, 64, 400, (33,), "up"),             # g = 3 (one head per block)
     ("bf16", 1, 100, 8, 2, 128, 200, (60,), "down"),          # positions in reverse order
+    ("bf16", 1, 64, 8, 2, 128, 2048, (500,), "up"),           # keys split over 16 workgroups, some of
+    ("bf16", 1, 64, 8, 2, 128, 2048, (500,), "down"),         # them wholly masked for early queries
+    ("bf16", 2, 40, 16, 2, 64, 1024, (700, 33), "up"),        # split keys at d = 64, g = 8
     ("bf16", 1, 50, 4, 2, 96, 120, (20,), "up"),              # generic kernel (d = 96)
     ("f32", 2, 20, 4, 2, 16, 48, (3, 11), "up"),
 ]
@@ -279,6 +282,25 @@ def test_attn_prefill_chunk(case):
     assert ref.max_rel_err(got, want) <= tol(dtype)
     np.testing.assert_array_equal(to_f64(tk), WK)
     np.testing.assert_array_equal(to_f64(tv), WV)
+
+
+def test_attn_prefill_chunk_split_matches_unsplit():
+    """A small chunk on a long prefix with its keys shared out over workgroups (partial records merged
+    by the combine pass) agrees with one workgroup per query block, to bf16 rounding."""
+    require_gpu()
+    B, S, nh, nkv, d, ctx, P = 1, 96, 32, 8, 128, 4096, 3900
+    lib = L._lib.load()
+    assert lib.gqa_attn_prefill_chunk_workspace_bytes(B, S, nh, nkv, d, ctx, 1) > 0   # the split path is taken
+    qkv = to_dev(normal(9, 154, (B, S, (nh + 2 * nkv) * d), "bf16"), "bf16")
+    kc = to_dev(normal(9, 155, (B, ctx, nkv, d), "bf16"), "bf16")
+    vc = to_dev(normal(9, 156, (B, ctx, nkv, d), "bf16"), "bf16")
+    pos = torch.arange(P, P + S, device=DEV, dtype=torch.int64).expand(B, S).contiguous()
+    k2, v2 = kc.clone(), vc.clone()
+    o1 = L.gqa_attn_prefill_chunk(qkv, pos, kc, vc, nh, nkv, d, split_keys=True)
+    o2 = L.gqa_attn_prefill_chunk(qkv, pos, k2, v2, nh, nkv, d, split_keys=False)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, k2) and torch.equal(vc, v2)
+    assert ref.max_rel_err(to_f64(o1), to_f64(o2)) <= 1e-2
 
 
 def test_attn_prefill_chunk_empty_prefix_equals_prefill():

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "LL_OK", 1: "LL_EINVAL", 2: "LL_EUNSUPPORTED", 3: "LL_EHIP", 
 EXPORTED = (
     "llama_layer_workspace_bytes", "llama_layer_forward", "llama_layer_forward_chunk", "llama_layer_forward_varlen",
     "llama_model_workspace_bytes", "llama_model_forward",
-    "rmsnorm", "rope_apply", "gqa_attn_prefill", "gqa_attn_prefill_chunk", "gqa_attn_prefill_varlen",
+    "rmsnorm", "rope_apply", "gqa_attn_prefill", "gqa_attn_prefill_chunk_workspace_bytes", "gqa_attn_prefill_chunk",
+    "gqa_attn_prefill_varlen",
     "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "swiglu_mlp_workspace_bytes", "swiglu_mlp",
     "ll_last_error", "ll_release_caches", "ll_profile_begin", "ll_profile_end", "ll_profile_stage_name",
     "ll_version",
@@ -118,8 +119,9 @@ def load() -> ctypes.CDLL:
                                c_vp]),
         "gqa_attn_prefill": (c_i32, [c_vp, ctypes.POINTER(LLRope), c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
                                      c_i64, c_i64, c_i64, c_i32, c_vp]),
+        "gqa_attn_prefill_chunk_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i32]),
         "gqa_attn_prefill_chunk": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64,
-                                           c_i32, c_vp]),
+                                           c_i32, c_vp, c_sz, c_vp]),
         "gqa_attn_prefill_varlen": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp]),
         "gqa_attn_decode_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i64]),
         "gqa_attn_decode": (c_i32, [c_vp, ctypes.POINTER(LLRope), c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64,
@@ -220,15 +222,24 @@ def gqa_attn_prefill(qkv: torch.Tensor, position_ids: Optional[torch.Tensor], n_
 
 def gqa_attn_prefill_chunk(qkv: torch.Tensor, position_ids: torch.Tensor, k_cache: torch.Tensor,
                            v_cache: torch.Tensor, n_heads: int, n_kv_heads: int, head_dim: int,
-                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           split_keys: bool = True) -> torch.Tensor:
     """qkv [B, S, (n_h + 2 n_kv) d] with q, k rotated; stores K/V at slots position_ids[b, s], then each
-    query attends over cache slots 0 .. its position -> o [B, S, n_h d]."""
+    query attends over cache slots 0 .. its position -> o [B, S, n_h d]. With split_keys (default) a
+    workspace for the key-split records is used (allocated here if not given); without, none is passed."""
     lib = load()
     B, S = qkv.shape[0], qkv.shape[1]
+    ctx = k_cache.shape[1]
     o = out if out is not None else torch.empty((B, S, n_heads * head_dim), dtype=qkv.dtype, device=qkv.device)
+    dt = _dtype_code(qkv.dtype)
+    ws = None
+    if split_keys:
+        need = lib.gqa_attn_prefill_chunk_workspace_bytes(B, S, n_heads, n_kv_heads, head_dim, ctx, dt)
+        ws = workspace if workspace is not None else (
+            torch.empty(need, dtype=torch.uint8, device=qkv.device) if need > 0 else None)
     _check(lib.gqa_attn_prefill_chunk(_ptr(qkv), _ptr(position_ids), _ptr(o), _ptr(k_cache), _ptr(v_cache),
-                                      k_cache.shape[1], B, S, n_heads, n_kv_heads, head_dim, _dtype_code(qkv.dtype),
-                                      _stream(qkv)), "gqa_attn_prefill_chunk")
+                                      ctx, B, S, n_heads, n_kv_heads, head_dim, dt, _ptr(ws),
+                                      ws.numel() if ws is not None else 0, _stream(qkv)), "gqa_attn_prefill_chunk")
     return o
 
 
@@ -359,7 +370,8 @@ def llama_layer_forward_chunk(cfg: LayerConfig, weights: dict, hidden: torch.Ten
     w = LLLayerWeights(*(weights[k].data_ptr() for k in ("w_qkv", "w_o", "w_gate_up", "w_down", "g_attn", "g_mlp")))
     for k in ("w_qkv", "w_o", "w_gate_up", "w_down", "g_attn", "g_mlp"):
         _ptr(weights[k])
-    need = lib.llama_layer_workspace_bytes(ctypes.byref(c), B, S, 0)
+    # sized with the cache length: includes room for key-split attention records on small chunks
+    need = lib.llama_layer_workspace_bytes(ctypes.byref(c), B, S, ctx)
     if need == 0:
         raise ValueError(f"invalid layer configuration: {last_error()}")
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=hidden.device)

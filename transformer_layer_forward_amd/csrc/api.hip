@@ -421,18 +421,27 @@ ll_status gqa_attn_prefill(const void* qkv, const ll_rope* rope, const int64_t* 
     return LL_OK;
 }
 
+size_t gqa_attn_prefill_chunk_workspace_bytes(int64_t B, int64_t S, int64_t n_heads, int64_t n_kv_heads,
+                                              int64_t head_dim, int64_t ctx, int32_t dtype) {
+    if (B <= 0 || S <= 0 || n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || ctx <= 0) return 0;
+    if (n_heads % n_kv_heads != 0) return 0;
+    return attn_chunk_workspace_bytes(dtype, B, S, n_heads, n_kv_heads, head_dim, ctx);
+}
+
 ll_status gqa_attn_prefill_chunk(const void* qkv, const int64_t* position_ids, void* o, void* k_cache, void* v_cache,
                                  int64_t ctx, int64_t B, int64_t S, int64_t n_heads, int64_t n_kv_heads,
-                                 int64_t head_dim, int32_t dtype, void* stream) {
+                                 int64_t head_dim, int32_t dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
     if (!k_cache || !v_cache) return fail(LL_EINVAL, "chunked prefill needs k_cache and v_cache");
     ll_status st = check_attn_common(qkv, nullptr, position_ids, 0, o, k_cache, v_cache, ctx, B, S, n_heads,
                                      n_kv_heads, head_dim, dtype);
     if (st != LL_OK || B * S == 0) return st;
     if (ctx > kIntMax) return fail(LL_EUNSUPPORTED, "ctx exceeds 2^31-1");
+    if (workspace && !aligned16(workspace)) return fail(LL_EINVAL, "workspace must be 16-byte aligned");
     hipError_t e = launch_attn_prefill_chunk(dtype, qkv, position_ids, o, k_cache, v_cache, ctx, static_cast<int>(B),
                                              static_cast<int>(S), static_cast<int>(n_heads),
-                                             static_cast<int>(n_kv_heads), static_cast<int>(head_dim),
-                                             as_stream(stream));
+                                             static_cast<int>(n_kv_heads), static_cast<int>(head_dim), workspace,
+                                             workspace ? workspace_bytes : 0, as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, "gqa_attn_prefill_chunk launch");
     return LL_OK;
 }
@@ -525,7 +534,12 @@ ll_status swiglu_mlp(const void* x, const void* w_gate_up, const void* w_down, c
 size_t llama_layer_workspace_bytes(const ll_layer_cfg* cfg, int64_t B, int64_t S, int64_t ctx) {
     if (!cfg || B < 0 || S < 0 || ctx < 0) return 0;
     if (check_cfg(cfg) != LL_OK) return 0;
-    return layer_ws(cfg, B, S, (S == 1 && ctx > 0) ? ctx : 0).total;
+    if (S == 1 && ctx > 0) return layer_ws(cfg, B, S, ctx).total;
+    // a chunk on a cache prefix may split its attention keys: room for the partial records
+    const size_t split = ctx > 0 ? attn_chunk_workspace_bytes(cfg->dtype, B, S, cfg->n_heads, cfg->n_kv_heads,
+                                                             cfg->head_dim, ctx)
+                                 : 0;
+    return layer_ws(cfg, B, S, 0).total + round_up(split);
 }
 
 struct Varlen {
@@ -625,9 +639,10 @@ static ll_status layer_forward_impl(const ll_layer_cfg* cfg, const ll_layer_weig
                                        static_cast<int>(S), o, static_cast<int>(s.nh), static_cast<int>(s.nkv),
                                        static_cast<int>(s.d), stream_h);
     } else if (chunk) {
+        // workspace past the layer's own part holds key-split records when the caller sized it for them
         e = launch_attn_prefill_chunk(dt, qkv, position_ids, o, k_cache, v_cache, ctx, static_cast<int>(B),
                                       static_cast<int>(S), static_cast<int>(s.nh), static_cast<int>(s.nkv),
-                                      static_cast<int>(s.d), stream_h);
+                                      static_cast<int>(s.d), ws + lw.total, workspace_bytes - lw.total, stream_h);
     } else if (decode) {
         e = launch_attn_decode(dt, qkv, position_ids, nullptr, 0, k_cache, v_cache, ctx, o, static_cast<int>(B),
                                static_cast<int>(s.nh), static_cast<int>(s.nkv), static_cast<int>(s.d), dws, dbytes,

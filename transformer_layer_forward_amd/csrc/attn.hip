@@ -421,11 +421,11 @@ __device__ __forceinline__ int vt_phys(int r, int c) {
     else return c ^ (2 * ((r >> 1) & 1)) ^ (4 * ((r >> 2) & 1));
 }
 
-template <int D, int HPB, bool CACHED>
+template <int D, int HPB, bool CACHED, bool SPLIT = false>
 __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, bf16_t* __restrict__ out, bf16_t* __restrict__ kc,
     bf16_t* __restrict__ vc, int64_t ctx, int B, int S_max, int nh, int nkv, float scale_log2,
-    const int* __restrict__ cu, int total) {
+    const int* __restrict__ cu, int total, int nsplit, float* __restrict__ part) {
     using C = PrefillCfg<D>;
     constexpr int NT = 128 * HPB, NW = NT / 64;
     constexpr int CH = D / 8;                        // 16-byte chunks per row
@@ -441,9 +441,12 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     const int g = nh / nkv;
     const int hchunks = g / HPB;
     const int nqb = (S_max + C::BQ - 1) / C::BQ;
-    const int per_qb = B * nkv * hchunks;
+    if constexpr (!SPLIT) nsplit = 1;
+    const int per_qb = B * nkv * hchunks * nsplit;
     const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / per_qb;
     int rem = static_cast<int>(blockIdx.x) % per_qb;
+    const int split = rem % nsplit;
+    rem /= nsplit;
     const int hc = rem % hchunks;
     rem /= hchunks;
     const int c = rem % nkv;
@@ -495,6 +498,29 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
         lo = __builtin_amdgcn_readfirstlane(l);
         hi = __builtin_amdgcn_readfirstlane(m);
     }
+    // key tiles of this split: the visible tiles 0 .. hi / 64 shared out evenly over nsplit workgroups
+    const int nkt_all = hi / C::BKV + 1;
+    const int j0 = SPLIT ? split * nkt_all / nsplit : 0;
+    const int j1 = SPLIT ? (split + 1) * nkt_all / nsplit : nkt_all;
+    if (SPLIT && j0 >= j1) {   // nothing visible here: an empty record (weight zero in the combine)
+        {
+#pragma unroll
+            for (int qf = 0; qf < 2; ++qf) {
+                const int qi = q0 + qf * 16 + lrow;
+                if (qi >= S) continue;
+                float* rec = part + ((static_cast<int64_t>(seq0) + qi) * nh + h) * nsplit * (D + 4) +
+                             static_cast<int64_t>(split) * (D + 4);
+                if (lgrp == 0) {
+                    rec[0] = -INFINITY;
+                    rec[1] = 0.f;
+                }
+#pragma unroll
+                for (int a = 0; a < C::DF; ++a)
+                    *reinterpret_cast<f32x4*>(rec + 4 + a * 16 + 4 * lgrp) = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        return;
+    }
     int qlim[2];
 #pragma unroll
     for (int qf = 0; qf < 2; ++qf) {
@@ -537,7 +563,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
 
     // ---- cache append: the first head chunk of each query block copies the block's own keys and
     // values (its diagonal tile) to their slots, so every token is written exactly once
-    if (!CACHED && kc != nullptr && hc == 0) {
+    if (!CACHED && kc != nullptr && hc == 0 && split == 0) {
         const int64_t* pos_b = pos + seq0;
         for (int job = tid; job < 2 * C::BKV * CH; job += NT) {
             const bool isv = job >= C::BKV * CH;
@@ -626,11 +652,11 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     for (int a = 0; a < C::DF; ++a) oacc[a][0] = oacc[a][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 sA[4][2], sB[4][2];
     float mbA[2] = {0.f, 0.f}, mbB[2] = {0.f, 0.f};   // reference max each accumulator set started from
+    if constexpr (SPLIT) m_i[0] = m_i[1] = -INFINITY;   // no reference yet (a split may start wholly masked)
     bf16x8 pfr[2][2];
 
-    const int nkt = hi / C::BKV + 1;
-    issue_tiles(0, 0, 0, 0);
-    issue_k_only(1, 1);
+    issue_tiles(j0, 0, j0, 0);
+    issue_k_only(j0 + 1, 1);
     __syncthreads();
 #pragma unroll
     for (int kf = 0; kf < 4; ++kf) sA[kf][0] = sA[kf][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -643,10 +669,9 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     // stage is one basic block in which matrix ops and vector work interleave.
 #define PD_ITER(SC, MBC, SN, MBN)                                                                          \
     {                                                                                                      \
-        const bool first_ = j == 0;                                                                        \
         /* K(j+2) into the buffer K(j) used, V(j+1) into the buffer V(j-1) used: both free since the */    \
         /* barrier that ended the previous iteration                                                 */    \
-        issue_tiles(j + 2, j & 1, j + 1, (j + 1) & 1);                                                     \
+        issue_tiles(j + 2, (j - j0) & 1, j + 1, (j - j0 + 1) & 1);                                         \
         if ((j + 1) * C::BKV - 1 > lo) {                                                                   \
             _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                             \
                 _Pragma("unroll") for (int kf = 0; kf < 4; ++kf)                                           \
@@ -658,28 +683,35 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
         }                                                                                                  \
         /* stage 1: first half of tile j+1's scores || column max of tile j */                            \
         _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                                 \
-            MBN[qf] = first_ ? 0.f : m_i[qf];                                                              \
+            MBN[qf] = (SPLIT ? m_i[qf] > -INFINITY : j != 0) ? m_i[qf] : 0.f;                              \
             _Pragma("unroll") for (int kf = 0; kf < 4; ++kf) SN[kf][qf] = f32x4{-MBN[qf], -MBN[qf], -MBN[qf], -MBN[qf]}; \
         }                                                                                                  \
-        PD_QK_HALF(SN, (j + 1) & 1, 0)                                                                     \
+        PD_QK_HALF(SN, (j - j0 + 1) & 1, 0)                                                                \
         float sub_[2], shift_[2];                                                                          \
+        bool fresh_[2];                                                                                    \
         bool any_sub_ = false;                                                                             \
         _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                                 \
             float mx = -INFINITY;                                                                          \
             _Pragma("unroll") for (int kf = 0; kf < 4; ++kf)                                               \
                 _Pragma("unroll") for (int r = 0; r < 4; ++r) mx = fmaxf(mx, SC[kf][qf][r]);               \
             mx = rows_max(mx);                                                                             \
-            const float delta = first_ ? 0.f : m_i[qf] - MBC[qf];                                          \
+            if constexpr (SPLIT) fresh_[qf] = m_i[qf] == -INFINITY;                                        \
+            const float delta = (SPLIT && fresh_[qf]) ? 0.f : m_i[qf] - MBC[qf];                           \
             const float rel = mx - delta;                                                                  \
-            shift_[qf] = (first_ || rel > kSlack) ? rel : 0.f;                                             \
+            if constexpr (SPLIT) {                                                                         \
+                shift_[qf] = (fresh_[qf] ? rel > -INFINITY : rel > kSlack) ? rel : 0.f;                    \
+            } else {                                                                                       \
+                fresh_[qf] = j == 0;                                                                       \
+                shift_[qf] = (fresh_[qf] || rel > kSlack) ? rel : 0.f;                                     \
+            }                                                                                              \
             sub_[qf] = delta + shift_[qf];                                                                 \
             any_sub_ |= sub_[qf] != 0.f;                                                                   \
         }                                                                                                  \
         /* stage 2 (rare): re-reference tile j's scores, rescale O and l where the reference moved */     \
         if (__any(any_sub_)) {                                                                             \
             _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                             \
-                const float alpha = first_ ? 1.f : fast_exp2(-shift_[qf]);                                 \
-                m_i[qf] = (first_ ? MBC[qf] : m_i[qf]) + shift_[qf];                                       \
+                const float alpha = fresh_[qf] ? 1.f : fast_exp2(-shift_[qf]);                             \
+                m_i[qf] = (SPLIT && fresh_[qf] ? 0.f : m_i[qf]) + shift_[qf];                              \
                 l_i[qf] *= alpha;                                                                          \
                 _Pragma("unroll") for (int a = 0; a < C::DF; ++a) oacc[a][qf] *= alpha;                    \
                 _Pragma("unroll") for (int kf = 0; kf < 4; ++kf) SC[kf][qf] -= sub_[qf];                   \
@@ -687,20 +719,20 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
         }                                                                                                  \
         float ls[2] = {0.f, 0.f};                                                                          \
         /* stage 3: second half of tile j+1's scores || exponentials of keys 0..31 */                      \
-        PD_QK_HALF(SN, (j + 1) & 1, KH)                                                                    \
+        PD_QK_HALF(SN, (j - j0 + 1) & 1, KH)                                                               \
         PD_EXP_HALF(SC, 0)                                                                                 \
         /* stage 4: P V of keys 0..31 || exponentials of keys 32..63 */                                    \
-        PD_PV_HALF(j & 1, 0)                                                                               \
+        PD_PV_HALF((j - j0) & 1, 0)                                                                        \
         PD_EXP_HALF(SC, 1)                                                                                 \
         /* stage 5: P V of keys 32..63 */                                                                  \
-        PD_PV_HALF(j & 1, 1)                                                                               \
+        PD_PV_HALF((j - j0) & 1, 1)                                                                        \
         l_i[0] += ls[0];                                                                                   \
         l_i[1] += ls[1];                                                                                   \
         __syncthreads();                                                                                   \
     }
-    for (int j = 0; j < nkt; j += 2) {
+    for (int j = j0; j < j1; j += 2) {
         PD_ITER(sA, mbA, sB, mbB)
-        if (j + 1 >= nkt) break;
+        if (j + 1 >= j1) break;
         {
             const int j_ = j;
             {
@@ -714,7 +746,27 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
 #undef PD_PV_HALF
 #undef PD_EXP_HALF
 
-    // ---- normalise and store: lane holds dims a*16 + 4 lgrp + {0..3} of query q0 + qf*16 + lrow
+    // ---- lane holds dims a*16 + 4 lgrp + {0..3} of query q0 + qf*16 + lrow. With key splits: this
+    // split's record for the combine kernel ([0] reference max, log2 units; [1] sum; [4..4+D) unnormalised
+    // o); else normalise and store.
+    if constexpr (SPLIT) {
+#pragma unroll
+        for (int qf = 0; qf < 2; ++qf) {
+            const float lsum = rows_sum(l_i[qf]);
+            const int qi = q0 + qf * 16 + lrow;
+            if (qi >= S) continue;
+            float* rec = part + ((static_cast<int64_t>(seq0) + qi) * nh + h) * nsplit * (D + 4) +
+                         static_cast<int64_t>(split) * (D + 4);
+            if (lgrp == 0) {
+                rec[0] = m_i[qf];
+                rec[1] = lsum;
+            }
+#pragma unroll
+            for (int a = 0; a < C::DF; ++a)
+                *reinterpret_cast<f32x4*>(rec + 4 + a * 16 + 4 * lgrp) = oacc[a][qf];
+        }
+        return;
+    }
 #pragma unroll
     for (int qf = 0; qf < 2; ++qf) {
         const float inv = 1.f / rows_sum(l_i[qf]);
@@ -1197,7 +1249,7 @@ static hipError_t prefill_go(const void* qkv, const int64_t* pos, const RopeTab*
     if (!ROPE && offsets_ok)
         hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, false>), dim3(blocks), dim3(128 * HPB), 0, st,
                            static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
-                           static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2, nullptr, 0);
+                           static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2, nullptr, 0, 1, nullptr);
     else
         hipLaunchKernelGGL((attn_prefill_mfma_kernel<D, HPB, ROPE, IL>), dim3(blocks), dim3(128 * HPB), 0, st,
                            static_cast<const bf16_t*>(qkv), pos, tab ? tab->cs : nullptr, tab ? tab->rows : 1,
@@ -1336,31 +1388,100 @@ hipError_t launch_attn_decode(int dtype, const void* qkv, const int64_t* pos, co
 }
 
 // Chunked prefill on a cache prefix: store the chunk's (already rotated) keys and values at their
-// slots, then every query attends over cache slots 0 .. its position.
+// slots, then every query attends over cache slots 0 .. its position. A small chunk gives few
+// query-block workgroups; their key tiles are then shared out over nsplit workgroups each, which write
+// (reference max, sum, unnormalised o) records that a combine kernel merges.
+constexpr int CHUNK_SPLIT_TARGET = 256;   // workgroups aimed for when splitting keys
+constexpr int CHUNK_SPLIT_MAX = 32;
+
+static int chunk_hpb(int g) { return g % 4 == 0 ? 4 : (g % 2 == 0 ? 2 : 1); }
+
+static int chunk_nsplit(int64_t B, int64_t S, int64_t nh, int64_t nkv, int64_t ctx) {
+    const int64_t g = nh / nkv;
+    const int64_t base = (S + 63) / 64 * B * nkv * (g / chunk_hpb(static_cast<int>(g)));
+    if (base <= 0 || base >= CHUNK_SPLIT_TARGET) return 1;
+    const int64_t tiles = (ctx + 63) / 64;
+    const int64_t cap = std::min<int64_t>(CHUNK_SPLIT_MAX, std::max<int64_t>(1, tiles / 2));
+    return static_cast<int>(std::max<int64_t>(1, std::min(cap, (CHUNK_SPLIT_TARGET + base - 1) / base)));
+}
+
+static bool chunk_mfma_path(int dtype, int64_t nh, int64_t nkv, int64_t d, int64_t ctx) {
+    return attn_mfma_supported(dtype, static_cast<int>(d), static_cast<int>(nh), static_cast<int>(nkv)) &&
+           ctx * nkv * d * 2 < (int64_t(1) << 32);
+}
+
+size_t attn_chunk_workspace_bytes(int dtype, int64_t B, int64_t S, int64_t nh, int64_t nkv, int64_t d, int64_t ctx) {
+    if (B <= 0 || S <= 0 || nkv <= 0 || ctx <= 0 || !chunk_mfma_path(dtype, nh, nkv, d, ctx)) return 0;
+    const int ns = chunk_nsplit(B, S, nh, nkv, ctx);
+    return ns > 1 ? static_cast<size_t>(B * S * nh * ns * (d + 4)) * sizeof(float) : 0;
+}
+
+// One wave per (token, query head): log-sum-exp merge of its key-split records (layout [rows][nsplit][D + 4]).
+template <int D>
+__global__ __launch_bounds__(256) void attn_split_combine_kernel(const float* __restrict__ part,
+                                                                 bf16_t* __restrict__ out, int64_t rows,
+                                                                 int nsplit) {
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int lane = threadIdx.x & 63;
+    constexpr int REC = D + 4;
+    const float* pr = part + row * nsplit * REC;
+    float M = -INFINITY;
+    for (int k = lane; k < nsplit; k += 64) M = fmaxf(M, pr[k * REC]);
+    M = wave_max(M);        // finite: key 0 is visible to every query and lies in some split
+    float den = 0.f;
+    for (int k = lane; k < nsplit; k += 64) {
+        const float m = pr[k * REC];
+        if (m > -INFINITY) den += pr[k * REC + 1] * exp2f(m - M);
+    }
+    den = wave_sum(den);
+    const float inv = 1.f / den;
+    for (int dd = lane; dd < D; dd += 64) {
+        float num = 0.f;
+        for (int k = 0; k < nsplit; ++k) {
+            const float m = pr[k * REC];
+            if (m > -INFINITY) num += pr[k * REC + 4 + dd] * exp2f(m - M);
+        }
+        out[row * D + dd] = f2bf(num * inv);
+    }
+}
+
 template <int D, int HPB>
 static hipError_t chunk_go(const void* qkv, const int64_t* pos, void* o, void* kc, void* vc, int64_t ctx, int B,
-                           int S, int nh, int nkv, hipStream_t st) {
+                           int S, int nh, int nkv, int nsplit, float* part, hipStream_t st) {
     const int g = nh / nkv;
     const int nqb = (S + 63) / 64;
-    const unsigned blocks = static_cast<unsigned>(nqb) * B * nkv * (g / HPB);
+    const unsigned blocks = static_cast<unsigned>(nqb) * B * nkv * (g / HPB) * nsplit;
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
-    hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, true>), dim3(blocks), dim3(128 * HPB), 0, st,
-                       static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
-                       static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2, nullptr, 0);
+    if (nsplit > 1)
+        hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, true, true>), dim3(blocks), dim3(128 * HPB), 0, st,
+                           static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
+                           static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2, nullptr, 0, nsplit, part);
+    else
+        hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, true>), dim3(blocks), dim3(128 * HPB), 0, st,
+                           static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
+                           static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2, nullptr, 0, 1, nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nsplit == 1) return e;
+    const int64_t rows = static_cast<int64_t>(B) * S * nh;
+    hipLaunchKernelGGL(attn_split_combine_kernel<D>, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, st,
+                       static_cast<const float*>(part), static_cast<bf16_t*>(o), rows, nsplit);
     return hipGetLastError();
 }
 
 template <int D>
 static hipError_t chunk_hpb_sel(const void* qkv, const int64_t* pos, void* o, void* kc, void* vc, int64_t ctx, int B,
-                                int S, int nh, int nkv, hipStream_t st) {
-    const int g = nh / nkv;
-    if (g % 4 == 0) return chunk_go<D, 4>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, st);
-    if (g % 2 == 0) return chunk_go<D, 2>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, st);
-    return chunk_go<D, 1>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, st);
+                                int S, int nh, int nkv, int nsplit, float* part, hipStream_t st) {
+    switch (chunk_hpb(nh / nkv)) {
+        case 4: return chunk_go<D, 4>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, nsplit, part, st);
+        case 2: return chunk_go<D, 2>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, nsplit, part, st);
+        default: return chunk_go<D, 1>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, nsplit, part, st);
+    }
 }
 
 hipError_t launch_attn_prefill_chunk(int dtype, const void* qkv, const int64_t* pos, void* o, void* kc, void* vc,
-                                     int64_t ctx, int B, int S, int nh, int nkv, int d, hipStream_t st) {
+                                     int64_t ctx, int B, int S, int nh, int nkv, int d, void* ws, size_t ws_bytes,
+                                     hipStream_t st) {
     if (B == 0 || S == 0) return hipSuccess;
     // 1) append the chunk's keys and values at slots pos[b, s]
     const unsigned kb = static_cast<unsigned>((static_cast<int64_t>(B) * S * nkv + 3) / 4);
@@ -1373,10 +1494,13 @@ hipError_t launch_attn_prefill_chunk(int dtype, const void* qkv, const int64_t* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // 2) attention over slots 0 .. pos[b, s]
-    const bool offsets_ok = ctx * nkv * d * 2 < (int64_t(1) << 32);
-    if (attn_mfma_supported(dtype, d, nh, nkv) && offsets_ok) {
-        if (d == 128) return chunk_hpb_sel<128>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, st);
-        return chunk_hpb_sel<64>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, st);
+    if (chunk_mfma_path(dtype, nh, nkv, d, ctx)) {
+        // key splits only with enough workspace for their records (none given: one workgroup per block)
+        const size_t need = attn_chunk_workspace_bytes(dtype, B, S, nh, nkv, d, ctx);
+        const int nsplit = (need > 0 && ws != nullptr && ws_bytes >= need) ? chunk_nsplit(B, S, nh, nkv, ctx) : 1;
+        float* part = static_cast<float*>(ws);
+        if (d == 128) return chunk_hpb_sel<128>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, nsplit, part, st);
+        return chunk_hpb_sel<64>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, nsplit, part, st);
     }
     const unsigned blocks = static_cast<unsigned>((static_cast<int64_t>(B) * S * nh + 3) / 4);
     const float scale = 1.f / sqrtf(static_cast<float>(d));
@@ -1402,7 +1526,7 @@ static hipError_t varlen_go(const void* qkv, const int* cu, int nseq, int max_se
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
     hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, false>), dim3(blocks), dim3(128 * HPB), 0, st,
                        static_cast<const bf16_t*>(qkv), nullptr, static_cast<bf16_t*>(o), nullptr, nullptr, 1, nseq,
-                       max_seqlen, nh, nkv, scale_log2, cu, total);
+                       max_seqlen, nh, nkv, scale_log2, cu, total, 1, nullptr);
     return hipGetLastError();
 }
 

@@ -95,9 +95,12 @@ hipError_t launch_attn_prefill(int dtype, const void* qkv, const int64_t* pos, c
                                void* o, void* kc, void* vc, int64_t ctx, int B, int S, int nh, int nkv, int d,
                                hipStream_t st);
 // chunked prefill on a cache prefix: q and k already rotated; stores the chunk's K/V at slots pos[b, s],
-// then query (b, s) attends over cache slots 0 .. pos[b, s]
+// then query (b, s) attends over cache slots 0 .. pos[b, s]. With ws of at least
+// attn_chunk_workspace_bytes bytes small chunks split their key range over several workgroups.
+size_t attn_chunk_workspace_bytes(int dtype, int64_t B, int64_t S, int64_t nh, int64_t nkv, int64_t d, int64_t ctx);
 hipError_t launch_attn_prefill_chunk(int dtype, const void* qkv, const int64_t* pos, void* o, void* kc, void* vc,
-                                     int64_t ctx, int B, int S, int nh, int nkv, int d, hipStream_t st);
+                                     int64_t ctx, int B, int S, int nh, int nkv, int d, void* ws, size_t ws_bytes,
+                                     hipStream_t st);
 // packed (varlen) prefill: q and k already rotated; sequence i is tokens cu[i] .. cu[i+1]-1 of `total`
 hipError_t launch_attn_prefill_varlen(int dtype, const void* qkv, const int* cu, int nseq, int max_seqlen, int total,
                                       void* o, int nh, int nkv, int d, hipStream_t st);
