@@ -261,14 +261,18 @@ def test_layer_varlen_small(case):
     check(to_f64(out), x64, want["out"], want["attn_proj"] + want["mlp_out"], cfg.dtype, cfg.name)
 
 
-def test_layer_varlen_equals_separate_calls():
-    """Packing changes nothing per token: the varlen layer equals one llama_layer_forward per sequence,
-    bit for bit (every sequence longer than 64 tokens, so both runs use the same GEMM kernels)."""
+@pytest.mark.parametrize("base", ["tiny_f32", "llama3_8b_prefill"])
+def test_layer_varlen_equals_separate_calls(base):
+    """Packing changes nothing per token: the varlen layer equals one llama_layer_forward per sequence.
+    fp32: bit for bit (its kernels compute each row alone). bf16: a projection with few 256 x 256
+    tiles splits K into a number of ranges that depends on the token count, so the packed and the
+    separate runs may round differently; they must agree to within a few bf16 steps, where a token
+    that saw another sequence's keys would be off by the size of the output itself."""
     require_gpu()
     lens = (130, 257, 65)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(cu[-1])
-    cfg = scaled(CONFIGS["llama3_8b_prefill"], B=1, S=T)
+    cfg = scaled(CONFIGS[base], B=1, S=T)
     W = dev_weights(make_weights(cfg, seed=6), cfg.dtype)
     x = to_dev(make_hidden(cfg, seed=6), cfg.dtype)[0]
     pos = torch.from_numpy(np.concatenate([np.arange(n) for n in lens]).astype(np.int64)).to(DEV)
@@ -279,7 +283,15 @@ def test_layer_varlen_equals_separate_calls():
         a, b = int(cu[i]), int(cu[i + 1])
         one = L.llama_layer_forward(lc, W, x[None, a:b].contiguous(), pos[None, a:b].contiguous(), kv_seq_len=kv)
         torch.cuda.synchronize()
-        assert torch.equal(packed[a:b], one[0]), i
+        if cfg.dtype == "f32":
+            assert torch.equal(packed[a:b], one[0]), i
+        else:
+            # the residual stream (|x| up to ~4) dominates the output: compare the layer's increment
+            got, want, xin = packed[a:b].float(), one[0].float(), x[a:b].float()
+            diff = (got - want).abs().max().item()
+            scale = (want - xin).abs().max().item()
+            print(f"seq {i}: max |packed - separate| {diff:.3e}, max |layer increment| {scale:.3e}")
+            assert diff <= 2.0 ** -7 * want.abs().max().item() + 2.0 ** -6 * scale, (i, diff, scale)
 
 
 # ------------------------------------------------------------------ full-size workloads, sampled rows

@@ -329,12 +329,16 @@ __device__ __forceinline__ int mf_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); 
 
 #define MF_WAITVM0() __builtin_amdgcn_s_waitcnt(0x0F70)   // vmcnt(0) only
 
-template <int EPI, int RD = 0>
+// SPLIT: the workgroup computes one K range (kw columns; blockIdx = tile * splits + range) and writes
+// its fp32 sums to P[range][M][Nw] (gate_up: gate sums at column n, up sums at N + n) for
+// gemm_splitk_reduce_kernel, which applies the epilogue. Few-tile shapes use it to fill the chip.
+template <int EPI, int RD = 0, bool SPLIT = false>
 __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, const bf16_t* __restrict__ R,
     int M, int N, int K, int tiles_m, int tiles_n, const int64_t* __restrict__ rpos, const float2* __restrict__ rcs,
-    int64_t rrows, int rope_cols, int ril) {
+    int64_t rrows, int rope_cols, int ril, float* __restrict__ P = nullptr, int kw = 0, int splits = 1) {
     static_assert(EPI != EPI_ROPE || RD == 64 || RD == 128, "fused RoPE for head sizes 64 and 128");
+    static_assert(!SPLIT || EPI == EPI_STORE || EPI == EPI_SILU, "split partials: plain or gate/up layout");
     extern __shared__ __align__(16) bf16_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
@@ -344,6 +348,12 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     // ---- tile order: a contiguous range per XCD, then groups of 8 token tiles
     const int T = tiles_m * tiles_n;
     int lin = blockIdx.x;
+    int range = 0, kb = 0;   // K range of this workgroup: columns [kb, min(K, kb + kw))
+    if constexpr (SPLIT) {
+        range = lin % splits;
+        lin /= splits;
+        kb = range * kw;
+    }
     if ((T & 7) == 0) lin = (lin & 7) * (T >> 3) + (lin >> 3);
     constexpr int GROUP = 8;
     const int group = lin / (GROUP * tiles_n);
@@ -411,9 +421,9 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     // done with stage t-1, whose slot receives stage t+1, its 16 loads spread over the first two k16
     // quarters of stage t. The last iteration re-reads the final stage into the free slot (never read),
     // which keeps the loop free of branches.
-    const int nk = K / MF_K;
+    const int nk = SPLIT ? (min(K, kb + kw) - kb) / MF_K : K / MF_K;
 #pragma unroll
-    for (int j = 0; j < MF_LPW; ++j) issue1(0, 0, j);
+    for (int j = 0; j < MF_LPW; ++j) issue1(0, kb, j);
     bf16x8 fa[2][4], fb[2][4];
 #define MF_MMA2(FA, FB, p)                                                                                   \
     {                                                                                                      \
@@ -424,7 +434,7 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     for (int t = 0; t < nk; ++t) {
         const int slot = t & 1;
         const bf16_t* st = smem + slot * MF_STAGE;
-        const int kn = min(t + 1, nk - 1) * MF_K;
+        const int kn = kb + min(t + 1, nk - 1) * MF_K;
         MF_WAITVM0();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
@@ -453,6 +463,46 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     // written to this wave's 32 KiB of LDS as [token][column] rows (16-byte chunks XOR-swizzled by
     // row), and then stored with full-row 16-byte-per-lane writes.
     MF_WAITVM0();                        // tail loads have landed: the ring may be overwritten
+    if constexpr (SPLIT) {
+        // fp32 sums straight from the accumulators: per row, the four 16-byte stores of a block's
+        // register groups fill whole 128-byte lines (gate_up: 64 bytes of gate and of up sums)
+        const int Nw = EPI == EPI_SILU ? 2 * N : N;
+        float* pr = P + static_cast<int64_t>(range) * M * Nw;
+        constexpr int OCS = EPI == EPI_SILU ? 64 : 128;
+        const int nws = n0 + wn * OCS;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int m = m0 + wm * 128 + 32 * b + l32;
+            if (m >= M) continue;
+            float* prow = pr + static_cast<int64_t>(m) * Nw;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                if constexpr (EPI == EPI_SILU) {
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        const int c = nws + 16 * a + 8 * g + 4 * lh;
+                        if (c >= N) continue;
+                        const f32x4 gt = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
+                                          acc[a][b][4 * g + 3]};
+                        const f32x4 up = {acc[a][b][4 * g + 8], acc[a][b][4 * g + 9], acc[a][b][4 * g + 10],
+                                          acc[a][b][4 * g + 11]};
+                        *reinterpret_cast<f32x4*>(prow + c) = gt;
+                        *reinterpret_cast<f32x4*>(prow + N + c) = up;
+                    }
+                } else {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int c = nws + 32 * a + 8 * g + 4 * lh;
+                        if (c >= N) continue;
+                        const f32x4 v = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
+                                         acc[a][b][4 * g + 3]};
+                        *reinterpret_cast<f32x4*>(prow + c) = v;
+                    }
+                }
+            }
+        }
+        return;
+    }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     constexpr int OC = EPI == EPI_SILU ? 64 : 128;           // output columns of this wave
@@ -814,12 +864,58 @@ static SkinnyPlan skinny_plan(int epi, int64_t N, int64_t K) {
     return p;
 }
 
+// Split-K plan for the 256 x 256 kernel. A shape with fewer tiles than the chip has compute units
+// (256) runs each tile as several K ranges; the count minimises a cost model: the waves of
+// workgroups times one range's MFMA time (MF_STAGE_US per 64-wide stage, as measured on the
+// unsplit kernel) plus the fp32 partials written and read back (MF_PART_BPUS bytes per microsecond)
+// and the reduce launch (MF_REDUCE_US).
+struct MfPlan {
+    int splits, kw;
+};
+constexpr int MF_CUS = 256, MF_MAX_SPLITS = 32;
+constexpr double MF_STAGE_US = 1.43, MF_PART_BPUS = 4.0e6, MF_REDUCE_US = 4.0;
+
+static bool mf_usable(int epi, int64_t N, int64_t K, const RopeEpi* re) {
+    const int64_t wspan = epi == EPI_SILU ? 2 * N : MF_N;
+    const bool offsets_ok = 2 * wspan * K < (int64_t(1) << 32) && 2 * int64_t(MF_M) * K < (int64_t(1) << 32);
+    const bool rope_ok = epi != EPI_ROPE || (re && (re->d == 64 || re->d == 128));
+    return K % MF_K == 0 && N % 8 == 0 && offsets_ok && rope_ok;
+}
+
+static MfPlan mf_plan(int epi, int64_t M, int64_t N, int64_t K) {
+    const int64_t ncols = epi == EPI_SILU ? MF_N / 2 : MF_N;
+    const int64_t T = ((M + MF_M - 1) / MF_M) * ((N + ncols - 1) / ncols);
+    const int64_t nk = K / MF_K, Nw = epi == EPI_SILU ? 2 * N : N;
+    MfPlan best{1, static_cast<int>(K)};
+    if (T >= MF_CUS) return best;
+    double best_t = static_cast<double>((T + MF_CUS - 1) / MF_CUS) * nk * MF_STAGE_US;
+    for (int64_t s = 2; s <= MF_MAX_SPLITS && s <= nk; ++s) {
+        const int64_t per = (nk + s - 1) / s, se = (nk + per - 1) / per;   // stages per range, ranges
+        if (se != s) continue;
+        const double t = static_cast<double>((T * s + MF_CUS - 1) / MF_CUS) * per * MF_STAGE_US +
+                         static_cast<double>(s * M * Nw * 8) / MF_PART_BPUS + MF_REDUCE_US;
+        if (t < best_t) {
+            best_t = t;
+            best = MfPlan{static_cast<int>(s), static_cast<int>(per * MF_K)};
+        }
+    }
+    return best;
+}
+
 size_t gemm_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K, int epi) {
-    if (dtype != LL_BF16 || !use_skinny(M)) return 0;
-    const SkinnyPlan p = skinny_plan(epi, N, K);
-    if (p.direct) return 0;
+    if (dtype != LL_BF16 || M == 0 || N == 0) return 0;
     const int64_t Nw = epi == EPI_SILU ? 2 * N : N;
-    return static_cast<size_t>(p.splits) * M * Nw * sizeof(float);
+    if (use_skinny(M)) {
+        const SkinnyPlan p = skinny_plan(epi, N, K);
+        if (p.direct) return 0;
+        return static_cast<size_t>(p.splits) * M * Nw * sizeof(float);
+    }
+    // the RoPE head size does not change the plan; a shape the 256 x 256 kernel cannot take needs none
+    RopeEpi probe{};
+    probe.d = 128;
+    if (!mf_usable(epi, N, K, &probe)) return 0;
+    const MfPlan p = mf_plan(epi, M, N, K);
+    return p.splits > 1 ? static_cast<size_t>(p.splits) * M * Nw * sizeof(float) : 0;
 }
 
 template <int EPI, bool DIRECT, int RD>
@@ -862,6 +958,34 @@ static hipError_t mfma32_launch(const void* X, const void* W, void* C, const voi
                        static_cast<const bf16_t*>(R), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tm,
                        tn, re ? re->pos : nullptr, re ? re->tab.cs : nullptr, re ? re->tab.rows : 1,
                        re ? re->rope_cols : 0, re ? re->interleaved : 0);
+    return hipGetLastError();
+}
+
+// K ranges of the 256 x 256 kernel into fp32 partials, then the reduce applies the epilogue
+template <int EPI>
+static hipError_t mfma32_split_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N,
+                                      int64_t K, const MfPlan& p, void* ws, hipStream_t st,
+                                      const RopeEpi* re = nullptr) {
+    constexpr int PE = EPI == EPI_SILU ? EPI_SILU : EPI_STORE;   // partial layout
+    static bool attr = [] {
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_mfma32_kernel<PE, 0, true>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, MF_LDS_BYTES) == hipSuccess;
+    }();
+    if (!attr) return hipErrorInvalidConfiguration;
+    const int ncols = EPI == EPI_SILU ? MF_N / 2 : MF_N;
+    const int tm = static_cast<int>((M + MF_M - 1) / MF_M), tn = static_cast<int>((N + ncols - 1) / ncols);
+    hipLaunchKernelGGL((gemm_bf16_mfma32_kernel<PE, 0, true>), dim3(tm * tn * p.splits), dim3(MF_THREADS),
+                       MF_LDS_BYTES, st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), nullptr,
+                       nullptr, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tm, tn, nullptr,
+                       nullptr, int64_t(1), 0, 0, static_cast<float*>(ws), p.kw, p.splits);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total = M * N, Nw = EPI == EPI_SILU ? 2 * N : N;
+    hipLaunchKernelGGL(gemm_splitk_reduce_kernel<EPI>, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
+                       st, static_cast<const float*>(ws), static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R),
+                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(Nw), p.splits,
+                       re ? re->pos : nullptr, re ? re->tab.cs : nullptr, re ? re->tab.rows : 1,
+                       re ? re->rope_cols : 0, re ? re->d : 2, re ? re->interleaved : 0);
     return hipGetLastError();
 }
 
@@ -923,10 +1047,18 @@ hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C
     }
     // the 4-wave kernel addresses operands by 32-bit byte offsets from its tile's first rows: 256 token
     // rows, and 256 weight rows (gate_up: up to row 2N - 1)
-    const int64_t wspan = epi == EPI_SILU ? 2 * N : MF_N;
-    const bool mf_offsets_ok = 2 * wspan * K < (int64_t(1) << 32) && 2 * int64_t(MF_M) * K < (int64_t(1) << 32);
-    const bool mf_rope_ok = epi != EPI_ROPE || re->d == 64 || re->d == 128;
-    if (K % MF_K == 0 && N % 8 == 0 && mf_offsets_ok && mf_rope_ok) {
+    if (mf_usable(epi, N, K, re)) {
+        const MfPlan p = mf_plan(epi, M, N, K);
+        const size_t need = static_cast<size_t>(p.splits) * M * (epi == EPI_SILU ? 2 * N : N) * sizeof(float);
+        if (p.splits > 1) {
+            if (ws_bytes < need || !ws) return hipErrorInvalidValue;
+            switch (epi) {
+                case EPI_STORE: return mfma32_split_launch<EPI_STORE>(X, W, C, R, M, N, K, p, ws, st);
+                case EPI_RESIDUAL: return mfma32_split_launch<EPI_RESIDUAL>(X, W, C, R, M, N, K, p, ws, st);
+                case EPI_ROPE: return mfma32_split_launch<EPI_ROPE>(X, W, C, R, M, N, K, p, ws, st, re);
+                default: return mfma32_split_launch<EPI_SILU>(X, W, C, R, M, N, K, p, ws, st);
+            }
+        }
         switch (epi) {
             case EPI_STORE: return mfma32_launch<EPI_STORE>(X, W, C, R, M, N, K, st);
             case EPI_RESIDUAL: return mfma32_launch<EPI_RESIDUAL>(X, W, C, R, M, N, K, st);
