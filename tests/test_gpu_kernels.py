@@ -83,7 +83,8 @@ def test_rope_apply(rc, il, dtype, d):
 @pytest.mark.parametrize("dtype,M,H,I", [("bf16", 1, 256, 512), ("bf16", 37, 512, 1000), ("bf16", 64, 256, 384),
                                          ("bf16", 48, 1288, 2056), ("bf16", 65, 256, 384), ("bf16", 300, 1024, 2048),
                                          ("bf16", 515, 512, 1032), ("bf16", 20, 200, 1000), ("bf16", 33, 520, 240),
-                                         ("bf16", 200, 512, 4096), ("bf16", 96, 256, 1984),
+                                         ("bf16", 200, 512, 4096), ("bf16", 96, 256, 1984), ("bf16", 16, 2048, 256),
+                                         ("bf16", 64, 384, 1152),
                                          ("f32", 32, 64, 176), ("f32", 45, 96, 200)])
 @pytest.mark.parametrize("with_residual", [False, True])
 def test_swiglu_mlp(dtype, M, H, I, with_residual):

@@ -431,6 +431,9 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
         acc[a_][b_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[a_], FB[b_], acc[a_][b_], 0, 0, 0);       \
         acc[a_][b_ + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[a_], FB[b_ + 1], acc[a_][b_ + 1], 0, 0, 0); \
     }
+    // no scalar load may be outstanding at the loop head: the compiler then waits for just the first
+    // fragments of each stage instead of all of them (LDS returns in order, scalar loads do not)
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     for (int t = 0; t < nk; ++t) {
         const int slot = t & 1;
         const bf16_t* st = smem + slot * MF_STAGE;
@@ -756,6 +759,151 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_bf16_skinny_kernel(
     }
 }
 
+// ------------------------------------------------------------------ bf16, small M, LDS ring (K % 128 == 0)
+// The decode projections again (M <= 64), with the weight tile streamed through a ring of three LDS
+// stages by buffer loads straight into LDS: a stage is 128 weight rows x 128 columns (256 bytes of
+// each row) plus the matching 64 x 128 activation block, 48 KiB; two stages are in flight while the
+// third is consumed, and no registers hold data in flight. Each workgroup walks its K range starting
+// at a stage rotated by its row block, so at any moment the workgroups read different column
+// offsets of their rows: with all of them at the same offset, rows a power-of-two stride apart crowd
+// the same memory channels (one range over K = 4096: 4.6 -> 5.1-5.4 TB/s). Wave w owns weight rows
+// 16w..16w+15 (gate_up: waves 0-3 gate rows, 4-7 the up rows of the same 64 columns) and multiplies
+// them by the 64 tokens with v_mfma_f32_16x16x32_bf16. Single range: epilogue in the kernel (gate_up:
+// the up waves hand their sums to the gate waves through LDS); several ranges: fp32 partials for
+// gemm_splitk_reduce_kernel.
+constexpr int SR_R = 128, SR_KS = 128, SR_NST = 3, SR_THREADS = 512;
+constexpr int SR_WST = SR_R * SR_KS, SR_XST = 64 * SR_KS, SR_STAGE = SR_WST + SR_XST;   // elements
+constexpr int SR_LDS = SR_NST * SR_STAGE * 2;                                              // 144 KiB
+#define SR_WAIT_VM6() __builtin_amdgcn_s_waitcnt(0x0F76)   // vmcnt(6): one stage (6 loads) may stay out
+#define SR_WAIT_VM0() __builtin_amdgcn_s_waitcnt(0x0F70)
+
+template <int EPI>
+__global__ __launch_bounds__(SR_THREADS, 1) void gemm_bf16_skinny_ring_kernel(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, const bf16_t* __restrict__ R,
+    float* __restrict__ P, int M, int N, int K, int nrb, int kw, int direct) {
+    extern __shared__ __align__(16) bf16_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    const int rb = blockIdx.x % nrb, kc = blockIdx.x / nrb;
+    const int kbeg = kc * kw, kend = min(K, kbeg + kw);
+    const int nst = (kend - kbeg) / SR_KS;
+    // weight row of tile row r (clamped to a valid row; results of clamped rows are never stored)
+    const int wbase = EPI == EPI_SILU ? rb * 64 : rb * SR_R;
+    auto wrow_of = [&](int r) {
+        if (EPI == EPI_SILU) return r < 64 ? min(wbase + r, N - 1) : N + min(wbase + r - 64, N - 1);
+        return min(wbase + r, N - 1);
+    };
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(W + static_cast<int64_t>(wbase) * K), (short)0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(X), (short)0, -1, 0x00020000);
+    // W load j (0..3) of this wave fills KiB 4*wave + j of a stage's weight block, X load j (0..1) KiB
+    // 2*wave + j of its activation block; lane l lands in row 4*KiB + l/16 at physical 16-byte chunk
+    // l%16 and fetches the logical chunk that the row's XOR swizzle (chunk ^ row%16) puts there
+    uint32_t wo[4], xo[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = (4 * wave + j) * 4 + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        wo[j] = static_cast<uint32_t>(wrow_of(r) - wbase) * static_cast<uint32_t>(K) * 2u + c * 16u;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = (2 * wave + j) * 4 + (lane >> 4);
+        const int c = (lane & 15) ^ (m & 15);
+        xo[j] = static_cast<uint32_t>(min(m, M - 1)) * static_cast<uint32_t>(K) * 2u + c * 16u;
+    }
+    // first stage of this workgroup's walk: 5 stages further per row block (a step of 1 put the gate
+    // and up halves of gate_up's blocks in lockstep on the same channels: 67 us against 45 at M = 64)
+    const int off = (rb * 5) % nst;
+    auto issue = [&](int s, int slot) {
+        const int sp = s + off < nst ? s + off : s + off - nst;
+        const int k0 = (kbeg + sp * SR_KS) * 2;
+        bf16_t* base = smem + slot * SR_STAGE;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (__attribute__((address_space(3))) void*)(base + (4 * wave + j) * 512), 16, wo[j], k0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void*)(base + SR_WST + (2 * wave + j) * 512), 16, xo[j], k0, 0, 0);
+    };
+    f32x4 acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    issue(0, 0);
+    if (nst > 1) issue(1, 1);
+    const int ra = 16 * wave + lrow;
+    for (int t = 0; t < nst; ++t) {
+        // this wave's loads of stage t have landed; after the barrier every wave's have, and every wave
+        // is done with stage t - 1, whose slot receives stage t + 2
+        if (t + 1 < nst) SR_WAIT_VM6();
+        else SR_WAIT_VM0();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 2 < nst) issue(t + 2, (t + 2) % SR_NST);
+        const bf16_t* sw = smem + (t % SR_NST) * SR_STAGE;
+        const bf16_t* sx = sw + SR_WST;
+#pragma unroll
+        for (int s = 0; s < SR_KS / 32; ++s) {
+            const int c = 4 * s + lgrp;
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(sw + ra * SR_KS + ((c ^ (ra & 15)) << 3));
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int m = 16 * b + lrow;
+                const bf16x8 x = *reinterpret_cast<const bf16x8*>(sx + m * SR_KS + ((c ^ (m & 15)) << 3));
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, x, acc[b], 0, 0, 0);
+            }
+        }
+    }
+    // lane holds acc[b][r] = sum for token 16b + lrow and output column col0 + 4*lgrp + r
+    const int col0 = EPI == EPI_SILU ? wbase + 16 * (wave & 3) : wbase + 16 * wave;
+    const int n = col0 + 4 * lgrp;
+    if (!direct) {
+        const int64_t Nw = EPI == EPI_SILU ? 2 * static_cast<int64_t>(N) : N;
+        const int wrow0 = EPI == EPI_SILU && wave >= 4 ? N : 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int m = 16 * b + lrow;
+            if (m >= M || n >= N) continue;
+            *reinterpret_cast<f32x4*>(P + (static_cast<int64_t>(kc) * M + m) * Nw + wrow0 + n) = acc[b];
+        }
+        return;
+    }
+    if (EPI == EPI_SILU) {
+        __syncthreads();   // every wave is past its last LDS read
+        f32x4* sU = reinterpret_cast<f32x4*>(smem);
+        if (wave >= 4) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) sU[((wave - 4) * 4 + b) * 64 + lane] = acc[b];
+        }
+        __syncthreads();
+        if (wave >= 4) return;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const f32x4 u = sU[(wave * 4 + b) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[b][r] = acc[b][r] / (1.f + __expf(-acc[b][r])) * u[r];
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int m = 16 * b + lrow;
+        if (m >= M || n >= N) continue;
+        const int64_t o = static_cast<int64_t>(m) * N + n;
+        float v[4] = {acc[b][0], acc[b][1], acc[b][2], acc[b][3]};
+        if (EPI == EPI_RESIDUAL) {
+            const uint2 rr = *reinterpret_cast<const uint2*>(R + o);
+            v[0] += __uint_as_float(rr.x << 16); v[1] += __uint_as_float(rr.x & 0xffff0000u);
+            v[2] += __uint_as_float(rr.y << 16); v[3] += __uint_as_float(rr.y & 0xffff0000u);
+        }
+        *reinterpret_cast<uint2*>(C + o) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
+}
+#undef SR_WAIT_VM6
+#undef SR_WAIT_VM0
+
 // Sum split partials P[splits][M][Nw] and apply the epilogue; N = output columns.
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __restrict__ P, bf16_t* __restrict__ C,
@@ -846,20 +994,35 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // ------------------------------------------------------------------ dispatch
 static bool use_skinny(int64_t M) { return M <= SK_MAXM; }
 
-// Decode plan: workgroups over 128 output columns (gate_up: 64) times K ranges of a multiple of
-// SK_SC columns, as many ranges as keep the grid near SK_WG_TARGET workgroups. A single range
-// applies the epilogue in the kernel, except RoPE, whose rotation partner lives in another wave.
+// Decode plan. The LDS-ring kernel takes K % 128 == 0 and N % 8 == 0 (every Llama projection):
+// workgroups over 128 weight rows (gate_up: 64 gate rows + their 64 up rows), times up to 8 K ranges
+// of whole 128-column stages, as many as fill the chip (256 workgroups) while each range keeps at
+// least 8 stages (a lab sweep at M = 64 put the best counts at gate_up 1, QKV 4, o_proj 4, down 8).
+// Other shapes take the register-ring kernel: workgroups over 128 output columns (gate_up: 64) times
+// K ranges of a multiple of SK_SC columns, as many as keep the grid near SK_WG_TARGET workgroups. A
+// single range applies the epilogue in the kernel, except RoPE, whose rotation partner lives in
+// another wave.
 struct SkinnyPlan {
     int nrb, splits, kw;
-    bool direct;
+    bool direct, ring;
 };
 
 static SkinnyPlan skinny_plan(int epi, int64_t N, int64_t K) {
     SkinnyPlan p;
+    const int64_t wspan = epi == EPI_SILU ? 2 * N : SR_R;   // weight rows one descriptor spans
+    p.ring = K % SR_KS == 0 && N % 8 == 0 && wspan * K * 2 < (int64_t(1) << 32) && 64 * K * 2 < (int64_t(1) << 32);
     p.nrb = static_cast<int>(epi == EPI_SILU ? (N + 63) / 64 : (N + 127) / 128);
-    const int64_t want = std::max<int64_t>(1, SK_WG_TARGET / p.nrb);
-    p.kw = static_cast<int>(((K + want - 1) / want + SK_SC - 1) / SK_SC * SK_SC);
-    p.splits = static_cast<int>((K + p.kw - 1) / p.kw);
+    if (p.ring) {
+        const int64_t nks = K / SR_KS;
+        const int64_t s = std::max<int64_t>(1, std::min<int64_t>({8, SK_WG_TARGET / p.nrb, nks / 8}));
+        const int64_t per = (nks + s - 1) / s;
+        p.splits = static_cast<int>((nks + per - 1) / per);
+        p.kw = static_cast<int>(per * SR_KS);
+    } else {
+        const int64_t want = std::max<int64_t>(1, SK_WG_TARGET / p.nrb);
+        p.kw = static_cast<int>(((K + want - 1) / want + SK_SC - 1) / SK_SC * SK_SC);
+        p.splits = static_cast<int>((K + p.kw - 1) / p.kw);
+    }
     p.direct = p.splits == 1 && epi != EPI_ROPE;
     return p;
 }
@@ -994,10 +1157,24 @@ static hipError_t skinny_launch(const void* X, const void* W, void* C, const voi
                                 void* ws, hipStream_t st, const RopeEpi* re = nullptr) {
     const SkinnyPlan p = skinny_plan(EPI, N, K);
     const int64_t Nw = EPI == EPI_SILU ? 2 * N : N;
-    hipLaunchKernelGGL(gemm_bf16_skinny_kernel<EPI>, dim3(static_cast<unsigned>(p.nrb) * p.splits), dim3(SK_THREADS),
-                       0, st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), static_cast<bf16_t*>(C),
-                       static_cast<const bf16_t*>(R), static_cast<float*>(ws), static_cast<int>(M),
-                       static_cast<int>(N), static_cast<int>(K), p.nrb, p.kw, p.direct ? 1 : 0);
+    if (p.ring) {
+        static bool attr = [] {
+            return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_skinny_ring_kernel<EPI>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SR_LDS) == hipSuccess;
+        }();
+        if (!attr) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(gemm_bf16_skinny_ring_kernel<EPI>, dim3(static_cast<unsigned>(p.nrb) * p.splits),
+                           dim3(SR_THREADS), SR_LDS, st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W),
+                           static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R), static_cast<float*>(ws),
+                           static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), p.nrb, p.kw,
+                           p.direct ? 1 : 0);
+    } else {
+        hipLaunchKernelGGL(gemm_bf16_skinny_kernel<EPI>, dim3(static_cast<unsigned>(p.nrb) * p.splits),
+                           dim3(SK_THREADS), 0, st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W),
+                           static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R), static_cast<float*>(ws),
+                           static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), p.nrb, p.kw,
+                           p.direct ? 1 : 0);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.direct) return e;
     const int64_t total = M * N;
