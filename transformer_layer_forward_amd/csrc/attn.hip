@@ -1393,6 +1393,7 @@ hipError_t launch_attn_decode(int dtype, const void* qkv, const int64_t* pos, co
 // (reference max, sum, unnormalised o) records that a combine kernel merges.
 constexpr int CHUNK_SPLIT_TARGET = 256;   // workgroups aimed for when splitting keys
 constexpr int CHUNK_SPLIT_MAX = 32;
+static_assert(CHUNK_SPLIT_MAX <= 64, "the combine holds one split per lane");
 
 static int chunk_hpb(int g) { return g % 4 == 0 ? 4 : (g % 2 == 0 ? 2 : 1); }
 
@@ -1421,29 +1422,38 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_split_combine_kernel(const float* __restrict__ part,
                                                                  bf16_t* __restrict__ out, int64_t rows,
                                                                  int nsplit) {
+    static_assert(D % 64 == 0 && D <= 256, "whole dims per lane");
+    constexpr int DPL = D / 64;                 // output dims per lane
     const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const int lane = threadIdx.x & 63;
     constexpr int REC = D + 4;
     const float* pr = part + row * nsplit * REC;
-    float M = -INFINITY;
-    for (int k = lane; k < nsplit; k += 64) M = fmaxf(M, pr[k * REC]);
-    M = wave_max(M);        // finite: key 0 is visible to every query and lies in some split
-    float den = 0.f;
-    for (int k = lane; k < nsplit; k += 64) {
-        const float m = pr[k * REC];
-        if (m > -INFINITY) den += pr[k * REC + 1] * exp2f(m - M);
-    }
-    den = wave_sum(den);
-    const float inv = 1.f / den;
-    for (int dd = lane; dd < D; dd += 64) {
-        float num = 0.f;
-        for (int k = 0; k < nsplit; ++k) {
-            const float m = pr[k * REC];
-            if (m > -INFINITY) num += pr[k * REC + 4 + dd] * exp2f(m - M);
+    // lane k holds split k's weight exp2(m_k - M) / sum_j l_j exp2(m_j - M) (nsplit <= 64)
+    const float mk = lane < nsplit ? pr[lane * REC] : -INFINITY;
+    const float lk = lane < nsplit ? pr[lane * REC + 1] : 0.f;
+    const float M = wave_max(mk);     // finite: key 0 is visible to every query and lies in some split
+    float wk = mk > -INFINITY ? exp2f(mk - M) : 0.f;
+    wk *= 1.f / wave_sum(wk * lk);
+    float acc[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+    const float* po = pr + 4 + lane * DPL;
+#pragma unroll 4
+    for (int k = 0; k < nsplit; ++k) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), k));
+        if (w == 0.f) continue;   // a split that saw no key (uniform branch)
+        if constexpr (DPL == 2) {
+            const f32x2 v = *reinterpret_cast<const f32x2*>(po + k * REC);
+            acc[0] += w * v[0];
+            acc[1] += w * v[1];
+        } else {
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) acc[i] += w * po[k * REC + i];
         }
-        out[row * D + dd] = f2bf(num * inv);
     }
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) out[row * D + lane * DPL + i] = f2bf(acc[i]);
 }
 
 template <int D, int HPB>
