@@ -322,7 +322,6 @@ constexpr int MF_THREADS = 256;                         // 4 waves, one per SIMD
 constexpr int MF_STAGE = (MF_M + MF_N) * MF_K;          // elements per LDS stage (64 KiB)
 constexpr int MF_NSLOT = 2;
 constexpr int MF_LDS_BYTES = MF_NSLOT * MF_STAGE * 2;   // 128 KiB
-constexpr int MF_LPW = 16;                              // 1 KiB direct loads per wave per stage
 
 // physical 16-byte chunk of logical chunk c in an LDS row of 8 chunks (128 bytes)
 __device__ __forceinline__ int mf_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -332,13 +331,21 @@ __device__ __forceinline__ int mf_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); 
 // SPLIT: the workgroup computes one K range (kw columns; blockIdx = tile * splits + range) and writes
 // its fp32 sums to P[range][M][Nw] (gate_up: gate sums at column n, up sums at N + n) for
 // gemm_splitk_reduce_kernel, which applies the epilogue. Few-tile shapes use it to fill the chip.
-template <int EPI, int RD = 0, bool SPLIT = false>
+// TN = 128: the same kernel on a 256 x 128 tile (each wave 128 x 64: 4 x 2 accumulators, 12 loads per
+// wave per stage, 96 KiB of LDS) for shapes with few 256 x 256 tiles; no fused RoPE (a wave's 64
+// columns hold half a head), so RoPE goes through the split partials and the reduce.
+template <int EPI, int RD = 0, bool SPLIT = false, int TN = MF_N>
 __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, const bf16_t* __restrict__ R,
     int M, int N, int K, int tiles_m, int tiles_n, const int64_t* __restrict__ rpos, const float2* __restrict__ rcs,
     int64_t rrows, int rope_cols, int ril, float* __restrict__ P = nullptr, int kw = 0, int splits = 1) {
     static_assert(EPI != EPI_ROPE || RD == 64 || RD == 128, "fused RoPE for head sizes 64 and 128");
     static_assert(!SPLIT || EPI == EPI_STORE || EPI == EPI_SILU, "split partials: plain or gate/up layout");
+    static_assert((TN == 256 || TN == 128) && (TN == 256 || EPI != EPI_ROPE), "tile widths 256 and 128");
+    constexpr int FA = TN / 64;                  // 32-row weight fragments per wave
+    constexpr int STAGE = (MF_M + TN) * MF_K;    // elements per LDS stage
+    constexpr int LPW = 8 + TN / 32;             // direct loads per wave per stage
+    constexpr int PST = 2 * FA;                  // matrix-op pairs per k16 quarter
     extern __shared__ __align__(16) bf16_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
@@ -362,7 +369,7 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     const int in_g = lin - group * GROUP * tiles_n;
     const int tm = first_m + in_g % gsz, tn = in_g / gsz;
     const int m0 = tm * MF_M;
-    constexpr int OUT_T = EPI == EPI_SILU ? MF_N / 2 : MF_N;     // output columns per tile
+    constexpr int OUT_T = EPI == EPI_SILU ? TN / 2 : TN;         // output columns per tile
     const int n0 = tn * OUT_T;
 
     // ---- direct loads: instruction j (0..15) of this wave fills the 128-byte segments of stage rows
@@ -379,10 +386,12 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
         __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(X + static_cast<int64_t>(m0) * K), (short)0, -1, 0x00020000);
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(W + static_cast<int64_t>(n0) * K), (short)0, -1, 0x00020000);
-    uint32_t voff[MF_LPW];
+    // sized for the widest tile: a lambda capturing an array whose size depends on a template
+    // parameter leaves the kernel without its host-side launch stub
+    uint32_t voff[8 + MF_N / 32];
 #pragma unroll
-    for (int j = 0; j < MF_LPW; ++j) {
-        const int r = 32 * (j & 7) + rsub;
+    for (int j = 0; j < LPW; ++j) {
+        const int r = 32 * (j < 8 ? j : j - 8) + rsub;
         int row;
         if (j < 8) {
             row = min(m0 + r, M - 1) - m0;
@@ -396,21 +405,21 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     }
     auto issue1 = [&](int slot, int k0, int j) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            j < 8 ? rx : rw, (__attribute__((address_space(3))) void*)(smem + slot * MF_STAGE + (4 * j + wave) * 8 * MF_K),
+            j < 8 ? rx : rw, (__attribute__((address_space(3))) void*)(smem + slot * STAGE + (4 * j + wave) * 8 * MF_K),
             16, voff[j], k0 * 2, 0, 0);
     };
     // operand fragment offsets within a stage (A: weight rows, B: tokens), one per 32-row block; k16
     // quarter q of a fragment sits at chunk (2q + lh) ^ swizzle = chunk(0) ^ 2q, i.e. offset(0) ^ 16q
-    int aoff[4], boff[4];
+    int aoff[FA], boff[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-        const int ra = wn * 128 + 32 * f + l32, rb = wm * 128 + 32 * f + l32;
-        aoff[f] = (MF_M + ra) * MF_K + ((lh ^ mf_swz(ra)) << 3);
+        const int ra = wn * (TN / 2) + 32 * f + l32, rb = wm * 128 + 32 * f + l32;
+        if (f < FA) aoff[f] = (MF_M + ra) * MF_K + ((lh ^ mf_swz(ra)) << 3);
         boff[f] = rb * MF_K + ((lh ^ mf_swz(rb)) << 3);
     }
-    f32x16 acc[4][4];
+    f32x16 acc[FA][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < FA; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -423,8 +432,8 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     // which keeps the loop free of branches.
     const int nk = SPLIT ? (min(K, kb + kw) - kb) / MF_K : K / MF_K;
 #pragma unroll
-    for (int j = 0; j < MF_LPW; ++j) issue1(0, kb, j);
-    bf16x8 fa[2][4], fb[2][4];
+    for (int j = 0; j < LPW; ++j) issue1(0, kb, j);
+    bf16x8 fa[2][FA], fb[2][4];
 #define MF_MMA2(FA, FB, p)                                                                                   \
     {                                                                                                      \
         const int a_ = (p) >> 1, b_ = ((p) & 1) * 2;                                                       \
@@ -436,26 +445,27 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     for (int t = 0; t < nk; ++t) {
         const int slot = t & 1;
-        const bf16_t* st = smem + slot * MF_STAGE;
+        const bf16_t* st = smem + slot * STAGE;
         const int kn = kb + min(t + 1, nk - 1) * MF_K;
         MF_WAITVM0();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-            fa[0][f] = *reinterpret_cast<const bf16x8*>(st + aoff[f]);
+            if (f < FA) fa[0][f] = *reinterpret_cast<const bf16x8*>(st + aoff[f]);
             fb[0][f] = *reinterpret_cast<const bf16x8*>(st + boff[f]);
         }
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
 #pragma unroll
-            for (int p = 0; p < 8; ++p) {
+            for (int p = 0; p < PST; ++p) {
                 MF_MMA2(fa[h & 1], fb[h & 1], p)
                 if (h < 3 && p < 4) {
-                    fa[(h + 1) & 1][p] = *reinterpret_cast<const bf16x8*>(st + (aoff[p] ^ (16 * (h + 1))));
+                    if (p < FA) fa[(h + 1) & 1][p] = *reinterpret_cast<const bf16x8*>(st + (aoff[p] ^ (16 * (h + 1))));
                     fb[(h + 1) & 1][p] = *reinterpret_cast<const bf16x8*>(st + (boff[p] ^ (16 * (h + 1))));
                 }
-                if (h < 2) issue1(slot ^ 1, kn, 8 * h + p);   // 16 loads over the first two quarters
+                // the next stage's loads over the first quarters (TN = 256: two, TN = 128: three)
+                if (h * PST + p < LPW) issue1(slot ^ 1, kn, h * PST + p);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -471,7 +481,7 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
         // register groups fill whole 128-byte lines (gate_up: 64 bytes of gate and of up sums)
         const int Nw = EPI == EPI_SILU ? 2 * N : N;
         float* pr = P + static_cast<int64_t>(range) * M * Nw;
-        constexpr int OCS = EPI == EPI_SILU ? 64 : 128;
+        constexpr int OCS = EPI == EPI_SILU ? TN / 4 : TN / 2;
         const int nws = n0 + wn * OCS;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -479,7 +489,7 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
             if (m >= M) continue;
             float* prow = pr + static_cast<int64_t>(m) * Nw;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
+            for (int a = 0; a < FA; ++a) {
                 if constexpr (EPI == EPI_SILU) {
 #pragma unroll
                     for (int g = 0; g < 2; ++g) {
@@ -508,9 +518,9 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    constexpr int OC = EPI == EPI_SILU ? 64 : 128;           // output columns of this wave
+    constexpr int OC = EPI == EPI_SILU ? TN / 4 : TN / 2;    // output columns of this wave
     constexpr int GPR = OC / 8;                               // 16-byte chunks per LDS row
-    bf16_t* reg = smem + wave * (128 * 128);                  // 32 KiB per wave
+    bf16_t* reg = smem + wave * (128 * OC);                   // 128 token rows of the wave
     const int mw = m0 + wm * 128;                             // first token of the wave
     const int nw = n0 + wn * OC;                              // first output column of the wave
     auto lds_at = [&](int m, int c) { return reg + m * OC + (((c >> 3) ^ (m & (GPR - 1))) << 3) + (c & 7); };
@@ -564,7 +574,7 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
             }
         }
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
+        for (int a = 0; a < FA; ++a) {
             if constexpr (EPI == EPI_SILU) {
                 // rows 0..15 of block a are gate columns 16a.., rows 16..31 the up columns of the same outputs
 #pragma unroll
@@ -1027,16 +1037,19 @@ static SkinnyPlan skinny_plan(int epi, int64_t N, int64_t K) {
     return p;
 }
 
-// Split-K plan for the 256 x 256 kernel. A shape with fewer tiles than the chip has compute units
-// (256) runs each tile as several K ranges; the count minimises a cost model: the waves of
-// workgroups times one range's MFMA time (MF_STAGE_US per 64-wide stage, as measured on the
-// unsplit kernel) plus the fp32 partials written and read back (MF_PART_BPUS bytes per microsecond)
-// and the reduce launch (MF_REDUCE_US).
+// Plan for the MFMA kernel: tile width (256, or 128 weight rows) and K ranges. A shape with at least as
+// many 256 x 256 tiles as the chip has compute units (256) runs unsplit on 256-wide tiles. Otherwise the
+// plan minimises a cost model over both widths and 1..32 ranges: the waves of workgroups times one
+// range's matrix time (MF_STAGE_US per 64-wide stage of a 256-wide tile, measured on the unsplit
+// kernel; MF_STAGE128_US for the 128-wide tile) plus, with fp32 partials, their bytes written and read
+// back (MF_PART_BPUS bytes per microsecond) and the reduce launch (MF_REDUCE_US). The 128-wide tile
+// writes partials even unsplit when the epilogue is RoPE, which it cannot apply itself.
 struct MfPlan {
-    int splits, kw;
+    int tn, splits, kw;
+    bool partial;   // fp32 partials + reduce kernel
 };
 constexpr int MF_CUS = 256, MF_MAX_SPLITS = 32;
-constexpr double MF_STAGE_US = 1.43, MF_PART_BPUS = 4.0e6, MF_REDUCE_US = 4.0;
+constexpr double MF_STAGE_US = 1.43, MF_STAGE128_US = 1.10, MF_PART_BPUS = 4.0e6, MF_REDUCE_US = 4.0;
 
 static bool mf_usable(int epi, int64_t N, int64_t K, const RopeEpi* re) {
     const int64_t wspan = epi == EPI_SILU ? 2 * N : MF_N;
@@ -1046,20 +1059,24 @@ static bool mf_usable(int epi, int64_t N, int64_t K, const RopeEpi* re) {
 }
 
 static MfPlan mf_plan(int epi, int64_t M, int64_t N, int64_t K) {
-    const int64_t ncols = epi == EPI_SILU ? MF_N / 2 : MF_N;
-    const int64_t T = ((M + MF_M - 1) / MF_M) * ((N + ncols - 1) / ncols);
-    const int64_t nk = K / MF_K, Nw = epi == EPI_SILU ? 2 * N : N;
-    MfPlan best{1, static_cast<int>(K)};
-    if (T >= MF_CUS) return best;
-    double best_t = static_cast<double>((T + MF_CUS - 1) / MF_CUS) * nk * MF_STAGE_US;
-    for (int64_t s = 2; s <= MF_MAX_SPLITS && s <= nk; ++s) {
-        const int64_t per = (nk + s - 1) / s, se = (nk + per - 1) / per;   // stages per range, ranges
-        if (se != s) continue;
-        const double t = static_cast<double>((T * s + MF_CUS - 1) / MF_CUS) * per * MF_STAGE_US +
-                         static_cast<double>(s * M * Nw * 8) / MF_PART_BPUS + MF_REDUCE_US;
-        if (t < best_t) {
-            best_t = t;
-            best = MfPlan{static_cast<int>(s), static_cast<int>(per * MF_K)};
+    const int64_t nk = K / MF_K, Nw = epi == EPI_SILU ? 2 * N : N, tm = (M + MF_M - 1) / MF_M;
+    auto tiles = [&](int tn) { const int64_t nc = epi == EPI_SILU ? tn / 2 : tn; return tm * ((N + nc - 1) / nc); };
+    MfPlan best{MF_N, 1, static_cast<int>(K), false};
+    if (tiles(MF_N) >= MF_CUS) return best;
+    double best_t = static_cast<double>((tiles(MF_N) + MF_CUS - 1) / MF_CUS) * nk * MF_STAGE_US;
+    for (int tn : {MF_N, 128}) {
+        const int64_t T = tiles(tn);
+        const double stage = tn == MF_N ? MF_STAGE_US : MF_STAGE128_US;
+        for (int64_t s = 1; s <= MF_MAX_SPLITS && s <= nk; ++s) {
+            const int64_t per = (nk + s - 1) / s, se = (nk + per - 1) / per;   // stages per range, ranges
+            if (se != s) continue;
+            const bool partial = s > 1 || (tn != MF_N && epi == EPI_ROPE);
+            const double t = static_cast<double>((T * s + MF_CUS - 1) / MF_CUS) * per * stage +
+                             (partial ? static_cast<double>(s * M * Nw * 8) / MF_PART_BPUS + MF_REDUCE_US : 0.0);
+            if (t < best_t) {
+                best_t = t;
+                best = MfPlan{tn, static_cast<int>(s), static_cast<int>(per * MF_K), partial};
+            }
         }
     }
     return best;
@@ -1078,7 +1095,7 @@ size_t gemm_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K, int epi)
     probe.d = 128;
     if (!mf_usable(epi, N, K, &probe)) return 0;
     const MfPlan p = mf_plan(epi, M, N, K);
-    return p.splits > 1 ? static_cast<size_t>(p.splits) * M * Nw * sizeof(float) : 0;
+    return p.partial ? static_cast<size_t>(p.splits) * M * Nw * sizeof(float) : 0;
 }
 
 template <int EPI, bool DIRECT, int RD>
@@ -1106,42 +1123,52 @@ static hipError_t big_launch(const void* X, const void* W, void* C, const void* 
     return big_launch_t<EPI, false, RD>(X, W, C, R, M, N, K, st, re);
 }
 
-template <int EPI, int RD = 0>
+template <int TN>
+constexpr int mf_lds_bytes() { return MF_NSLOT * (MF_M + TN) * MF_K * 2; }
+
+// raise a kernel's dynamic LDS limit (once per instantiation, through a function-scope static)
+template <typename Fn>
+static bool allow_lds(Fn* kernel, int bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               bytes) == hipSuccess;
+}
+
+template <int EPI, int RD = 0, int TN = MF_N>
 static hipError_t mfma32_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N,
                                 int64_t K, hipStream_t st, const RopeEpi* re = nullptr) {
-    static bool attr = [] {
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_mfma32_kernel<EPI, RD>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, MF_LDS_BYTES) == hipSuccess;
-    }();
+    static const bool attr = allow_lds(&gemm_bf16_mfma32_kernel<EPI, RD, false, TN>, mf_lds_bytes<TN>());
     if (!attr) return hipErrorInvalidConfiguration;
-    const int ncols = EPI == EPI_SILU ? MF_N / 2 : MF_N;
+    const int ncols = EPI == EPI_SILU ? TN / 2 : TN;
     const int tm = static_cast<int>((M + MF_M - 1) / MF_M), tn = static_cast<int>((N + ncols - 1) / ncols);
-    hipLaunchKernelGGL((gemm_bf16_mfma32_kernel<EPI, RD>), dim3(tm * tn), dim3(MF_THREADS), MF_LDS_BYTES, st,
-                       static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), static_cast<bf16_t*>(C),
-                       static_cast<const bf16_t*>(R), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tm,
-                       tn, re ? re->pos : nullptr, re ? re->tab.cs : nullptr, re ? re->tab.rows : 1,
-                       re ? re->rope_cols : 0, re ? re->interleaved : 0);
+    hipLaunchKernelGGL((gemm_bf16_mfma32_kernel<EPI, RD, false, TN>), dim3(tm * tn), dim3(MF_THREADS),
+                       mf_lds_bytes<TN>(), st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W),
+                       static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R), static_cast<int>(M), static_cast<int>(N),
+                       static_cast<int>(K), tm, tn, re ? re->pos : nullptr, re ? re->tab.cs : nullptr,
+                       re ? re->tab.rows : 1, re ? re->rope_cols : 0, re ? re->interleaved : 0);
     return hipGetLastError();
 }
 
-// K ranges of the 256 x 256 kernel into fp32 partials, then the reduce applies the epilogue
-template <int EPI>
-static hipError_t mfma32_split_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N,
-                                      int64_t K, const MfPlan& p, void* ws, hipStream_t st,
-                                      const RopeEpi* re = nullptr) {
-    constexpr int PE = EPI == EPI_SILU ? EPI_SILU : EPI_STORE;   // partial layout
-    static bool attr = [] {
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_mfma32_kernel<PE, 0, true>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, MF_LDS_BYTES) == hipSuccess;
-    }();
+// K ranges of the MFMA kernel into fp32 partials (PE: plain layout, or gate/up apart for silu·up)
+template <int PE, int TN>
+static hipError_t mfma32_partials_launch(const void* X, const void* W, int64_t M, int64_t N, int64_t K,
+                                         const MfPlan& p, void* ws, hipStream_t st) {
+    static const bool attr = allow_lds(&gemm_bf16_mfma32_kernel<PE, 0, true, TN>, mf_lds_bytes<TN>());
     if (!attr) return hipErrorInvalidConfiguration;
-    const int ncols = EPI == EPI_SILU ? MF_N / 2 : MF_N;
+    const int ncols = PE == EPI_SILU ? TN / 2 : TN;
     const int tm = static_cast<int>((M + MF_M - 1) / MF_M), tn = static_cast<int>((N + ncols - 1) / ncols);
-    hipLaunchKernelGGL((gemm_bf16_mfma32_kernel<PE, 0, true>), dim3(tm * tn * p.splits), dim3(MF_THREADS),
-                       MF_LDS_BYTES, st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), nullptr,
+    hipLaunchKernelGGL((gemm_bf16_mfma32_kernel<PE, 0, true, TN>), dim3(tm * tn * p.splits), dim3(MF_THREADS),
+                       mf_lds_bytes<TN>(), st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W), nullptr,
                        nullptr, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tm, tn, nullptr,
                        nullptr, int64_t(1), 0, 0, static_cast<float*>(ws), p.kw, p.splits);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+// partials, then the reduce sums the ranges and applies the epilogue
+template <int EPI, int TN>
+static hipError_t mfma32_split_launch_t(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N,
+                                        int64_t K, const MfPlan& p, void* ws, hipStream_t st, const RopeEpi* re) {
+    constexpr int PE = EPI == EPI_SILU ? EPI_SILU : EPI_STORE;
+    hipError_t e = mfma32_partials_launch<PE, TN>(X, W, M, N, K, p, ws, st);
     if (e != hipSuccess) return e;
     const int64_t total = M * N, Nw = EPI == EPI_SILU ? 2 * N : N;
     hipLaunchKernelGGL(gemm_splitk_reduce_kernel<EPI>, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
@@ -1150,6 +1177,14 @@ static hipError_t mfma32_split_launch(const void* X, const void* W, void* C, con
                        re ? re->pos : nullptr, re ? re->tab.cs : nullptr, re ? re->tab.rows : 1,
                        re ? re->rope_cols : 0, re ? re->d : 2, re ? re->interleaved : 0);
     return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t mfma32_split_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N,
+                                      int64_t K, const MfPlan& p, void* ws, hipStream_t st,
+                                      const RopeEpi* re = nullptr) {
+    if (p.tn == MF_N) return mfma32_split_launch_t<EPI, MF_N>(X, W, C, R, M, N, K, p, ws, st, re);
+    return mfma32_split_launch_t<EPI, 128>(X, W, C, R, M, N, K, p, ws, st, re);
 }
 
 template <int EPI>
@@ -1227,13 +1262,21 @@ hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C
     if (mf_usable(epi, N, K, re)) {
         const MfPlan p = mf_plan(epi, M, N, K);
         const size_t need = static_cast<size_t>(p.splits) * M * (epi == EPI_SILU ? 2 * N : N) * sizeof(float);
-        if (p.splits > 1) {
+        if (p.partial) {
             if (ws_bytes < need || !ws) return hipErrorInvalidValue;
             switch (epi) {
                 case EPI_STORE: return mfma32_split_launch<EPI_STORE>(X, W, C, R, M, N, K, p, ws, st);
                 case EPI_RESIDUAL: return mfma32_split_launch<EPI_RESIDUAL>(X, W, C, R, M, N, K, p, ws, st);
                 case EPI_ROPE: return mfma32_split_launch<EPI_ROPE>(X, W, C, R, M, N, K, p, ws, st, re);
                 default: return mfma32_split_launch<EPI_SILU>(X, W, C, R, M, N, K, p, ws, st);
+            }
+        }
+        if (p.tn != MF_N) {   // 128-wide tiles, whole K, epilogue in the kernel (never RoPE: see the plan)
+            switch (epi) {
+                case EPI_STORE: return mfma32_launch<EPI_STORE, 0, 128>(X, W, C, R, M, N, K, st);
+                case EPI_RESIDUAL: return mfma32_launch<EPI_RESIDUAL, 0, 128>(X, W, C, R, M, N, K, st);
+                case EPI_SILU: return mfma32_launch<EPI_SILU, 0, 128>(X, W, C, R, M, N, K, st);
+                default: return hipErrorInvalidValue;
             }
         }
         switch (epi) {
