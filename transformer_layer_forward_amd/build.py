@@ -1,6 +1,6 @@
 """Build the gfx950 HIP library ``libllama_layer.so`` in-tree with hipcc.
 
-Every call recompiles all sources (the build check must not trust a stale library).
+Every call recompiles all sources, so a stale library is never reused.
 Usage: python -m transformer_layer_forward_amd.build
 """
 from __future__ import annotations

@@ -1225,12 +1225,20 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(const float* __
         if (live(k)) den += pr[k * rec + 1] * exp2f(pr[k * rec] - M);
     den = wave_sum(den);
     const float inv = 1.f / den;
-    for (int dd = lane; dd < d; dd += 64) {
-        float num = 0.f;
-        for (int k = 0; k < nsplit; ++k)
-            if (live(k)) num += pr[k * rec + 2 + dd] * exp2f(pr[k * rec] - M);
-        stf<T>(out + static_cast<int64_t>(bh) * d + dd, num * inv);
+    // splits outer: one weight per split, the lane's dims lane, lane + 64, ... (d <= 256) in registers
+    float num[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int k = 0; k < nsplit; ++k) {
+        if (!live(k)) continue;   // uniform
+        const float w = exp2f(pr[k * rec] - M);
+        const float* po = pr + k * rec + 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (lane + 64 * i < d) num[i] += w * po[lane + 64 * i];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i < d) stf<T>(out + static_cast<int64_t>(bh) * d + lane + 64 * i, num[i] * inv);
 }
 
 // ------------------------------------------------------------------ dispatch
