@@ -954,6 +954,80 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __
     C[idx] = f2bf(s);
 }
 
+// The same reduce four columns per thread (N % 4 == 0): 16-byte partial loads. A RoPE partner quad is
+// the quad d/2 columns away (half-split; d % 8 == 0 keeps a quad inside one half) or the quad itself
+// (interleaved pairs (2j, 2j+1)).
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce4_kernel(const float* __restrict__ P, bf16_t* __restrict__ C,
+                                                                  const bf16_t* __restrict__ R, int M, int N, int Nw,
+                                                                  int splits, const int64_t* __restrict__ rpos,
+                                                                  const float2* __restrict__ rcs, int64_t rrows,
+                                                                  int rope_cols, int rd, int ril) {
+    const int64_t nq = N / 4;
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (q >= static_cast<int64_t>(M) * nq) return;
+    const int m = static_cast<int>(q / nq), n = static_cast<int>(q - static_cast<int64_t>(m) * nq) * 4;
+    const bool rot = EPI == EPI_ROPE && n < rope_cols;
+    const int j = n % rd;
+    const int pn = ril ? n : (j < rd / 2 ? n + rd / 2 : n - rd / 2);
+    f32x4 s = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < splits; ++k) {
+        const float* prow = P + (static_cast<int64_t>(k) * M + m) * Nw;
+        s += *reinterpret_cast<const f32x4*>(prow + n);
+        if (EPI == EPI_SILU) u += *reinterpret_cast<const f32x4*>(prow + N + n);
+        if (EPI == EPI_ROPE && rot && !ril) y += *reinterpret_cast<const f32x4*>(prow + pn);
+    }
+    float v[4] = {s[0], s[1], s[2], s[3]};
+    if (EPI == EPI_ROPE && rot) {
+        const float2* cs = rcs + clamp_pos(rpos[m], rrows) * (rd / 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ji = j + i;
+            if (ril) {
+                const float2 c = cs[ji >> 1];
+                v[i] = s[i] * c.x + ((ji & 1) ? 1.f : -1.f) * s[i ^ 1] * c.y;
+            } else {
+                const float2 c = cs[ji < rd / 2 ? ji : ji - rd / 2];
+                v[i] = s[i] * c.x + (ji < rd / 2 ? -1.f : 1.f) * y[i] * c.y;
+            }
+        }
+    }
+    if (EPI == EPI_SILU) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = v[i] / (1.f + __expf(-v[i])) * u[i];
+    }
+    const int64_t o = static_cast<int64_t>(m) * N + n;
+    if (EPI == EPI_RESIDUAL) {
+        const uint2 rr = *reinterpret_cast<const uint2*>(R + o);
+        v[0] += __uint_as_float(rr.x << 16); v[1] += __uint_as_float(rr.x & 0xffff0000u);
+        v[2] += __uint_as_float(rr.y << 16); v[3] += __uint_as_float(rr.y & 0xffff0000u);
+    }
+    *reinterpret_cast<uint2*>(C + o) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+
+// sum the ranges and apply the epilogue: the quad kernel when N % 4 == 0 (and, for RoPE, d % 8 == 0)
+template <int EPI>
+static hipError_t splitk_reduce_launch(const float* P, void* C, const void* R, int64_t M, int64_t N, int64_t Nw,
+                                       int splits, const RopeEpi* re, hipStream_t st) {
+    const bool quad = N % 4 == 0 && (EPI != EPI_ROPE || (re && re->d % 8 == 0 && re->rope_cols % 4 == 0));
+    if (quad) {
+        const int64_t total = M * (N / 4);
+        hipLaunchKernelGGL(gemm_splitk_reduce4_kernel<EPI>, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256),
+                           0, st, P, static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R), static_cast<int>(M),
+                           static_cast<int>(N), static_cast<int>(Nw), splits, re ? re->pos : nullptr,
+                           re ? re->tab.cs : nullptr, re ? re->tab.rows : 1, re ? re->rope_cols : 0,
+                           re ? re->d : 2, re ? re->interleaved : 0);
+    } else {
+        const int64_t total = M * N;
+        hipLaunchKernelGGL(gemm_splitk_reduce_kernel<EPI>, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256),
+                           0, st, P, static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R), static_cast<int>(M),
+                           static_cast<int>(N), static_cast<int>(Nw), splits, re ? re->pos : nullptr,
+                           re ? re->tab.cs : nullptr, re ? re->tab.rows : 1, re ? re->rope_cols : 0,
+                           re ? re->d : 2, re ? re->interleaved : 0);
+    }
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ fp32
 constexpr int GF_T = 32, GF_K = 16;
 
@@ -1170,13 +1244,8 @@ static hipError_t mfma32_split_launch_t(const void* X, const void* W, void* C, c
     constexpr int PE = EPI == EPI_SILU ? EPI_SILU : EPI_STORE;
     hipError_t e = mfma32_partials_launch<PE, TN>(X, W, M, N, K, p, ws, st);
     if (e != hipSuccess) return e;
-    const int64_t total = M * N, Nw = EPI == EPI_SILU ? 2 * N : N;
-    hipLaunchKernelGGL(gemm_splitk_reduce_kernel<EPI>, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
-                       st, static_cast<const float*>(ws), static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R),
-                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(Nw), p.splits,
-                       re ? re->pos : nullptr, re ? re->tab.cs : nullptr, re ? re->tab.rows : 1,
-                       re ? re->rope_cols : 0, re ? re->d : 2, re ? re->interleaved : 0);
-    return hipGetLastError();
+    const int64_t Nw = EPI == EPI_SILU ? 2 * N : N;
+    return splitk_reduce_launch<EPI>(static_cast<const float*>(ws), C, R, M, N, Nw, p.splits, re, st);
 }
 
 template <int EPI>
@@ -1212,13 +1281,7 @@ static hipError_t skinny_launch(const void* X, const void* W, void* C, const voi
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.direct) return e;
-    const int64_t total = M * N;
-    hipLaunchKernelGGL(gemm_splitk_reduce_kernel<EPI>, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
-                       st, static_cast<const float*>(ws), static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R),
-                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(Nw), p.splits,
-                       re ? re->pos : nullptr, re ? re->tab.cs : nullptr, re ? re->tab.rows : 1,
-                       re ? re->rope_cols : 0, re ? re->d : 2, re ? re->interleaved : 0);
-    return hipGetLastError();
+    return splitk_reduce_launch<EPI>(static_cast<const float*>(ws), C, R, M, N, Nw, p.splits, re, st);
 }
 
 template <int EPI>
