@@ -107,6 +107,31 @@ def test_swiglu_mlp(dtype, M, H, I, with_residual):
         assert ref.max_rel_err(got, want) <= tol(dtype)
 
 
+@pytest.mark.parametrize("with_residual", [False, True])
+def test_swiglu_mlp_wide_tiles_sampled_rows(with_residual):
+    """M = 2048, hidden = intermediate = 4096: the down projection has 128 tiles of 256 x 256, so it runs
+    unsplit on 256 x 128 tiles with its epilogue (residual or plain store) in the kernel. The oracle is
+    evaluated on 16 sampled rows (first, last and 14 seeded)."""
+    require_gpu()
+    dtype, M, H, I = "bf16", 2048, 4096, 4096
+    x = normal(5, 140, (M, H), dtype)
+    wgu = normal(5, 141, (2 * I, H), dtype, std=0.02)
+    wd = normal(5, 142, (H, I), dtype, std=0.02)
+    r = normal(5, 143, (M, H), dtype)
+    res = to_dev(r, dtype) if with_residual else None
+    out = L.swiglu_mlp(to_dev(x, dtype), to_dev(wgu, dtype), to_dev(wd, dtype), residual=res)
+    rows = sorted({0, M - 1, *np.random.default_rng([7, 140]).integers(0, M, 14).tolist()})
+    want = ref.linear(ref.swiglu_act(bits_to_f64(x, dtype)[rows], bits_to_f64(wgu, dtype), I), bits_to_f64(wd, dtype))
+    got = to_f64(out)[rows]
+    if with_residual:
+        rr = bits_to_f64(r, dtype)[rows]
+        assert ref.max_rel_err(got, want + rr) <= tol(dtype)
+        bound = tol(dtype) * np.max(np.abs(want)) + 2.0 ** -8 * np.max(np.abs(got))
+        assert np.max(np.abs(got - rr - want)) <= bound
+    else:
+        assert ref.max_rel_err(got, want) <= tol(dtype)
+
+
 # ------------------------------------------------------------------ prefill attention
 PREFILL = [
     # dtype, B, S, nh, nkv, d
