@@ -316,12 +316,12 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_big_kernel(
 // global->LDS loads (full 128-byte row segments); operand fragments are double-buffered in
 // registers across the four k16 quarters of a stage, and the loads of the next stage are spread
 // over the first two quarters. The epilogue stages each wave's results through LDS and writes whole
-// output rows. Used when K % 64 == 0 and N % 8 == 0, for every epilogue but the fused RoPE.
+// output rows (RoPE rotated in fp32 first, for head sizes 64 and 128). Used when K % 64 == 0 and
+// N % 8 == 0 and the operands fit 32-bit byte offsets; shapes with few tiles use the split / 128-wide
+// forms below.
 constexpr int MF_M = 256, MF_N = 256, MF_K = 64;
 constexpr int MF_THREADS = 256;                         // 4 waves, one per SIMD, 128 x 128 each
-constexpr int MF_STAGE = (MF_M + MF_N) * MF_K;          // elements per LDS stage (64 KiB)
 constexpr int MF_NSLOT = 2;
-constexpr int MF_LDS_BYTES = MF_NSLOT * MF_STAGE * 2;   // 128 KiB
 
 // physical 16-byte chunk of logical chunk c in an LDS row of 8 chunks (128 bytes)
 __device__ __forceinline__ int mf_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
