@@ -169,3 +169,27 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "numpy" not in text or f == "build.py", f
+
+
+def test_workspace_sizes_follow_the_projection_plans():
+    """Host-only sizing: a projection with few output tiles splits K and needs fp32 partials beyond the
+    activation buffer; one with enough tiles needs none; the key-split area of chunked attention
+    appears only when the caller passes the cache length."""
+    lib = _lib.load()
+
+    def act(m, i):
+        return (m * i * 2 + 255) // 256 * 256
+
+    # M = 256 tokens, Llama-3-8B MLP: down (N = 4096, K = 14336) has 16 tiles of 256 x 256 -> partials
+    few = lib.swiglu_mlp_workspace_bytes(256, 4096, 14336, 1)
+    assert few > act(256, 14336)
+    # M = 8192: every projection has >= 256 tiles -> the activation buffer alone
+    assert lib.swiglu_mlp_workspace_bytes(8192, 4096, 14336, 1) == act(8192, 14336)
+    # decode-sized M = 64: the down projection streams its weights in K ranges -> partials
+    assert lib.swiglu_mlp_workspace_bytes(64, 4096, 14336, 1) > act(64, 14336)
+    # fp32 runs its own kernel, no partials
+    assert lib.swiglu_mlp_workspace_bytes(256, 4096, 14336, 0) == (256 * 14336 * 4 + 255) // 256 * 256
+    cfg = L.LayerConfig(4096, 32, 8, 128, 14336, 1e-5, L.Rope(), torch.bfloat16).to_c()
+    no_cache = lib.llama_layer_workspace_bytes(ctypes.byref(cfg), 1, 256, 0)
+    with_cache = lib.llama_layer_workspace_bytes(ctypes.byref(cfg), 1, 256, 8192)
+    assert with_cache > no_cache > 0
