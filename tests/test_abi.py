@@ -150,6 +150,11 @@ def test_kernel_entry_point_errors():
                           None) == _lib.LL_EUNSUPPORTED
     # out aliasing x is rejected
     assert lib.swiglu_mlp(FAKE, FAKE, FAKE, None, FAKE, 8, 64, 128, _lib.LL_BF16, FAKE, mneed, None) == _lib.LL_EINVAL
+    # a workspace off 16-byte alignment is rejected (the projections use 16-byte vector accesses on it)
+    other = ctypes.c_void_p(FAKE.value + 4096)
+    assert lib.swiglu_mlp(FAKE, FAKE, FAKE, None, other, 8, 64, 128, _lib.LL_BF16,
+                          ctypes.c_void_p(FAKE.value + 8192 + 8), mneed, None) == _lib.LL_EINVAL
+    assert "aligned" in _lib.last_error()
 
 
 def test_profile_stage_names():

@@ -518,6 +518,7 @@ ll_status swiglu_mlp(const void* x, const void* w_gate_up, const void* w_down, c
         return fail(LL_EINVAL, "pointers must be 16-byte aligned");
     const size_t need = swiglu_mlp_workspace_bytes(M, hidden, intermediate, dtype);
     if (workspace_bytes < need || !workspace) return fail(LL_EINVAL, "workspace too small: %zu < %zu", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(LL_EINVAL, "workspace must be 16-byte aligned");
     char* ws = static_cast<char*>(workspace);
     void* act = ws;
     void* gws = ws + round_up(static_cast<size_t>(M * intermediate) * elem_size(dtype));
