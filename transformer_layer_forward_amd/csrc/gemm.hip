@@ -781,16 +781,23 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_bf16_skinny_kernel(
 // them by the 64 tokens with v_mfma_f32_16x16x32_bf16. Single range: epilogue in the kernel (gate_up:
 // the up waves hand their sums to the gate waves through LDS); several ranges: fp32 partials for
 // gemm_splitk_reduce_kernel.
-constexpr int SR_R = 128, SR_KS = 128, SR_NST = 3, SR_THREADS = 512;
-constexpr int SR_WST = SR_R * SR_KS, SR_XST = 64 * SR_KS, SR_STAGE = SR_WST + SR_XST;   // elements
-constexpr int SR_LDS = SR_NST * SR_STAGE * 2;                                              // 144 KiB
-#define SR_WAIT_VM6() __builtin_amdgcn_s_waitcnt(0x0F76)   // vmcnt(6): one stage (6 loads) may stay out
+// NW = 4 is the same with 64 weight rows per workgroup (4 waves; each loads 4 KiB of weights and 4 KiB
+// of activations per stage): twice the row blocks for the smaller projections, so they fill the chip
+// with fewer, longer K ranges.
+constexpr int SR_KS = 128, SR_NST = 3, SR_XST = 64 * SR_KS;
+template <int NW>
+constexpr int sr_lds_bytes() { return SR_NST * (16 * NW * SR_KS + SR_XST) * 2; }   // 144 / 96 KiB
 #define SR_WAIT_VM0() __builtin_amdgcn_s_waitcnt(0x0F70)
 
-template <int EPI>
-__global__ __launch_bounds__(SR_THREADS, 1) void gemm_bf16_skinny_ring_kernel(
+template <int EPI, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_skinny_ring_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, const bf16_t* __restrict__ R,
     float* __restrict__ P, int M, int N, int K, int nrb, int kw, int direct) {
+    static_assert(NW == 8 || NW == 4, "8 or 4 waves");
+    constexpr int SR_R = 16 * NW;                        // weight rows per workgroup
+    constexpr int SR_WST = SR_R * SR_KS, SR_STAGE = SR_WST + SR_XST;
+    constexpr int XL = 16 / NW;                          // activation loads per wave per stage
+    constexpr int HALF = SR_R / 2;                       // gate_up: gate rows, then their up rows
     extern __shared__ __align__(16) bf16_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -799,9 +806,9 @@ __global__ __launch_bounds__(SR_THREADS, 1) void gemm_bf16_skinny_ring_kernel(
     const int kbeg = kc * kw, kend = min(K, kbeg + kw);
     const int nst = (kend - kbeg) / SR_KS;
     // weight row of tile row r (clamped to a valid row; results of clamped rows are never stored)
-    const int wbase = EPI == EPI_SILU ? rb * 64 : rb * SR_R;
+    const int wbase = EPI == EPI_SILU ? rb * HALF : rb * SR_R;
     auto wrow_of = [&](int r) {
-        if (EPI == EPI_SILU) return r < 64 ? min(wbase + r, N - 1) : N + min(wbase + r - 64, N - 1);
+        if (EPI == EPI_SILU) return r < HALF ? min(wbase + r, N - 1) : N + min(wbase + r - HALF, N - 1);
         return min(wbase + r, N - 1);
     };
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -810,7 +817,7 @@ __global__ __launch_bounds__(SR_THREADS, 1) void gemm_bf16_skinny_ring_kernel(
     // W load j (0..3) of this wave fills KiB 4*wave + j of a stage's weight block, X load j (0..1) KiB
     // 2*wave + j of its activation block; lane l lands in row 4*KiB + l/16 at physical 16-byte chunk
     // l%16 and fetches the logical chunk that the row's XOR swizzle (chunk ^ row%16) puts there
-    uint32_t wo[4], xo[2];
+    uint32_t wo[4], xo[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = (4 * wave + j) * 4 + (lane >> 4);
@@ -818,8 +825,8 @@ __global__ __launch_bounds__(SR_THREADS, 1) void gemm_bf16_skinny_ring_kernel(
         wo[j] = static_cast<uint32_t>(wrow_of(r) - wbase) * static_cast<uint32_t>(K) * 2u + c * 16u;
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int m = (2 * wave + j) * 4 + (lane >> 4);
+    for (int j = 0; j < XL; ++j) {
+        const int m = (XL * wave + j) * 4 + (lane >> 4);
         const int c = (lane & 15) ^ (m & 15);
         xo[j] = static_cast<uint32_t>(min(m, M - 1)) * static_cast<uint32_t>(K) * 2u + c * 16u;
     }
@@ -835,9 +842,9 @@ __global__ __launch_bounds__(SR_THREADS, 1) void gemm_bf16_skinny_ring_kernel(
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rw, (__attribute__((address_space(3))) void*)(base + (4 * wave + j) * 512), 16, wo[j], k0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < XL; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (__attribute__((address_space(3))) void*)(base + SR_WST + (2 * wave + j) * 512), 16, xo[j], k0, 0, 0);
+                rx, (__attribute__((address_space(3))) void*)(base + SR_WST + (XL * wave + j) * 512), 16, xo[j], k0, 0, 0);
     };
     f32x4 acc[4];
 #pragma unroll
@@ -848,8 +855,12 @@ __global__ __launch_bounds__(SR_THREADS, 1) void gemm_bf16_skinny_ring_kernel(
     for (int t = 0; t < nst; ++t) {
         // this wave's loads of stage t have landed; after the barrier every wave's have, and every wave
         // is done with stage t - 1, whose slot receives stage t + 2
-        if (t + 1 < nst) SR_WAIT_VM6();
-        else SR_WAIT_VM0();
+        if (t + 1 < nst) {
+            if constexpr (NW == 8) __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6): next stage's 6 loads out
+            else __builtin_amdgcn_s_waitcnt(0x0F78);                      // vmcnt(8)
+        } else {
+            SR_WAIT_VM0();
+        }
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         if (t + 2 < nst) issue(t + 2, (t + 2) % SR_NST);
@@ -868,11 +879,11 @@ __global__ __launch_bounds__(SR_THREADS, 1) void gemm_bf16_skinny_ring_kernel(
         }
     }
     // lane holds acc[b][r] = sum for token 16b + lrow and output column col0 + 4*lgrp + r
-    const int col0 = EPI == EPI_SILU ? wbase + 16 * (wave & 3) : wbase + 16 * wave;
+    const int col0 = EPI == EPI_SILU ? wbase + 16 * (wave % (NW / 2)) : wbase + 16 * wave;
     const int n = col0 + 4 * lgrp;
     if (!direct) {
         const int64_t Nw = EPI == EPI_SILU ? 2 * static_cast<int64_t>(N) : N;
-        const int wrow0 = EPI == EPI_SILU && wave >= 4 ? N : 0;
+        const int wrow0 = EPI == EPI_SILU && wave >= NW / 2 ? N : 0;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int m = 16 * b + lrow;
@@ -884,12 +895,12 @@ __global__ __launch_bounds__(SR_THREADS, 1) void gemm_bf16_skinny_ring_kernel(
     if (EPI == EPI_SILU) {
         __syncthreads();   // every wave is past its last LDS read
         f32x4* sU = reinterpret_cast<f32x4*>(smem);
-        if (wave >= 4) {
+        if (wave >= NW / 2) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) sU[((wave - 4) * 4 + b) * 64 + lane] = acc[b];
+            for (int b = 0; b < 4; ++b) sU[((wave - NW / 2) * 4 + b) * 64 + lane] = acc[b];
         }
         __syncthreads();
-        if (wave >= 4) return;
+        if (wave >= NW / 2) return;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const f32x4 u = sU[(wave * 4 + b) * 64 + lane];
@@ -911,7 +922,6 @@ __global__ __launch_bounds__(SR_THREADS, 1) void gemm_bf16_skinny_ring_kernel(
         *reinterpret_cast<uint2*>(C + o) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
 }
-#undef SR_WAIT_VM6
 #undef SR_WAIT_VM0
 
 // Sum split partials P[splits][M][Nw] and apply the epilogue; N = output columns.
@@ -1087,15 +1097,20 @@ static bool use_skinny(int64_t M) { return M <= SK_MAXM; }
 // single range applies the epilogue in the kernel, except RoPE, whose rotation partner lives in
 // another wave.
 struct SkinnyPlan {
-    int nrb, splits, kw;
+    int nrb, splits, kw, nw;
     bool direct, ring;
 };
 
 static SkinnyPlan skinny_plan(int epi, int64_t N, int64_t K) {
     SkinnyPlan p;
-    const int64_t wspan = epi == EPI_SILU ? 2 * N : SR_R;   // weight rows one descriptor spans
+    const int64_t wspan = epi == EPI_SILU ? 2 * N : 128;   // weight rows one descriptor spans
     p.ring = K % SR_KS == 0 && N % 8 == 0 && wspan * K * 2 < (int64_t(1) << 32) && 64 * K * 2 < (int64_t(1) << 32);
     p.nrb = static_cast<int>(epi == EPI_SILU ? (N + 63) / 64 : (N + 127) / 128);
+    p.nw = 8;
+    if (p.ring && epi != EPI_SILU && p.nrb < 128) {   // 64-row workgroups for the smaller projections
+        p.nw = 4;
+        p.nrb = static_cast<int>((N + 63) / 64);
+    }
     if (p.ring) {
         const int64_t nks = K / SR_KS;
         const int64_t s = std::max<int64_t>(1, std::min<int64_t>({8, SK_WG_TARGET / p.nrb, nks / 8}));
@@ -1256,22 +1271,28 @@ static hipError_t mfma32_split_launch(const void* X, const void* W, void* C, con
     return mfma32_split_launch_t<EPI, 128>(X, W, C, R, M, N, K, p, ws, st, re);
 }
 
+template <int EPI, int NW>
+static hipError_t skinny_ring_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N,
+                                     int64_t K, const SkinnyPlan& p, void* ws, hipStream_t st) {
+    static const bool attr = allow_lds(&gemm_bf16_skinny_ring_kernel<EPI, NW>, sr_lds_bytes<NW>());
+    if (!attr) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((gemm_bf16_skinny_ring_kernel<EPI, NW>), dim3(static_cast<unsigned>(p.nrb) * p.splits),
+                       dim3(64 * NW), sr_lds_bytes<NW>(), st, static_cast<const bf16_t*>(X),
+                       static_cast<const bf16_t*>(W), static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R),
+                       static_cast<float*>(ws), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), p.nrb,
+                       p.kw, p.direct ? 1 : 0);
+    return hipGetLastError();
+}
+
 template <int EPI>
 static hipError_t skinny_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N, int64_t K,
                                 void* ws, hipStream_t st, const RopeEpi* re = nullptr) {
     const SkinnyPlan p = skinny_plan(EPI, N, K);
     const int64_t Nw = EPI == EPI_SILU ? 2 * N : N;
     if (p.ring) {
-        static bool attr = [] {
-            return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_skinny_ring_kernel<EPI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, SR_LDS) == hipSuccess;
-        }();
-        if (!attr) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(gemm_bf16_skinny_ring_kernel<EPI>, dim3(static_cast<unsigned>(p.nrb) * p.splits),
-                           dim3(SR_THREADS), SR_LDS, st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W),
-                           static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R), static_cast<float*>(ws),
-                           static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), p.nrb, p.kw,
-                           p.direct ? 1 : 0);
+        hipError_t el = p.nw == 8 ? skinny_ring_launch<EPI, 8>(X, W, C, R, M, N, K, p, ws, st)
+                                  : skinny_ring_launch<EPI, 4>(X, W, C, R, M, N, K, p, ws, st);
+        if (el != hipSuccess) return el;
     } else {
         hipLaunchKernelGGL(gemm_bf16_skinny_kernel<EPI>, dim3(static_cast<unsigned>(p.nrb) * p.splits),
                            dim3(SK_THREADS), 0, st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W),
