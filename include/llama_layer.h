@@ -86,8 +86,9 @@ typedef struct {
     const void* g_mlp;         /* [H] gain of the second RMSNorm */
 } ll_layer_weights;
 
-/* Bytes of device workspace llama_layer_forward needs for B sequences of S tokens; ctx is the
- * cache length that will be passed (0 without caches; it only matters for decode, S == 1).
+/* Bytes of device workspace llama_layer_forward (and _chunk, _varlen) needs for B sequences of S tokens;
+ * ctx is the cache length that will be passed (0 without caches). It matters for decode (S == 1: the
+ * per-split attention records) and for chunked prefill (room for a small chunk's key-split records).
  * Returns 0 for invalid arguments. */
 size_t llama_layer_workspace_bytes(const ll_layer_cfg* cfg, int64_t B, int64_t S, int64_t ctx);
 
@@ -118,8 +119,10 @@ ll_status llama_layer_forward(const ll_layer_cfg* cfg, const ll_layer_weights* w
  * and V of token (b, s) are stored at slot position_ids[b, s]; then query (b, s) attends over cache
  * slots 0 .. position_ids[b, s] (slots not written by this call are used as stored, i.e. the prefix
  * written by earlier calls). With position_ids[b, s] = s it equals llama_layer_forward with caches.
- * Positions of one sequence must be distinct and in [0, ctx). Workspace as llama_layer_workspace_bytes
- * for (B, S) with ctx = 0. */
+ * Positions of one sequence must be distinct and in [0, ctx). Workspace: at least
+ * llama_layer_workspace_bytes(cfg, B, S, 0); sized with the call's ctx instead, it also holds the
+ * records that let a small chunk share each query block's keys out over several workgroups (same
+ * results up to rounding, much faster for short chunks on long prefixes). */
 ll_status llama_layer_forward_chunk(const ll_layer_cfg* cfg, const ll_layer_weights* w,
                                     const void* hidden, const int64_t* position_ids,
                                     int64_t B, int64_t S, int64_t kv_seq_len,
