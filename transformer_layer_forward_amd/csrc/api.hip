@@ -623,6 +623,16 @@ static ll_status layer_forward_impl(const ll_layer_cfg* cfg, const ll_layer_weig
     re.rope_cols = static_cast<int>((s.nh + s.nkv) * s.d);
     re.d = static_cast<int>(s.d);
     re.interleaved = cfg->rope.interleaved;
+    // decode: the QKV reduce also appends the new keys and values (no separate store pass)
+    const bool appended = decode && gemm_rope_fusable(dt, s.M, re.d) &&
+                          gemm_rope_appends_cache(dt, s.M, s.qkvd, s.H, re.d, re.rope_cols);
+    if (appended) {
+        re.kc = k_cache;
+        re.vc = v_cache;
+        re.ctx = ctx;
+        re.nh = static_cast<int>(s.nh);
+        re.nkv = static_cast<int>(s.nkv);
+    }
     if (gemm_rope_fusable(dt, s.M, re.d)) {
         e = launch_gemm(dt, EPI_ROPE, xn, w->w_qkv, qkv, nullptr, s.M, s.qkvd, s.H, gws, gbytes, stream_h, &re);
         if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
@@ -647,7 +657,7 @@ static ll_status layer_forward_impl(const ll_layer_cfg* cfg, const ll_layer_weig
     } else if (decode) {
         e = launch_attn_decode(dt, qkv, position_ids, nullptr, 0, k_cache, v_cache, ctx, o, static_cast<int>(B),
                                static_cast<int>(s.nh), static_cast<int>(s.nkv), static_cast<int>(s.d), dws, dbytes,
-                               stream_h);
+                               stream_h, appended);
     } else {
         e = launch_attn_prefill(dt, qkv, position_ids, nullptr, 0, o, k_cache, v_cache, ctx, static_cast<int>(B),
                                 static_cast<int>(S), static_cast<int>(s.nh), static_cast<int>(s.nkv),

@@ -1361,20 +1361,23 @@ static hipError_t decode_g_sel(const void* qkv, const int64_t* pos, const RopeTa
 
 hipError_t launch_attn_decode(int dtype, const void* qkv, const int64_t* pos, const RopeTab* tab, int il, void* kc,
                               void* vc, int64_t ctx, void* o, int B, int nh, int nkv, int d, void* ws,
-                              size_t ws_bytes, hipStream_t st) {
+                              size_t ws_bytes, hipStream_t st, bool appended) {
     if (B == 0) return hipSuccess;
     const float2* cs = tab ? tab->cs : nullptr;
     const int64_t rows = tab ? tab->rows : 1;
-    // 1) append the new (rotated) key and value at slot pos[b]
-    const unsigned kb = static_cast<unsigned>((static_cast<int64_t>(B) * nkv + 3) / 4);
-    if (dtype == LL_BF16)
-        hipLaunchKernelGGL(kv_store_kernel<bf16_t>, dim3(kb), dim3(256), 0, st, static_cast<const bf16_t*>(qkv), pos,
-                           cs, rows, il, static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, B, 1, nh, nkv, d);
-    else
-        hipLaunchKernelGGL(kv_store_kernel<float>, dim3(kb), dim3(256), 0, st, static_cast<const float*>(qkv), pos, cs,
-                           rows, il, static_cast<float*>(kc), static_cast<float*>(vc), ctx, B, 1, nh, nkv, d);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // 1) append the new (rotated) key and value at slot pos[b], unless the QKV reduce already did
+    if (!appended) {
+        const unsigned kb = static_cast<unsigned>((static_cast<int64_t>(B) * nkv + 3) / 4);
+        if (dtype == LL_BF16)
+            hipLaunchKernelGGL(kv_store_kernel<bf16_t>, dim3(kb), dim3(256), 0, st, static_cast<const bf16_t*>(qkv),
+                               pos, cs, rows, il, static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, B, 1, nh,
+                               nkv, d);
+        else
+            hipLaunchKernelGGL(kv_store_kernel<float>, dim3(kb), dim3(256), 0, st, static_cast<const float*>(qkv), pos,
+                               cs, rows, il, static_cast<float*>(kc), static_cast<float*>(vc), ctx, B, 1, nh, nkv, d);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     // 2) attention over slots 0..pos[b]
     const int g = nkv > 0 ? nh / nkv : 0;
     if (attn_mfma_supported(dtype, d, nh, nkv) && (g == 1 || g == 2 || g == 4 || g == 8)) {

@@ -75,6 +75,12 @@ struct RopeEpi {
     int rope_cols;
     int d;
     int interleaved;
+    // optional: also store each token's rotated key and value columns at cache slot clamp(pos[row]) of
+    // [rows, ctx, nkv, d] caches (one token per sequence: decode); only the partial-sum reduce does it
+    void* kc = nullptr;
+    void* vc = nullptr;
+    int64_t ctx = 0;
+    int nh = 0, nkv = 0;
 };
 
 // ---- launchers (host) ----
@@ -91,6 +97,9 @@ hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C
                        int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t st, const RopeEpi* re = nullptr);
 // whether EPI_ROPE can be fused for this projection (else the caller rotates with launch_rope_apply)
 bool gemm_rope_fusable(int dtype, int64_t M, int d);
+// whether a fused-RoPE projection of this shape ends in the partial-sum reduce that can also append the
+// rotated keys and values to the caches (RopeEpi::kc / vc)
+bool gemm_rope_appends_cache(int dtype, int64_t M, int64_t N, int64_t K, int d, int rope_cols);
 hipError_t launch_attn_prefill(int dtype, const void* qkv, const int64_t* pos, const RopeTab* tab, int interleaved,
                                void* o, void* kc, void* vc, int64_t ctx, int B, int S, int nh, int nkv, int d,
                                hipStream_t st);
@@ -105,9 +114,10 @@ hipError_t launch_attn_prefill_chunk(int dtype, const void* qkv, const int64_t* 
 hipError_t launch_attn_prefill_varlen(int dtype, const void* qkv, const int* cu, int nseq, int max_seqlen, int total,
                                       void* o, int nh, int nkv, int d, hipStream_t st);
 size_t attn_decode_workspace_bytes(int64_t B, int64_t nh, int64_t d, int64_t ctx);
+// appended: the new keys and values are already in the caches (the QKV reduce stored them)
 hipError_t launch_attn_decode(int dtype, const void* qkv, const int64_t* pos, const RopeTab* tab, int interleaved,
                               void* kc, void* vc, int64_t ctx, void* o, int B, int nh, int nkv, int d, void* ws,
-                              size_t ws_bytes, hipStream_t st);
+                              size_t ws_bytes, hipStream_t st, bool appended = false);
 bool attn_mfma_supported(int dtype, int d, int nh, int nkv);
 
 }  // namespace ll

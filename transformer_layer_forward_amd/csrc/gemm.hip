@@ -972,7 +972,10 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce4_kernel(const float* _
                                                                   const bf16_t* __restrict__ R, int M, int N, int Nw,
                                                                   int splits, const int64_t* __restrict__ rpos,
                                                                   const float2* __restrict__ rcs, int64_t rrows,
-                                                                  int rope_cols, int rd, int ril) {
+                                                                  int rope_cols, int rd, int ril,
+                                                                  bf16_t* __restrict__ kc = nullptr,
+                                                                  bf16_t* __restrict__ vc = nullptr, int64_t ctx = 0,
+                                                                  int nh = 0, int nkv = 0) {
     const int64_t nq = N / 4;
     const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (q >= static_cast<int64_t>(M) * nq) return;
@@ -1012,7 +1015,18 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce4_kernel(const float* _
         v[0] += __uint_as_float(rr.x << 16); v[1] += __uint_as_float(rr.x & 0xffff0000u);
         v[2] += __uint_as_float(rr.y << 16); v[3] += __uint_as_float(rr.y & 0xffff0000u);
     }
-    *reinterpret_cast<uint2*>(C + o) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    const uint2 packed = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    *reinterpret_cast<uint2*>(C + o) = packed;
+    if (EPI == EPI_ROPE && kc != nullptr && n >= nh * rd) {
+        // row m is sequence m's one new token: its rotated key / value quad also goes to the cache slot
+        const int col = n - nh * rd;
+        const bool is_k = col < nkv * rd;
+        const int cc = is_k ? col : col - nkv * rd;
+        bf16_t* cache = is_k ? kc : vc;
+        const int64_t slot = clamp_pos(rpos[m], ctx);
+        *reinterpret_cast<uint2*>(cache + ((static_cast<int64_t>(m) * ctx + slot) * nkv + cc / rd) * rd + cc % rd) =
+            packed;
+    }
 }
 
 // sum the ranges and apply the epilogue: the quad kernel when N % 4 == 0 (and, for RoPE, d % 8 == 0)
@@ -1026,7 +1040,9 @@ static hipError_t splitk_reduce_launch(const float* P, void* C, const void* R, i
                            0, st, P, static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R), static_cast<int>(M),
                            static_cast<int>(N), static_cast<int>(Nw), splits, re ? re->pos : nullptr,
                            re ? re->tab.cs : nullptr, re ? re->tab.rows : 1, re ? re->rope_cols : 0,
-                           re ? re->d : 2, re ? re->interleaved : 0);
+                           re ? re->d : 2, re ? re->interleaved : 0, re ? static_cast<bf16_t*>(re->kc) : nullptr,
+                           re ? static_cast<bf16_t*>(re->vc) : nullptr, re ? re->ctx : 0, re ? re->nh : 0,
+                           re ? re->nkv : 0);
     } else {
         const int64_t total = M * N;
         hipLaunchKernelGGL(gemm_splitk_reduce_kernel<EPI>, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256),
@@ -1313,6 +1329,14 @@ static hipError_t f32_launch(const void* X, const void* W, void* C, const void* 
                        static_cast<const float*>(W), static_cast<float*>(C), static_cast<const float*>(R),
                        static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
     return hipGetLastError();
+}
+
+bool gemm_rope_appends_cache(int dtype, int64_t M, int64_t N, int64_t K, int d, int rope_cols) {
+    if (dtype != LL_BF16 || N % 4 || d % 8 || rope_cols % 4) return false;
+    if (use_skinny(M)) return true;   // the decode kernels never rotate: always partials + the reduce
+    RopeEpi probe{};
+    probe.d = d;
+    return mf_usable(EPI_ROPE, N, K, &probe) && mf_plan(EPI_ROPE, M, N, K).partial;
 }
 
 bool gemm_rope_fusable(int dtype, int64_t M, int d) {
