@@ -540,7 +540,7 @@ def main():
                "data": "synthetic (seeded N(0,1) hidden and caches, N(0,0.02) weights, 1+N(0,0.1) gains)",
                "config": {"workload": summ["workload"], "B": cfg.B, "ctx": cfg.ctx, **shape},
                "hbm_gbs": summ["hbm_gbs"], "stages_ms": summ["stages_ms"],
-               "roofline": {"kernel": "attention stage (cache append + attn_decode_split_kernel + combine)",
+               "roofline": {"kernel": "attention stage (attn_decode_split_kernel + combine; the cache append rides in the QKV reduce)",
                             "bound": "hbm", "achieved": round(kvb / (attn_ms / 1e3) / 1e9, 1),
                             "peak": MI355X_HBM_GBS, "unit": "GB/s",
                             "frac": round(kvb / (attn_ms / 1e3) / 1e9 / MI355X_HBM_GBS, 4), "traffic": None},
