@@ -30,8 +30,10 @@ form with linear interpolation in orig/wavelength; eps sits inside the square
 root; the causal mask is by token index; decode treats cached slots as already
 rotated and overwrites slot pos_b with the new token.
 
-Parity unpinned (pinned only by the stated reading): dynamic-NTK frequencies for
-L > original_max_pos, Llama3 mid-band interior values, and the GQA head mapping.
+No function is parity unpinned. The three readings the pages leave open (dynamic-NTK
+frequencies for L > original_max_pos, the Llama3 middle band, and the repeat_kv head
+mapping) are pinned against the Hugging Face Llama modules that the verl and nanotron
+pages build on, run in float64 (tests/test_oracle_library_pins.py).
 """
 from __future__ import annotations
 

@@ -2,8 +2,8 @@
 
 Plants one plausible mistake at a time (a dropped term, a wrong sign or index, a
 transposed operand, a moved threshold) in a temporary copy of oracle/ref.py and
-runs tests/test_oracle_pins.py against that copy. Every mutant must make at
-least one pin fail; the script exits non-zero if any survives. Takes ~10 minutes
+runs tests/test_oracle_pins.py and tests/test_oracle_library_pins.py against that copy. Every mutant must make at
+least one pin fail; the script exits non-zero if any survives. Takes ~15 minutes
 on 8 cores, so it is not part of the collected suite.
 """
 import os, shutil, subprocess, sys, tempfile
@@ -21,6 +21,10 @@ MUTS = [
     ("ntk off by one", "if L > orig:", "if L > orig + 1:"),
     ("llama3 interp swapped", "(1.0 - s) * f[j] / rope.factor + s * f[j]", "s * f[j] / rope.factor + (1.0 - s) * f[j]"),
     ("llama3 band edges swapped", "if lam[j] < lam_hi:", "if lam[j] < lam_lo:"),
+    ("llama3 interpolation linear in wavelength", "s = (orig / lam[j] - rope.low_freq_factor) / (rope.high_freq_factor - rope.low_freq_factor)", "s = (lam_lo - lam[j]) / (lam_lo - lam_hi)"),
+    ("llama3 interpolation on theta not f", "out[j] = (1.0 - s) * f[j] / rope.factor + s * f[j]", "out[j] = f[j] / ((1.0 - s) * rope.factor + s)"),
+    ("ntk base without the factor", "theta * (rope.factor * L / orig - (rope.factor - 1.0))", "theta * (L / orig)"),
+    ("ntk exponent dropped", "** (d / (d - 2.0))", "** 1.0"),
     ("rope sign half", "out[..., :h] = a * c - b * s", "out[..., :h] = a * c + b * s"),
     ("rope sign half2", "out[..., h:] = b * c + a * s", "out[..., h:] = b * c - a * s"),
     ("rope sign interleaved", "out[..., 0::2] = a * c - b * s", "out[..., 0::2] = a * c + b * s"),
@@ -66,9 +70,10 @@ for name, a, b in MUTS:
     for f in ("synth_inputs.py", "pytest.ini"):
         shutil.copy(f"{REPO}/{f}", d)
     shutil.copytree(f"{REPO}/oracle", f"{d}/oracle")
-    shutil.copytree(f"{REPO}/tests", f"{d}/tests", ignore=shutil.ignore_patterns("__pycache__", "test_gpu*", "test_abi.py"))
+    shutil.copytree(f"{REPO}/tests", f"{d}/tests", ignore=shutil.ignore_patterns("__pycache__", "test_gpu*", "test_abi.py", "test_zz*"))
     open(f"{d}/oracle/ref.py", "w").write(SRC.replace(a, b))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-m", "not gpu", "-p", "no:cacheprovider", "tests/test_oracle_pins.py"],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-m", "not gpu", "-p", "no:cacheprovider",
+                        "tests/test_oracle_pins.py", "tests/test_oracle_library_pins.py"],
                        cwd=d, capture_output=True, text=True)
     caught = r.returncode != 0
     failing = [l for l in r.stdout.splitlines() if l.startswith("FAILED")]

@@ -506,19 +506,6 @@ def _model64(cfg, n_layers, vocab, seed=0):
             "lm_head": to_f64(M["lm_head"], cfg.dtype)}
 
 
-def test_model_without_layers_is_head_of_embeddings():
-    """With no decoder layers the driver is output(norm(tok_embeddings(tokens))) ([meta-qa] #### 5)."""
-    cfg = scaled(CONFIGS["tiny_f32"], B=2, S=5)
-    M = _model64(cfg, 0, 23)
-    tok = np.array([[1, 22, 0, 5, 5], [9, 3, 3, 17, 2]])
-    pos = make_prefill_positions(cfg)
-    got = ref.model_prefill(cfg, M, tok, pos, 16)["logits"]
-    x = M["tok_embeddings"][tok]
-    want = (x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + cfg.eps) * M["g_final"]) @ M["lm_head"].T
-    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13)
-    assert got.shape == (2, 5, 23)
-
-
 def test_model_stack_causality_and_layer_order():
     """Logits of token i depend only on tokens 0..i (bitwise), and the layers apply in order (swapping two
     different layers changes the result)."""
@@ -534,19 +521,6 @@ def test_model_stack_causality_and_layer_order():
     assert not np.array_equal(a[:, 6:], b[:, 6:])
     M2 = dict(M, layers=M["layers"][::-1])
     assert not np.allclose(ref.model_prefill(cfg, M2, tok, pos, 16)["logits"], a)
-
-
-def test_model_applies_layers_in_list_order():
-    """for layer in self.layers: h = layer(h, ...) ([meta-qa] #### 5): the stack equals applying the
-    layer forward to the embeddings, first layer first."""
-    cfg = scaled(CONFIGS["tiny_f32"], B=1, S=7)
-    M = _model64(cfg, 2, 19)
-    pos = make_prefill_positions(cfg)
-    tok = np.array([[3, 1, 4, 1, 5, 9, 2]])
-    h = M["tok_embeddings"][tok]
-    for W in M["layers"]:
-        h = ref.layer_prefill(cfg, W, h, pos, 16)["out"]
-    np.testing.assert_array_equal(ref.model_prefill(cfg, M, tok, pos, 16)["h"], h)
 
 
 # ------------------------------------------------------------------ shapes
