@@ -14,9 +14,13 @@
  *     w_qkv = [W_q; W_k; W_v] (verl "parallel_attention.py", §2 split([q,k,v])), and
  *     w_gate_up = [W_gate; W_up] (nanotron §9.4 gate_up_proj + chunk(2)).
  *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work on it: they never
- *     synchronise the device and never allocate device memory, except that the first call needing a
- *     RoPE table for a new (rope parameters, head_dim, length, device) builds it once (host fp64,
- *     blocking upload) and keeps it until ll_release_caches().
+ *     synchronise the device or the host. The one library-owned state is the RoPE cos/sin table: one
+ *     per (rope parameters, head_dim, device, stream), generated on the device by a kernel enqueued on
+ *     that stream (fp64 angles and fp64 cos/sin, stored fp32). A call allocates device memory only when
+ *     it needs more table rows than the stream's table holds (the table then at least doubles, so a
+ *     growing kv_seq_len allocates O(log kv_seq_len) times); outgrown tables are kept until
+ *     ll_release_caches(). A dynamic-NTK call whose kv_seq_len differs from the table's regenerates the
+ *     rows it needs in place, in stream order, without allocating.
  *   - Errors: every host-checkable precondition is validated before any HIP call; a failed check
  *     returns LL_EINVAL (bad argument) or LL_EUNSUPPORTED (valid but not implemented) and enqueues
  *     nothing. A failed launch returns LL_EHIP. ll_last_error() gives the text of the last failure
@@ -247,8 +251,8 @@ ll_status swiglu_mlp(const void* x, const void* w_gate_up, const void* w_down, c
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char* ll_last_error(void);
 
-/* Frees the library-owned RoPE tables of every device. Not safe while work that reads them is
- * still pending on any stream. */
+/* Frees the library-owned RoPE tables of every device and stream. Not safe while work that reads them
+ * is still pending on any stream. */
 void ll_release_caches(void);
 
 /* Per-stage timing of llama_layer_forward, for benchmarking. ll_profile_begin() enables HIP event

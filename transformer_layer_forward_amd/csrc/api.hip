@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "common.h"
+#include "rope_cache.h"
 
 using namespace ll;
 
@@ -103,74 +104,70 @@ void rope_freqs(const ll_rope& r, int d, int64_t L, std::vector<double>& f) {
     }
 }
 
-struct TabKey {
-    int type, d, dev;
-    double theta, factor, lff, hff;
-    int64_t omp, L;
-    bool operator<(const TabKey& o) const {
-        return std::tie(type, d, dev, theta, factor, lff, hff, omp, L) <
-               std::tie(o.type, o.d, o.dev, o.theta, o.factor, o.lff, o.hff, o.omp, o.L);
+// Library-owned tables: one slot per (RoPE parameters, head size, device, stream), generated on the
+// device in stream order (rope_cache.h states the policy).
+struct HipRopeBackend {
+    const ll_rope* rope = nullptr;   // parameters of the call being served
+    int64_t L = 0;                   // its kv_seq_len
+    hipError_t last = hipSuccess;
+    void* alloc(int, size_t bytes) {
+        void* p = nullptr;
+        last = hipMalloc(&p, bytes);
+        return last == hipSuccess ? p : nullptr;
     }
-};
-
-struct TabEntry {
-    float2* dev_ptr = nullptr;
-    int64_t rows = 0;
+    void release(int dev, void* p) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(dev);
+        (void)hipFree(p);
+        (void)hipSetDevice(cur);
+    }
+    bool generate(const RopeFamily& fam, void* p, int64_t rows, int64_t) {
+        std::vector<double> f;
+        rope_freqs(*rope, fam.d, L, f);
+        RopeFreqs fr{};
+        for (size_t i = 0; i < f.size(); ++i) fr.f[i] = f[i];
+        last = launch_rope_table(static_cast<float2*>(p), rows, fam.d / 2, fr,
+                                 static_cast<hipStream_t>(const_cast<void*>(fam.stream)));
+        return last == hipSuccess;
+    }
 };
 
 std::mutex g_tab_mu;
-std::map<TabKey, TabEntry> g_tabs;
-std::vector<std::pair<int, void*>> g_retired;  // older, shorter tables kept until release
+RopeTableCache<HipRopeBackend> g_tabs{HipRopeBackend{}};
 
-ll_status rope_table_get(const ll_rope& r, int d, int64_t kv_seq_len, RopeTab* out) {
+RopeFamily rope_family(const ll_rope& r, int d, int dev, const void* stream) {
+    RopeFamily k;
+    k.type = r.type;
+    k.d = d;
+    k.dev = dev;
+    k.theta = r.theta;
+    k.factor = r.type == LL_ROPE_DEFAULT ? 1.0 : r.factor;
+    k.lff = r.type == LL_ROPE_LLAMA3 ? r.low_freq_factor : 0.0;
+    k.hff = r.type == LL_ROPE_LLAMA3 ? r.high_freq_factor : 0.0;
+    k.omp = (r.type == LL_ROPE_LLAMA3 || r.type == LL_ROPE_DYNAMIC_NTK) ? r.original_max_pos : 0;
+    k.stream = stream;
+    return k;
+}
+
+// The table of (r, d) for positions < kv_seq_len, valid for work enqueued on `stream` after this call.
+ll_status rope_table_get(const ll_rope& r, int d, int64_t kv_seq_len, hipStream_t stream, RopeTab* out) {
     int dev = 0;
     LL_CHECK_HIP(hipGetDevice(&dev), "hipGetDevice");
-    TabKey key{};
-    key.type = r.type;
-    key.d = d;
-    key.dev = dev;
-    key.theta = r.theta;
-    key.factor = r.type == LL_ROPE_DEFAULT ? 1.0 : r.factor;
-    key.lff = r.type == LL_ROPE_LLAMA3 ? r.low_freq_factor : 0.0;
-    key.hff = r.type == LL_ROPE_LLAMA3 ? r.high_freq_factor : 0.0;
-    key.omp = (r.type == LL_ROPE_LLAMA3 || r.type == LL_ROPE_DYNAMIC_NTK) ? r.original_max_pos : 0;
     const bool dyn = r.type == LL_ROPE_DYNAMIC_NTK && kv_seq_len > r.original_max_pos;
-    key.L = dyn ? kv_seq_len : 0;
     std::lock_guard<std::mutex> lock(g_tab_mu);
-    auto it = g_tabs.find(key);
-    if (it != g_tabs.end() && it->second.rows >= kv_seq_len) {
-        out->cs = it->second.dev_ptr;
-        out->rows = it->second.rows;
-        return LL_OK;
+    HipRopeBackend& be = g_tabs.backend();
+    be.rope = &r;
+    be.L = kv_seq_len;
+    bool alloc_failed = false;
+    const RopeSlot* slot = g_tabs.get(rope_family(r, d, dev, stream), kv_seq_len, dyn ? kv_seq_len : 0, dyn,
+                                      &alloc_failed);
+    if (!slot) {
+        if (alloc_failed) return fail(LL_ENOMEM, "RoPE table allocation: %s", hipGetErrorString(be.last));
+        return hip_fail(be.last, "RoPE table launch");
     }
-    int64_t rows = dyn ? kv_seq_len : std::max<int64_t>(kv_seq_len, 4096);
-    if (!dyn && it != g_tabs.end()) rows = std::max(rows, 2 * it->second.rows);
-    std::vector<double> f;
-    rope_freqs(r, d, kv_seq_len, f);
-    const int half = d / 2;
-    std::vector<float2> host(static_cast<size_t>(rows) * half);
-    for (int64_t p = 0; p < rows; ++p)
-        for (int i = 0; i < half; ++i) {
-            const double a = static_cast<double>(p) * f[i];
-            host[static_cast<size_t>(p) * half + i] = make_float2(static_cast<float>(std::cos(a)),
-                                                                   static_cast<float>(std::sin(a)));
-        }
-    void* dptr = nullptr;
-    hipError_t e = hipMalloc(&dptr, host.size() * sizeof(float2));
-    if (e != hipSuccess) return fail(LL_ENOMEM, "RoPE table allocation (%zu bytes): %s", host.size() * sizeof(float2),
-                                     hipGetErrorString(e));
-    e = hipMemcpy(dptr, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-        (void)hipFree(dptr);
-        return hip_fail(e, "RoPE table upload");
-    }
-    if (it != g_tabs.end()) g_retired.emplace_back(dev, it->second.dev_ptr);
-    TabEntry ent;
-    ent.dev_ptr = static_cast<float2*>(dptr);
-    ent.rows = rows;
-    g_tabs[key] = ent;
-    out->cs = ent.dev_ptr;
-    out->rows = rows;
+    out->cs = static_cast<const float2*>(slot->ptr);
+    out->rows = slot->valid;
     return LL_OK;
 }
 
@@ -276,19 +273,7 @@ const char* ll_version(void) { return "llama_layer gfx950 1.0"; }
 
 void ll_release_caches(void) {
     std::lock_guard<std::mutex> lock(g_tab_mu);
-    int cur = 0;
-    (void)hipGetDevice(&cur);
-    for (auto& kv : g_tabs) {
-        (void)hipSetDevice(kv.first.dev);
-        (void)hipFree(kv.second.dev_ptr);
-    }
-    for (auto& p : g_retired) {
-        (void)hipSetDevice(p.first);
-        (void)hipFree(p.second);
-    }
-    (void)hipSetDevice(cur);
-    g_tabs.clear();
-    g_retired.clear();
+    g_tabs.release_all();
 }
 
 ll_status ll_profile_begin(int32_t reserve_calls) {
@@ -366,11 +351,12 @@ ll_status rope_apply(const ll_rope* rope, void* qkv, const int64_t* position_ids
     if (B < 0 || S < 0 || n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || head_dim % 2)
         return fail(LL_EINVAL, "bad shape");
     if (n_heads % n_kv_heads) return fail(LL_EINVAL, "n_heads %% n_kv_heads != 0");
+    if (head_dim > 256) return fail(LL_EUNSUPPORTED, "head_dim > 256 not supported");
     if (kv_seq_len <= 0) return fail(LL_EINVAL, "kv_seq_len must be > 0");
     if (B * S == 0) return LL_OK;
     if (!qkv || !position_ids) return fail(LL_EINVAL, "NULL tensor pointer");
     RopeTab tab;
-    st = rope_table_get(*rope, static_cast<int>(head_dim), kv_seq_len, &tab);
+    st = rope_table_get(*rope, static_cast<int>(head_dim), kv_seq_len, as_stream(stream), &tab);
     if (st != LL_OK) return st;
     hipError_t e = launch_rope_apply(dtype, qkv, position_ids, tab, B * S, static_cast<int>(n_heads),
                                      static_cast<int>(n_kv_heads), static_cast<int>(head_dim), rope->interleaved,
@@ -410,7 +396,7 @@ ll_status gqa_attn_prefill(const void* qkv, const ll_rope* rope, const int64_t* 
     if (st != LL_OK || B * S == 0) return st;
     RopeTab tab;
     if (rope) {
-        st = rope_table_get(*rope, static_cast<int>(head_dim), kv_seq_len, &tab);
+        st = rope_table_get(*rope, static_cast<int>(head_dim), kv_seq_len, as_stream(stream), &tab);
         if (st != LL_OK) return st;
     }
     hipError_t e = launch_attn_prefill(dtype, qkv, position_ids, rope ? &tab : nullptr, rope ? rope->interleaved : 0, o,
@@ -483,7 +469,7 @@ ll_status gqa_attn_decode(const void* qkv, const ll_rope* rope, const int64_t* p
     if (need && !workspace) return fail(LL_EINVAL, "workspace is NULL");
     RopeTab tab;
     if (rope) {
-        st = rope_table_get(*rope, static_cast<int>(head_dim), kv_seq_len, &tab);
+        st = rope_table_get(*rope, static_cast<int>(head_dim), kv_seq_len, as_stream(stream), &tab);
         if (st != LL_OK) return st;
     }
     hipError_t e = launch_attn_decode(dtype, qkv, pos, rope ? &tab : nullptr, rope ? rope->interleaved : 0, k_cache,
@@ -578,7 +564,7 @@ static ll_status layer_forward_impl(const ll_layer_cfg* cfg, const ll_layer_weig
 
     const Shapes s = shapes_of(cfg, B, S);
     RopeTab tab;
-    st = rope_table_get(cfg->rope, static_cast<int>(s.d), kv_seq_len, &tab);
+    st = rope_table_get(cfg->rope, static_cast<int>(s.d), kv_seq_len, as_stream(stream), &tab);
     if (st != LL_OK) return st;
 
     char* ws = static_cast<char*>(workspace);

@@ -61,6 +61,11 @@ struct RopeTab {
     int64_t rows;   // positions covered; device code clamps into [0, rows)
 };
 
+// Pair frequencies f'_j (j < head_dim / 2 <= 128) handed to the table kernel by value.
+struct RopeFreqs {
+    double f[128];
+};
+
 __device__ __forceinline__ int64_t clamp_pos(int64_t p, int64_t rows) {
     return p < 0 ? 0 : (p >= rows ? rows - 1 : p);
 }
@@ -89,6 +94,8 @@ hipError_t launch_rmsnorm(int dtype, const void* x, const void* g, void* y, int6
 // out[r, :] = table[clamp(tokens[r], 0, vocab-1), :] for r < rows
 hipError_t launch_embedding(int dtype, const void* table, const int64_t* tokens, void* out, int64_t rows, int64_t H,
                             int64_t vocab, hipStream_t st);
+// fill cs[0 .. rows * half) of a RoPE table from the pair frequencies (enqueued on st)
+hipError_t launch_rope_table(float2* cs, int64_t rows, int half, const RopeFreqs& fr, hipStream_t st);
 hipError_t launch_rope_apply(int dtype, void* qkv, const int64_t* pos, RopeTab tab, int64_t tokens, int nh, int nkv,
                              int d, int interleaved, hipStream_t st);
 // C[M, ldc] (epi) = X[M, K] . W^T; W has N rows (EPI_SILU: 2*inter rows, N = inter output columns).

@@ -8,6 +8,8 @@
 // Token embedding (CSDN answer "#### 5." tok_embeddings(tokens), nn.Embedding): one row per workgroup,
 // copied from the table with 16-byte vectors; ids outside [0, vocab) are clamped (no out-of-bounds read).
 //
+// RoPE table: built on the device from the pair frequencies, fp64 angles and fp64 cos/sin rounded to fp32.
+//
 // RoPE apply (verl "parallel_attention.py" §1 rotary_emb/apply_rotary_pos_emb; NJU lecture 5
 // "RoPE高效实现" rotate_half): one lane per (token, head, pair), in place on packed qkv, reading
 // (cos, sin) from the fp32 table built from fp64 angles.
@@ -176,6 +178,29 @@ hipError_t launch_rope_apply(int dtype, void* qkv, const int64_t* pos, RopeTab t
     else
         hipLaunchKernelGGL(rope_apply_kernel<float>, dim3(blocks), dim3(256), 0, st, static_cast<float*>(qkv), pos,
                            tab.cs, tab.rows, tokens, nh, nkv, d, interleaved);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ RoPE table
+// cs[p * half + j] = (cos(p f_j), sin(p f_j)) for p < rows: the angle is formed and its cosine and sine
+// evaluated in double precision (the device math library), then rounded to fp32 once. One lane per entry.
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ cs, int64_t rows, int half,
+                                                         RopeFreqs fr) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= rows * half) return;
+    const int64_t p = i / half;
+    const int j = static_cast<int>(i - p * half);
+    const double a = static_cast<double>(p) * fr.f[j];
+    double sn, cn;
+    sincos(a, &sn, &cn);
+    cs[i] = make_float2(static_cast<float>(cn), static_cast<float>(sn));
+}
+
+hipError_t launch_rope_table(float2* cs, int64_t rows, int half, const RopeFreqs& fr, hipStream_t st) {
+    const int64_t n = rows * half;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, cs, rows,
+                       half, fr);
     return hipGetLastError();
 }
 
