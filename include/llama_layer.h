@@ -116,6 +116,23 @@ ll_status llama_layer_forward(const ll_layer_cfg* cfg, const ll_layer_weights* w
                               void* k_cache, void* v_cache, int64_t ctx,
                               void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* llama_layer_forward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, layout, modes and results as
+ * llama_layer_forward, without the workspace: the workspace and the call's RoPE table (generated on the
+ * device for kv_seq_len rows) live in a static 64 MiB device array of the library, one per GPU, held until
+ * the process ends. The call performs no hipMalloc, hipFree or other allocation (the library-owned RoPE
+ * tables are not used) and records no profiling events.
+ * Limit: llama_layer_workspace_bytes(cfg, B, S, ctx) rounded up to 256, plus kv_seq_len * head_dim * 4
+ * bytes of table, must not exceed 64 MiB (e.g. Llama-3-8B-shaped decode at B = 64 with kv_seq_len 8192);
+ * larger calls return LL_EINVAL and enqueue nothing.
+ * Every call on one GPU uses that GPU's one array, which keeps the last call's contents: calls that overlap
+ * on one GPU (different streams, or host threads without ordering) race and must not be issued. */
+ll_status llama_layer_forward_noalloc(const ll_layer_cfg* cfg, const ll_layer_weights* w,
+                                      const void* hidden, const int64_t* position_ids,
+                                      int64_t B, int64_t S, int64_t kv_seq_len,
+                                      void* k_cache, void* v_cache, int64_t ctx,
+                                      void* out, void* stream);
+
 /* Chunked prefill on a cache prefix (llama3 结构详解 §3.2: the new keys/values go to cache slots
  * start_pos .. start_pos + seqlen - 1 and attention reads slots 0 .. start_pos + seqlen - 1; CSDN answer
  * "#### 5.": for start_pos > 0 the causal mask gains start_pos leading zero columns).

@@ -122,6 +122,26 @@ def test_layer_argument_errors():
     assert call(w=ctypes.byref(bad)) == _lib.LL_EINVAL
 
 
+def test_noalloc_entry_point_checks_before_any_hip_call():
+    """llama_layer_forward_noalloc validates like llama_layer_forward and refuses a call whose workspace plus
+    RoPE table exceeds its 64 MiB static scratch, all before touching the device."""
+    lib = L.load()
+    w = _lib.LLLayerWeights(*([FAKE.value] * 6))
+    c8 = L.LayerConfig(4096, 32, 8, 128, 14336, dtype=torch.bfloat16).to_c()
+
+    def call(c, B, S, L_, kc=None, vc=None, ctx=0, hidden=FAKE):
+        return lib.llama_layer_forward_noalloc(ctypes.byref(c), ctypes.byref(w), hidden, FAKE, B, S, L_, kc, vc, ctx,
+                                               FAKE, None)
+
+    assert call(c8, 1, 4096, 4096) == _lib.LL_EINVAL            # 256 MiB of workspace
+    assert "static scratch" in L.last_error()
+    assert call(c8, 64, 1, 1 << 24, FAKE, FAKE, 1 << 24) == _lib.LL_EINVAL   # a 8 GiB RoPE table
+    assert call(c8, 1, 300, 300, hidden=None) == _lib.LL_EINVAL
+    assert call(c8, 0, 1, 300) == _lib.LL_OK
+    bad = _cfg(head_dim=15)
+    assert call(bad, 1, 8, 8) == _lib.LL_EINVAL
+
+
 def test_kernel_entry_point_errors():
     lib = L.load()
     assert lib.rmsnorm(None, None, None, 4, 64, 1e-5, _lib.LL_BF16, None) == _lib.LL_EINVAL

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     last_error,
     llama_layer_forward,
     llama_layer_forward_chunk,
+    llama_layer_forward_noalloc,
     llama_layer_forward_varlen,
     llama_model_forward,
     load,

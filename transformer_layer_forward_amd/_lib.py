@@ -22,7 +22,7 @@ ROPE_TYPES = {"default": 0, "linear": 1, "dynamic_ntk": 2, "llama3": 3}
 STATUS_NAMES = {0: "LL_OK", 1: "LL_EINVAL", 2: "LL_EUNSUPPORTED", 3: "LL_EHIP", 4: "LL_ENOMEM"}
 
 EXPORTED = (
-    "llama_layer_workspace_bytes", "llama_layer_forward", "llama_layer_forward_chunk", "llama_layer_forward_varlen",
+    "llama_layer_workspace_bytes", "llama_layer_forward", "llama_layer_forward_noalloc", "llama_layer_forward_chunk", "llama_layer_forward_varlen",
     "llama_model_workspace_bytes", "llama_model_forward",
     "rmsnorm", "rope_apply", "gqa_attn_prefill", "gqa_attn_prefill_chunk_workspace_bytes", "gqa_attn_prefill_chunk",
     "gqa_attn_prefill_varlen",
@@ -107,6 +107,8 @@ def load() -> ctypes.CDLL:
         "llama_layer_workspace_bytes": (c_sz, [ctypes.POINTER(LLLayerCfg), c_i64, c_i64, c_i64]),
         "llama_layer_forward": (c_i32, [ctypes.POINTER(LLLayerCfg), ctypes.POINTER(LLLayerWeights), c_vp, c_vp, c_i64,
                                         c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_sz, c_vp]),
+        "llama_layer_forward_noalloc": (c_i32, [ctypes.POINTER(LLLayerCfg), ctypes.POINTER(LLLayerWeights), c_vp, c_vp,
+                                                c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp]),
         "llama_layer_forward_chunk": (c_i32, [ctypes.POINTER(LLLayerCfg), ctypes.POINTER(LLLayerWeights), c_vp, c_vp,
                                               c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_sz, c_vp]),
         "llama_layer_forward_varlen": (c_i32, [ctypes.POINTER(LLLayerCfg), ctypes.POINTER(LLLayerWeights), c_vp,
@@ -324,6 +326,28 @@ def llama_layer_forward(cfg: LayerConfig, weights: dict, hidden: torch.Tensor, p
                                    int(kv_seq_len), _ptr(k_cache), _ptr(v_cache), ctx, _ptr(y), _ptr(ws), ws.numel(),
                                    _stream(hidden)), "llama_layer_forward")
     return y
+
+
+def llama_layer_forward_noalloc(cfg: LayerConfig, weights: dict, hidden: torch.Tensor, position_ids: torch.Tensor,
+                                kv_seq_len: Optional[int] = None, k_cache: Optional[torch.Tensor] = None,
+                                v_cache: Optional[torch.Tensor] = None, out: torch.Tensor = None) -> torch.Tensor:
+    """llama_layer_forward whose workspace and RoPE table live in the library's static device scratch: the
+    library allocates nothing. ``out`` must be given (this wrapper allocates nothing either)."""
+    lib = load()
+    B, S = hidden.shape[0], hidden.shape[1]
+    ctx = k_cache.shape[1] if k_cache is not None else 0
+    if kv_seq_len is None:
+        kv_seq_len = ctx if ctx else S
+    if out is None:
+        raise ValueError("llama_layer_forward_noalloc needs a preallocated out tensor")
+    c = cfg.to_c()
+    w = LLLayerWeights(*(weights[k].data_ptr() for k in ("w_qkv", "w_o", "w_gate_up", "w_down", "g_attn", "g_mlp")))
+    for k in ("w_qkv", "w_o", "w_gate_up", "w_down", "g_attn", "g_mlp"):
+        _ptr(weights[k])
+    _check(lib.llama_layer_forward_noalloc(ctypes.byref(c), ctypes.byref(w), _ptr(hidden), _ptr(position_ids), B, S,
+                                           int(kv_seq_len), _ptr(k_cache), _ptr(v_cache), ctx, _ptr(out),
+                                           _stream(hidden)), "llama_layer_forward_noalloc")
+    return out
 
 
 def llama_layer_forward_varlen(cfg: LayerConfig, weights: dict, hidden: torch.Tensor, position_ids: torch.Tensor,

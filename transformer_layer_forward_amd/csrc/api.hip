@@ -171,6 +171,35 @@ ll_status rope_table_get(const ll_rope& r, int d, int64_t kv_seq_len, hipStream_
     return LL_OK;
 }
 
+// ------------------------------------------------------------------ static scratch
+// Device memory of llama_layer_forward_noalloc: the layer workspace and the call's RoPE table live in
+// this file-scope array, so that entry point needs no allocation at all. Each device that runs it holds
+// its own copy until the process ends. In host code `scratch` names a host-side stand-in, never the
+// device address: host code uses only the per-device address from hipGetSymbolAddress below.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;   // device -> device address of its scratch
+
+// The current device's scratch address, looked up once per device (with that device current).
+ll_status scratch_address(void** out) {
+    int dev = 0;
+    LL_CHECK_HIP(hipGetDevice(&dev), "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it == g_scratch_ptr.end()) {
+        void* p = nullptr;
+        LL_CHECK_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(LL_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        it = g_scratch_ptr.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return LL_OK;
+}
+
+size_t rope_table_bytes(int64_t rows, int64_t d) { return static_cast<size_t>(rows) * static_cast<size_t>(d / 2) * 8u; }
+
 // ------------------------------------------------------------------ profiling
 constexpr int kMaxStages = 8;
 const char* kStageNames[kMaxStages] = {"rmsnorm_attn", "qkv_proj",    "attention",   "o_proj_residual",
@@ -538,7 +567,7 @@ static ll_status layer_forward_impl(const ll_layer_cfg* cfg, const ll_layer_weig
                                     const int64_t* position_ids, int64_t B, int64_t S, int64_t kv_seq_len,
                                     void* k_cache, void* v_cache, int64_t ctx, void* out, void* workspace,
                                     size_t workspace_bytes, void* stream, bool chunk,
-                                    const Varlen* vl = nullptr) {
+                                    const Varlen* vl = nullptr, bool use_scratch = false) {
     ll_status st = check_cfg(cfg);
     if (st != LL_OK) return st;
     if (!w) return fail(LL_EINVAL, "weights is NULL");
@@ -559,13 +588,37 @@ static ll_status layer_forward_impl(const ll_layer_cfg* cfg, const ll_layer_weig
     if (chunk && !k_cache) return fail(LL_EINVAL, "chunked prefill needs k_cache and v_cache");
     const bool decode = !chunk && (S == 1 && k_cache != nullptr);
     const LayerWs lw = layer_ws(cfg, B, S, decode ? ctx : 0);
-    if (!workspace || workspace_bytes < lw.total)
-        return fail(LL_EINVAL, "workspace too small: %zu < %zu", workspace_bytes, lw.total);
-
     const Shapes s = shapes_of(cfg, B, S);
+    if (use_scratch) {
+        // workspace, then this call's RoPE table, both in the static scratch
+        const size_t need = round_up(lw.total) + rope_table_bytes(kv_seq_len, s.d);
+        if (need > kScratchBytes)
+            return fail(LL_EINVAL, "llama_layer_forward_noalloc needs %zu bytes of scratch; its static scratch holds %zu",
+                        need, kScratchBytes);
+    } else if (!workspace || workspace_bytes < lw.total) {
+        return fail(LL_EINVAL, "workspace too small: %zu < %zu", workspace_bytes, lw.total);
+    }
+
     RopeTab tab;
-    st = rope_table_get(cfg->rope, static_cast<int>(s.d), kv_seq_len, as_stream(stream), &tab);
-    if (st != LL_OK) return st;
+    if (use_scratch) {
+        void* base = nullptr;
+        st = scratch_address(&base);
+        if (st != LL_OK) return st;
+        workspace = base;
+        workspace_bytes = round_up(lw.total);
+        float2* cs = reinterpret_cast<float2*>(static_cast<char*>(base) + round_up(lw.total));
+        std::vector<double> f;
+        rope_freqs(cfg->rope, static_cast<int>(s.d), kv_seq_len, f);
+        RopeFreqs fr{};
+        for (size_t i = 0; i < f.size(); ++i) fr.f[i] = f[i];
+        LL_CHECK_HIP(launch_rope_table(cs, kv_seq_len, static_cast<int>(s.d / 2), fr, as_stream(stream)),
+                     "RoPE table launch");
+        tab.cs = cs;
+        tab.rows = kv_seq_len;
+    } else {
+        st = rope_table_get(cfg->rope, static_cast<int>(s.d), kv_seq_len, as_stream(stream), &tab);
+        if (st != LL_OK) return st;
+    }
 
     char* ws = static_cast<char*>(workspace);
     void* xn = ws + lw.xn;
@@ -581,7 +634,7 @@ static ll_status layer_forward_impl(const ll_layer_cfg* cfg, const ll_layer_weig
     const float eps = static_cast<float>(cfg->eps);
     hipStream_t stream_h = as_stream(stream);
 
-    const bool prof = g_prof.on;
+    const bool prof = g_prof.on && !use_scratch;   // the no-allocation entry point records no events
     size_t ev0 = 0;
     if (prof) {
         ev0 = g_prof.used;
@@ -676,6 +729,13 @@ ll_status llama_layer_forward(const ll_layer_cfg* cfg, const ll_layer_weights* w
                               void* stream) {
     return layer_forward_impl(cfg, w, hidden, position_ids, B, S, kv_seq_len, k_cache, v_cache, ctx, out, workspace,
                               workspace_bytes, stream, false);
+}
+
+ll_status llama_layer_forward_noalloc(const ll_layer_cfg* cfg, const ll_layer_weights* w, const void* hidden,
+                                      const int64_t* position_ids, int64_t B, int64_t S, int64_t kv_seq_len,
+                                      void* k_cache, void* v_cache, int64_t ctx, void* out, void* stream) {
+    return layer_forward_impl(cfg, w, hidden, position_ids, B, S, kv_seq_len, k_cache, v_cache, ctx, out, nullptr, 0,
+                              stream, false, nullptr, true);
 }
 
 size_t llama_model_workspace_bytes(const ll_layer_cfg* cfg, int64_t vocab, int64_t B, int64_t S) {
