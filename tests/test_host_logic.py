@@ -1,6 +1,6 @@
 """Host-side logic of the library checked on the CPU with a plain C++ compiler (no GPU, no HIP runtime).
 
-The RoPE table bookkeeping (transformer_layer_forward_amd/csrc/rope_cache.h) is built together with a
+The balanced decode partition (csrc/decode_partition.h) and the RoPE table bookkeeping (transformer_layer_forward_amd/csrc/rope_cache.h) is built together with a
 driver that replaces device memory and the table kernel by counters, under AddressSanitizer and
 UndefinedBehaviorSanitizer, and run: one slot per (RoPE parameters, head size, device, stream), geometric
 growth, in-place regeneration of a dynamic-NTK table whose length changes, everything freed on release.
@@ -36,3 +36,10 @@ def test_rope_table_cache_policy(tmp_path):
     out = _build_and_run("rope_cache_check.cpp", tmp_path)
     assert "all checks passed" in out
 
+
+def test_balanced_decode_partition(tmp_path):
+    """The balanced decode kernel's work split (csrc/decode_partition.h), replayed for 3000 random batches:
+    every tile of every (sequence, head group) processed exactly once, record indices unique, and the
+    combine finds exactly the records each segment's pieces wrote."""
+    out = _build_and_run("decode_partition_check.cpp", tmp_path)
+    assert "all checks passed" in out

@@ -35,6 +35,7 @@
 // online softmax; used for the fp32 configuration and for head sizes the matrix-core kernels
 // do not cover.
 #include "common.h"
+#include "decode_partition.h"
 
 namespace ll {
 
@@ -1015,6 +1016,28 @@ __device__ __forceinline__ void dec_load(DecTile<D>& t, const bf16_t* __restrict
     }
 }
 
+// The same tile through buffer loads: one 32-bit byte offset per cache row (the dims' 64-byte steps
+// ride in the instruction's offset field) instead of a 64-bit address per load. The resource covers the
+// rows of one (sequence, kv head); offsets stay below 2^31 (checked by the launcher).
+template <int D>
+__device__ __forceinline__ void dec_load_buf(DecTile<D>& t, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                             int row_bytes, int t0, int last, int lrow, int lgrp, int dch,
+                                             int ksub) {
+#pragma unroll
+    for (int kf = 0; kf < 2; ++kf) {
+        const int kk = t0 + kf * 16 + lrow, key = kk < last ? kk : last;
+        const int off = key * row_bytes + lgrp * 16;
+#pragma unroll
+        for (int k = 0; k < DecTile<D>::KC32; ++k)
+            t.k[kf][k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off + k * 64, 0, 0));
+    }
+#pragma unroll
+    for (int it = 0; it < DecTile<D>::PV_IT; ++it) {
+        const int kk = t0 + it * DecTile<D>::KPI + ksub, key = kk < last ? kk : last;
+        t.v[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, key * row_bytes + dch * 16, 0, 0));
+    }
+}
+
 // number of key splits per (sequence, kv head) for a call: enough workgroups to fill the chip, at most
 // one per 128-key block of the cache
 static int dec_nsplit(int64_t B, int64_t nh, int64_t ctx) {
@@ -1241,6 +1264,309 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(const float* __
         if (lane + 64 * i < d) stf<T>(out + static_cast<int64_t>(bh) * d + lane + 64 * i, num[i] * inv);
 }
 
+// ------------------------------------------------------------------ decode, balanced shares
+// A persistent grid of NG workgroups (one per compute unit) splits the tiles of all sequences into equal
+// contiguous shares (decode_partition.h), so the longest sequences no longer set the kernel's duration.
+// A workgroup has 8 waves over the HW = min(n_kv, 8) kv heads of a head group: wave w serves head
+// w % HW and, when HW < 8, every P-th tile of the share (phase w / HW, P = 8 / HW). With n_kv >= 8 the
+// 8 waves read the 8 heads' slices of the same cache rows at the same time, i.e. whole contiguous
+// rows. The key loop per wave is that of the split kernel above (32-key tiles, the next two tiles
+// loading into registers, both products on the matrix cores). At the end of each piece (the part of the
+// share inside one segment) the P waves of a head merge through LDS and the piece writes one
+// (max, sum, o) record per query head at index g + s; the combine kernel merges a head's records.
+constexpr int DV_WAVES = 8;
+constexpr int DV_THREADS = 64 * DV_WAVES;
+constexpr int DV_MAX_SEGS = 4096;   // (sequence, head group) pairs one call may have
+constexpr int DV_MAX_WG = 512;
+constexpr int DV_REC_PAD = 4;       // record = [max, sum, -, -, o[0 .. D)]: o starts 16-byte aligned
+
+template <int D, int G, bool ROPE, bool IL>
+__global__ __launch_bounds__(DV_THREADS) void attn_decode_bal_kernel(
+    const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, const float2* __restrict__ cs, int64_t rope_rows,
+    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, int64_t ctx, float* __restrict__ part,
+    int* __restrict__ seg_prefix, int nseg, int ngroups, int HW, int nh, int nkv, float scale_log2) {
+    using TT = DecTile<D>;
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    constexpr int DF = D / 16;
+    constexpr int REC = D + DV_REC_PAD;
+    __shared__ int sPre[DV_MAX_SEGS + 1];
+    __shared__ int sWave[DV_WAVES];
+    __shared__ __align__(16) bf16_t sV[DV_WAVES][DEC_TILE * D];
+    __shared__ float sM[DV_WAVES][G], sL[DV_WAVES][G];
+    __shared__ float sO[DV_WAVES][G][D];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t NG = gridDim.x, g = blockIdx.x;
+    const int P = DV_WAVES / HW;
+    const int hw = wave % HW, ph = wave / HW;
+    const int SEGH = HW * G;
+
+    // 1. tiles per segment and their exclusive prefix: each thread sums a run of segments, a wave scan
+    //    and the 8 wave totals give each run its start
+    const int per = (nseg + DV_THREADS - 1) / DV_THREADS;
+    const int s_a = min(nseg, tid * per), s_e = min(nseg, s_a + per);
+    int run = 0;
+    for (int sg = s_a; sg < s_e; ++sg) run += static_cast<int>(dv_tiles(pos[sg / ngroups], ctx));
+    int inc = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) sWave[wave] = inc;
+    __syncthreads();
+    int acc = inc - run;
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < DV_WAVES; ++w) {
+        acc += w < wave ? sWave[w] : 0;
+        total += sWave[w];
+    }
+    for (int sg = s_a; sg < s_e; ++sg) {
+        sPre[sg] = acc;
+        acc += static_cast<int>(dv_tiles(pos[sg / ngroups], ctx));
+    }
+    if (tid == 0) sPre[nseg] = total;
+    __syncthreads();
+    const int64_t T = total;
+    if (g == 0)
+        for (int sg = tid; sg <= nseg; sg += DV_THREADS) seg_prefix[sg] = sPre[sg];
+    const int64_t t0 = dv_share_begin(g, T, NG), t1 = dv_share_begin(g + 1, T, NG);
+    if (t0 >= t1) return;   // an empty share (T < NG): the whole workgroup leaves together
+
+    // first segment of the share: the last one starting at or before t0
+    int s0 = 0;
+    {
+        int hi = nseg - 1;
+        while (s0 < hi) {
+            const int mid = (s0 + hi + 1) >> 1;
+            if (sPre[mid] <= t0) s0 = mid;
+            else hi = mid - 1;
+        }
+    }
+
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    const int dch = lane % TT::DL, ksub = lane / TT::DL;
+    bf16_t* sVw = sV[wave];
+
+    for (int sg = s0; sg < nseg && sPre[sg] < t1; ++sg) {
+        int64_t ja, je;
+        dv_piece(g, T, NG, sPre[sg], sPre[sg + 1] - sPre[sg], &ja, &je);
+        const int b = sg / ngroups, hg = sg - b * ngroups;
+        const int c = hg * HW + hw;
+        const int L = static_cast<int>(clamp_pos(pos[b], ctx)) + 1;
+        const int last = static_cast<int>(L < je * DEC_TILE ? L : je * DEC_TILE) - 1;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t*>(kc + (static_cast<int64_t>(b) * ctx * nkv + c) * D), (short)0, -1, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t*>(vc + (static_cast<int64_t>(b) * ctx * nkv + c) * D), (short)0, -1, 0x00020000);
+        const int row_bytes = nkv * D * 2;
+
+        // B operand of S = K q: column lrow = query head c*G + lrow (zero for lrow >= G), k = dims
+        bf16x8 qfr[TT::KC32];
+        {
+            const int64_t rs = static_cast<int64_t>(nh + 2 * nkv) * D;
+            const bf16_t* qp = qkv + b * rs + static_cast<int64_t>(c * G + (lrow < G ? lrow : 0)) * D;
+            const float2* row = ROPE ? cs + clamp_pos(pos[b], rope_rows) * (D / 2) : nullptr;
+#pragma unroll
+            for (int k = 0; k < TT::KC32; ++k) {
+                const int d0 = k * 32 + lgrp * 8;
+                float f[8];
+                unpack8(*reinterpret_cast<const uint4*>(qp + d0), f);
+                if (ROPE) {
+                    if (IL) {
+                        rope8_inter(f, row, d0);
+                    } else {
+                        float g8[8];
+                        const int pd = d0 < D / 2 ? d0 + D / 2 : d0 - D / 2;
+                        unpack8(*reinterpret_cast<const uint4*>(qp + pd), g8);
+                        if (d0 < D / 2) rope8_half(f, g8, row, d0);
+                        else rope8_half(g8, f, row, pd);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = lrow < G ? f[e] : 0.f;
+                qfr[k] = __builtin_bit_cast(bf16x8, pack8(f));
+            }
+        }
+
+        float m_w = -INFINITY, l_w = 0.f;
+        f32x4 oacc[DF];
+#pragma unroll
+        for (int a = 0; a < DF; ++a) oacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        auto compute = [&](const DecTile<D>& t, int k0) {
+#pragma unroll
+            for (int it = 0; it < TT::PV_IT; ++it) {
+                const int r = it * TT::KPI + ksub;
+                *reinterpret_cast<uint4*>(&sVw[r * D + vt_phys<D>(r, dch) * 8]) = t.v[it];
+            }
+            f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int k = 0; k < TT::KC32; ++k)
+#pragma unroll
+                for (int kf = 0; kf < 2; ++kf)
+                    sacc[kf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[kf][k]), qfr[k],
+                                                                        sacc[kf], 0, 0, 0);
+            float sv[2][4], mx = -INFINITY;
+#pragma unroll
+            for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = k0 + kf * 16 + 4 * lgrp + r;
+                    const float v = key < L ? sacc[kf][r] * scale_log2 : -INFINITY;
+                    sv[kf][r] = v;
+                    mx = fmaxf(mx, v);
+                }
+            mx = rows_max(mx);
+            const float mnew = fmaxf(m_w, mx);
+            const float alpha = fast_exp2(m_w - mnew);
+            m_w = mnew;
+            float pr[2][4], ls = 0.f;
+#pragma unroll
+            for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pr[kf][r] = fast_exp2(sv[kf][r] - mnew);
+                    ls += pr[kf][r];
+                }
+            l_w = l_w * alpha + ls;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+                for (int a = 0; a < DF; ++a) oacc[a] *= alpha;
+            }
+            uint4 pu;
+            pu.x = pack_bf16x2(pr[0][0], pr[0][1]);
+            pu.y = pack_bf16x2(pr[0][2], pr[0][3]);
+            pu.z = pack_bf16x2(pr[1][0], pr[1][1]);
+            pu.w = pack_bf16x2(pr[1][2], pr[1][3]);
+            const bf16x8 pfr = __builtin_bit_cast(bf16x8, pu);
+#pragma unroll
+            for (int a = 0; a < DF; ++a) {
+                s16x4 hv[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int r = 16 * u + 4 * lgrp + (lrow >> 2);
+                    const int cc = 2 * a + ((lrow & 3) >> 1);
+                    hv[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
+                        &sVw[r * D + vt_phys<D>(r, cc) * 8 + (lrow & 1) * 4]));
+                }
+                const bf16x8 vfr =
+                    __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, pfr, oacc[a], 0, 0, 0);
+            }
+        };
+
+        // this wave's tiles of the piece: ja + ph, ja + ph + P, ... < je; loads clamp their slots to the
+        // piece's last one, so the two tiles loaded past the end stay in bounds
+        const int first = static_cast<int>(ja) + ph;
+        const int nt = first < je ? static_cast<int>((je - first + P - 1) / P) : 0;
+        const int step = P * DEC_TILE;
+        DecTile<D> ta, tb;
+        dec_load_buf<D>(ta, rk, rv, row_bytes, first * DEC_TILE, last, lrow, lgrp, dch, ksub);
+        dec_load_buf<D>(tb, rk, rv, row_bytes, first * DEC_TILE + step, last, lrow, lgrp, dch, ksub);
+        for (int i = 0; i < nt; i += 2) {
+            const int k0 = (first + i * P) * DEC_TILE;
+            compute(ta, k0);
+            dec_load_buf<D>(ta, rk, rv, row_bytes, k0 + 2 * step, last, lrow, lgrp, dch, ksub);
+            if (i + 1 < nt) compute(tb, k0 + step);
+            dec_load_buf<D>(tb, rk, rv, row_bytes, k0 + 3 * step, last, lrow, lgrp, dch, ksub);
+        }
+
+        const float lt = rows_sum(l_w);
+        float* rec = part + (static_cast<int64_t>(g + sg) * SEGH) * REC;
+        if (P == 1) {
+            // one wave per head: its G records straight from registers
+            if (lrow < G) {
+                float* r = rec + static_cast<int64_t>(hw * G + lrow) * REC;
+                if (lgrp == 0) {
+                    r[0] = m_w;
+                    r[1] = lt;
+                }
+#pragma unroll
+                for (int a = 0; a < DF; ++a)
+                    *reinterpret_cast<f32x4*>(r + DV_REC_PAD + 16 * a + 4 * lgrp) = oacc[a];
+            }
+        } else {
+            // the P waves of each head merge through LDS (phase 0 always saw key 32 * ja: M is finite)
+            if (lgrp == 0 && lrow < G) {
+                sM[wave][lrow] = m_w;
+                sL[wave][lrow] = lt;
+            }
+            if (lrow < G) {
+#pragma unroll
+                for (int a = 0; a < DF; ++a)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sO[wave][lrow][16 * a + 4 * lgrp + r] = oacc[a][r];
+            }
+            __syncthreads();
+            for (int e = tid; e < SEGH * (D + 2); e += DV_THREADS) {
+                const int hh = e / (D + 2), k = e - hh * (D + 2);
+                const int w0 = hh / G, gi = hh - w0 * G;
+                float M = -INFINITY;
+                for (int p2 = 0; p2 < P; ++p2) M = fmaxf(M, sM[w0 + HW * p2][gi]);
+                float v = 0.f;
+                for (int p2 = 0; p2 < P; ++p2) {
+                    const int w = w0 + HW * p2;
+                    const float sc = exp2f(sM[w][gi] - M);
+                    if (k == 1) v += sL[w][gi] * sc;
+                    else if (k >= 2) v += sO[w][gi][k - 2] * sc;
+                }
+                if (k == 0) v = M;
+                rec[static_cast<int64_t>(hh) * REC + (k < 2 ? k : DV_REC_PAD + k - 2)] = v;
+            }
+            __syncthreads();   // sM, sL, sO are rewritten by the next piece
+        }
+    }
+}
+
+// One wave per (b, h): log-sum-exp merge of the records of the pieces of h's segment.
+template <int D>
+__global__ __launch_bounds__(64) void attn_decode_bal_combine_kernel(const float* __restrict__ part,
+                                                                     const int* __restrict__ seg_prefix, int nseg,
+                                                                     int ngroups, int HW, int G, int NG, int nh,
+                                                                     bf16_t* __restrict__ out) {
+    constexpr int REC = D + DV_REC_PAD;
+    constexpr int DPL = D / 64;   // dims per lane
+    const int bh = blockIdx.x, lane = threadIdx.x;
+    const int b = bh / nh, h = bh - b * nh;
+    const int c = h / G, hg = c / HW, hw = c - hg * HW;
+    const int hh = hw * G + (h - c * G);
+    const int sg = b * ngroups + hg;
+    const int64_t T = seg_prefix[nseg];
+    const int64_t ps = seg_prefix[sg], ns = seg_prefix[sg + 1] - ps;
+    const int64_t g_lo = dv_owner(ps, T, NG), g_hi = dv_owner(ps + ns - 1, T, NG);
+    const int SEGH = HW * G;
+    auto live = [&](int64_t g) {
+        int64_t lo, hi;
+        dv_piece(g, T, NG, ps, ns, &lo, &hi);
+        return lo < hi;
+    };
+    auto recp = [&](int64_t g) { return part + ((g + sg) * SEGH + hh) * REC; };
+    float M = -INFINITY;
+    for (int64_t g = g_lo + lane; g <= g_hi; g += 64)
+        if (live(g)) M = fmaxf(M, recp(g)[0]);
+    M = wave_max(M);
+    float den = 0.f;
+    for (int64_t g = g_lo + lane; g <= g_hi; g += 64)
+        if (live(g)) den += recp(g)[1] * exp2f(recp(g)[0] - M);
+    den = wave_sum(den);
+    const float inv = 1.f / den;
+    float num[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) num[i] = 0.f;
+    for (int64_t g = g_lo; g <= g_hi; ++g) {
+        if (!live(g)) continue;   // uniform
+        const float* r = recp(g);
+        const float w = exp2f(r[0] - M);
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) num[i] += w * r[DV_REC_PAD + lane + 64 * i];
+    }
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) out[static_cast<int64_t>(bh) * D + lane + 64 * i] = f2bf(num[i] * inv);
+}
+
 // ------------------------------------------------------------------ dispatch
 bool attn_mfma_supported(int dtype, int d, int nh, int nkv) {
     return dtype == LL_BF16 && (d == 64 || d == 128) && nkv > 0 && nh % nkv == 0 && (nh / nkv) <= 64;
@@ -1317,15 +1643,68 @@ hipError_t launch_attn_prefill(int dtype, const void* qkv, const int64_t* pos, c
     return hipGetLastError();
 }
 
+// workgroups of the balanced decode kernel: one per compute unit (looked up once), at most DV_MAX_WG
+static int dv_workgroups() {
+    static const int n = [] {
+        int dev = 0, cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+            cu = 256;
+        return cu < DV_MAX_WG ? cu : DV_MAX_WG;
+    }();
+    return n;
+}
+
+// head groups of the balanced kernel (HW = min(n_kv, 8) heads each), or 0 when it does not apply
+static int dv_groups(int64_t B, int64_t nkv, int64_t ctx) {
+    const bool shape = nkv <= 8 ? 8 % nkv == 0 : nkv % 8 == 0;
+    if (!shape) return 0;
+    const int64_t ng = nkv <= 8 ? 1 : nkv / 8;
+    if (B * ng > DV_MAX_SEGS) return 0;
+    if (B * ng * ((ctx + DEC_TILE - 1) / DEC_TILE) >= (int64_t(1) << 31)) return 0;
+    // buffer offsets: one sequence's cache (ctx rows of n_kv heads of <= 128 bf16 dims) below 2^31 bytes
+    if (ctx * nkv * 128 * 2 >= (int64_t(1) << 31)) return 0;
+    return static_cast<int>(ng);
+}
+
+static size_t dv_workspace_bytes(int64_t B, int64_t nh, int64_t d, int64_t nseg) {
+    const size_t rec = static_cast<size_t>((DV_MAX_WG + nseg) * nh * (d + DV_REC_PAD)) * sizeof(float);
+    return ((rec + 255) & ~static_cast<size_t>(255)) + static_cast<size_t>(nseg + 1) * sizeof(int);
+}
+
 size_t attn_decode_workspace_bytes(int64_t B, int64_t nh, int64_t d, int64_t ctx) {
-    return static_cast<size_t>(B * nh * dec_nsplit(B, nh, ctx) * (d + 2)) * sizeof(float);
+    const size_t split = static_cast<size_t>(B * nh * dec_nsplit(B, nh, ctx) * (d + 2)) * sizeof(float);
+    // the balanced kernel: records of at most DV_MAX_WG + B * max(1, nh / 8) pieces of at most nh heads each
+    const int64_t nseg = B * (nh >= 8 ? nh / 8 : 1);
+    const size_t bal = dv_workspace_bytes(B, nh, d, nseg);
+    return split > bal ? split : bal;
 }
 
 template <int D, int G, bool ROPE, bool IL>
 static hipError_t decode_go(const void* qkv, const int64_t* pos, const RopeTab* tab, const void* kc, const void* vc,
                             int64_t ctx, void* o, int B, int nh, int nkv, void* ws, hipStream_t st) {
-    const int nsplit = dec_nsplit(B, nh, ctx);
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
+    const int ngroups = dv_groups(B, nkv, ctx);
+    if (ngroups > 0) {
+        const int HW = nkv < 8 ? nkv : 8;
+        const int nseg = B * ngroups;
+        const int NG = dv_workgroups();
+        const size_t rec = static_cast<size_t>((DV_MAX_WG + nseg) * static_cast<int64_t>(HW * G) * (D + DV_REC_PAD)) *
+                           sizeof(float);
+        float* part = static_cast<float*>(ws);
+        int* prefix = reinterpret_cast<int*>(static_cast<char*>(ws) + ((rec + 255) & ~static_cast<size_t>(255)));
+        hipLaunchKernelGGL((attn_decode_bal_kernel<D, G, ROPE, IL>), dim3(NG), dim3(DV_THREADS), 0, st,
+                           static_cast<const bf16_t*>(qkv), pos, tab ? tab->cs : nullptr, tab ? tab->rows : 1,
+                           static_cast<const bf16_t*>(kc), static_cast<const bf16_t*>(vc), ctx, part, prefix, nseg,
+                           ngroups, HW, nh, nkv, scale_log2);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_decode_bal_combine_kernel<D>, dim3(B * nh), dim3(64), 0, st,
+                           static_cast<const float*>(part), static_cast<const int*>(prefix), nseg, ngroups, HW, G, NG,
+                           nh, static_cast<bf16_t*>(o));
+        return hipGetLastError();
+    }
+    const int nsplit = dec_nsplit(B, nh, ctx);
     const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(B) * nsplit * nkv);
     hipLaunchKernelGGL((attn_decode_split_kernel<D, G, ROPE, IL>), dim3(blocks), dim3(DEC_THREADS), 0, st,
                        static_cast<const bf16_t*>(qkv), pos, tab ? tab->cs : nullptr, tab ? tab->rows : 1,
