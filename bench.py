@@ -6,8 +6,9 @@ Prints one JSON line: tokens/s, per-stage times from HIP events recorded by the 
 launch stream during the timed steps, the roofline position of the dominant kernel (the fused
 gate_up GEMM) and the fp64 CPU oracle timed on a bounded sample of the same workload.
 
-The headline run also times the 8B decode step (B=64 against 8192-slot KV caches, caches flushed before
-each call) and reports it under "decode" with its HBM GB/s.
+The headline run also times, cache-cold (a 512 MiB read before each call), the stand-alone RMSNorm on the
+workload's hidden states ("rmsnorm_cold") and the 8B decode step (B=64 against 8192-slot KV caches,
+"decode"), each with its HBM GB/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-cpu-baseline]
 """
@@ -170,8 +171,67 @@ def cpu_baseline(cfg, W_bits, x_bits, tokens):
     t0 = time.perf_counter()
     ref.layer_prefill(c, W, x, pos, c.S)
     dt = time.perf_counter() - t0
-    return {"value": c.B * c.S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{sample}, fp64 NumPy, {dt:.1f} s"}
+    return {"value": c.B * c.S / dt, "unit": "tokens/s", "cores": int(threads), "cpu_model": cpu_model(),
+            "kind": "oracle", "sample": f"{sample}, fp64 NumPy, {dt:.1f} s"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first /proc/cpuinfo entry) and its logical CPU count."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{name} ({os.cpu_count()} logical CPUs)"
+
+
+FLUSH_BYTES = 512 << 20
+
+
+def cache_flusher(torch, dev):
+    """A 512 MiB buffer whose full read (outside any timed region) evicts L2 and the 256 MB Infinity Cache
+    with clean lines, so the next kernel starts cache-cold without write-backs of dirty lines."""
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def flush():
+        buf.amax()
+    return flush
+
+
+def rmsnorm_cold(L, torch, np, cfg, W, steps=30):
+    """The stand-alone RMSNorm on the workload's [B*S, H] hidden states, cache-cold: a 512 MiB read before
+    each call, each call timed by HIP events on its stream; median, p10, p90 and HBM GB/s of its
+    algorithmic bytes (read x and the gain, write y)."""
+    from synth_inputs import make_hidden
+    dev = "cuda:0"
+    x = torch.from_numpy(np.ascontiguousarray(make_hidden(cfg, seed=0)).view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty_like(x)
+    flush = cache_flusher(torch, dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        L.rmsnorm(x, W["g_attn"], cfg.eps, out=y)
+    times = []
+    for _ in range(steps):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        L.rmsnorm(x, W["g_attn"], cfg.eps, out=y)
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    ms = times[len(times) // 2]
+    nbytes = 2 * x.numel() * 2 + cfg.hidden * 2
+    return {"kernel": "rmsnorm_vec_kernel", "rows": cfg.B * cfg.S, "hidden": cfg.hidden,
+            "timing": "median of per-call HIP events, 512 MiB read before each call (cache-cold)",
+            "ms": round(ms, 4), "p10_ms": round(times[len(times) // 10], 4),
+            "p90_ms": round(times[(9 * len(times)) // 10], 4), "algorithmic_bytes": nbytes,
+            "hbm_gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / MI355X_HBM_GBS, 4)}
 
 
 def lib_config(L, cfg, torch):
@@ -417,9 +477,9 @@ def decode_bytes(cfg, pos_np):
 
 
 def run_decode(L, torch, np, cfg, W, steps, warmup, cold):
-    """Decode layer calls. cold=True: before each call 512 MiB of scratch is written (outside the timed
-    region) so that L2 and the Infinity Cache start cold, and each call is timed by HIP events on the
-    launch stream; the median is reported. cold=False: `steps` calls back to back, wall clock."""
+    """Decode layer calls. cold=True: before each call a 512 MiB buffer is read (outside the timed region)
+    so that L2 and the Infinity Cache start cold, and each call is timed by HIP events on the launch
+    stream; the median is reported. cold=False: `steps` calls back to back, wall clock."""
     dev = "cuda:0"
     x, pos, pos_np, kc, vc = decode_inputs(L, torch, np, cfg, W)
     lc = lib_config(L, cfg, torch)
@@ -434,11 +494,11 @@ def run_decode(L, torch, np, cfg, W, steps, warmup, cold):
     torch.cuda.synchronize()
     L.profile_begin(steps)
     if cold:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        flush = cache_flusher(torch, dev)
         stream = torch.cuda.current_stream()
         times = []
         for _ in range(steps):
-            flush.fill_(1)
+            flush()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             call()
@@ -467,7 +527,7 @@ def decode_summary(cfg, ms, p10, p90, stages, pos_np, cold):
     gemm_ms = sum(stage_ms(stages, k) for k in ("qkv_proj", "o_proj_residual", "gate_up_silu", "down_residual"))
     rec = {"workload": f"Llama-3-8B-shaped decode step, B={cfg.B} against [{cfg.B}, {cfg.ctx}, {cfg.n_kv_heads}, "
                        f"{cfg.head_dim}] bf16 K/V caches, positions uniform on [1024, {cfg.ctx})",
-           "timing": "median of per-call HIP events, caches flushed before each call" if cold
+           "timing": "median of per-call HIP events, 512 MiB read before each call (cache-cold)" if cold
            else "back-to-back calls, wall clock",
            "ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.B / (ms / 1e3), 1),
            "algorithmic_bytes": tot, "hbm_gbs": round(tot / (ms / 1e3) / 1e9, 1),
@@ -540,7 +600,7 @@ def main():
                "data": "synthetic (seeded N(0,1) hidden and caches, N(0,0.02) weights, 1+N(0,0.1) gains)",
                "config": {"workload": summ["workload"], "B": cfg.B, "ctx": cfg.ctx, **shape},
                "hbm_gbs": summ["hbm_gbs"], "stages_ms": summ["stages_ms"],
-               "roofline": {"kernel": "attention stage (attn_decode_split_kernel + combine; the cache append rides in the QKV reduce)",
+               "roofline": {"kernel": "attention stage (attn_decode_bal_kernel + combine; the cache append rides in the QKV reduce)",
                             "bound": "hbm", "achieved": round(kvb / (attn_ms / 1e3) / 1e9, 1),
                             "peak": MI355X_HBM_GBS, "unit": "GB/s",
                             "frac": round(kvb / (attn_ms / 1e3) / 1e9 / MI355X_HBM_GBS, 4), "traffic": None},
@@ -597,7 +657,7 @@ def main():
         "attention_mfma_util_pct": round(100.0 * attn_flops / (stage_ms(stages, "attention") / 1e3) / 1e12
                                          / MI355X_BF16_DENSE_TFLOPS, 2),
         "gemm_mfma_util_pct": round(100.0 * gemm_flops / (gemm_ms / 1e3) / 1e12 / MI355X_BF16_DENSE_TFLOPS, 2),
-        "rmsnorm_hbm_gbs": round(norm_bytes / (norm_ms / 1e3) / 1e9, 1),
+        "rmsnorm_hbm_gbs": round(norm_bytes / (norm_ms / 1e3) / 1e9, 1),   # in-layer (warm) stages
         "stages_ms": {k: round(v[0] / v[1], 4) for k, v in stages.items()},
         "roofline": {
             "kernel": "gemm_bf16_mfma32_kernel<EPI_SILU> (fused gate_up + silu*up)",
@@ -610,6 +670,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.workload == WORKLOAD:
+        rec["rmsnorm_cold"] = rmsnorm_cold(L, torch, np, cfg, W)
     if args.workload == WORKLOAD and not args.no_decode:
         dcfg = CONFIGS["llama3_8b_decode"]      # same 8B weights (same seed and shapes)
         rec["decode"] = decode_summary(dcfg, *run_decode(L, torch, np, dcfg, W, 30, 3, cold=True), cold=True)

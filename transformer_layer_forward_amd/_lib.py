@@ -14,7 +14,8 @@ from typing import Optional
 import torch  # loaded first so the library binds to the HIP runtime torch already holds
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libllama_layer.so")
+# LLAMA_LAYER_LIB selects another build of the same library (the CPU checks load the host-sanitized one)
+LIB_PATH = os.environ.get("LLAMA_LAYER_LIB") or os.path.join(_PKG, "libllama_layer.so")
 
 LL_OK, LL_EINVAL, LL_EUNSUPPORTED, LL_EHIP, LL_ENOMEM = range(5)
 LL_F32, LL_BF16 = 0, 1

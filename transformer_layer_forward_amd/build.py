@@ -1,7 +1,9 @@
 """Build the gfx950 HIP library ``libllama_layer.so`` in-tree with hipcc.
 
 Every call recompiles all sources, so a stale library is never reused.
-Usage: python -m transformer_layer_forward_amd.build
+Usage: python -m transformer_layer_forward_amd.build [--sanitize]
+(--sanitize: libllama_layer_asan.so, host code under AddressSanitizer and UndefinedBehaviorSanitizer, for
+the CPU checks of the C ABI; it is never loaded on the GPU.)
 """
 from __future__ import annotations
 
@@ -39,13 +41,37 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the gfx950 library)")
 
 
-def build(verbose: bool = False) -> str:
+ASAN_LIB_PATH = os.path.join(PKG, "libllama_layer_asan.so")
+# host-side AddressSanitizer + UndefinedBehaviorSanitizer for the CPU checks of the C ABI's host logic
+# (argument validation, workspace carving, the RoPE table map); the device code is built as usual
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (preloaded by processes that load the
+    sanitized library)."""
+    clang = os.path.join(os.path.dirname(_hipcc()), "..", "lib", "llvm", "bin", "clang")
+    for cand in (clang, "/opt/rocm/llvm/bin/clang", shutil.which("clang")):
+        if cand and os.path.exists(cand):
+            r = subprocess.run([cand, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+            path = r.stdout.strip()
+            if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    raise RuntimeError("the clang AddressSanitizer runtime was not found")
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every source and link the library; sanitize=True builds libllama_layer_asan.so with the
+    host code under ASan and UBSan instead."""
     hipcc = _hipcc()
+    flags = HIPCC_FLAGS + (SANITIZE_HOST if sanitize else [])
+    out_path = ASAN_LIB_PATH if sanitize else LIB_PATH
     tmp = tempfile.mkdtemp(prefix="llbuild_")
     try:
         def compile_one(src):
             obj = os.path.join(tmp, src + ".o")
-            cmd = [hipcc, *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *flags, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -58,16 +84,18 @@ def build(verbose: bool = False) -> str:
 
         with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
             objs = list(ex.map(compile_one, SOURCES))
-        out_tmp = LIB_PATH + ".tmp"
-        cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out_tmp, *objs]
+        out_tmp = out_path + ".tmp"
+        link = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-shared-libasan"] if sanitize else []
+        cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *link, "-o", out_tmp, *objs]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{r.stderr}")
-        os.replace(out_tmp, LIB_PATH)
+        os.replace(out_tmp, out_path)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB_PATH
+    return out_path
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))
