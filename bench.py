@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="combine rocprofv3 FETCH_SIZE and WRITE_SIZE databases (bench + copy calibration) "
                          "into the per-launch HBM traffic record of the gate_up kernel and exit")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DB",
+                    help="per-kernel medians of the rocprofv3 --pmc counters in these databases (and derived MFMA "
+                         "busy share, shader clock, HBM bytes) as a markdown table, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the bench, run a plain 1 GiB device-to-device copy 3 times (counter calibration)")
     return ap.parse_args()
@@ -107,6 +110,73 @@ def pmc_summary(fetch_db: str, write_db: str) -> None:
     if None not in (f_gu, w_gu, f_scale, w_scale):
         rec["hbm_bytes_per_launch"] = round((f_gu * f_scale + w_gu * w_scale) * 1024.0)
     print(json.dumps(rec, indent=1))
+
+
+SIMDS = 1024   # 256 compute units x 4 SIMDs
+
+
+def counter_summary(dbs) -> None:
+    """Per kernel and grid size (the library's own kernels and the 1 GiB copy used for calibration): dispatches, median
+    duration and the median per dispatch of every counter found in the databases. SQ counters are summed
+    over the instances rocprofv3 reports, GRBM_GUI_ACTIVE takes their maximum. Derived:
+    mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs), the matrix cores' busy share per
+    shader clock; clock = GRBM_GUI_ACTIVE / duration; bf16_tflops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 /
+    duration; FETCH_SIZE and WRITE_SIZE are in KiB."""
+    import sqlite3
+    vals, durs = {}, {}
+    for db in dbs:
+        con = sqlite3.connect(db)
+        rows = con.execute("select name, dispatch_id, counter_name, counter_value, duration from pmc_events").fetchall()
+        grid = dict(con.execute("select dispatch_id, max(grid_size) from counters_collection group by dispatch_id"))
+        per = {}
+        for name, disp, cname, v, dur in rows:
+            key = (db, disp)
+            # one kernel serves several projections: the grid size tells them apart
+            rec = per.setdefault(key, {"name": f"{name.split('(')[0]} grid {grid.get(disp)}", "dur": dur, "c": {}})
+            acc = rec["c"].setdefault(cname, [])
+            acc.append(v)
+        # one kernel and grid size can still serve two projections of different K (o_proj and down at the
+        # 8B prefill shape): dispatches of one key whose durations differ by more than 2x form two groups
+        bykey = {}
+        for (db_, disp), rec in per.items():
+            bykey.setdefault(rec["name"], []).append(rec)
+        for name, recs in bykey.items():
+            ds = sorted(r["dur"] for r in recs if r["dur"])
+            if len(ds) >= 2 and ds[-1] > 2.0 * ds[0]:
+                cut = max(range(1, len(ds)), key=lambda i: ds[i] / ds[i - 1])
+                thr = ds[cut]
+                for r in recs:
+                    r["name"] = f"{name} ({'long' if r['dur'] and r['dur'] >= thr else 'short'} dispatches)"
+        for (db_, disp), rec in per.items():
+            name = rec["name"]
+            if not (name.startswith("void ll::") or name.startswith("ll::") or "copyBuffer" in name):
+                continue
+            short = name.replace("void ", "")
+            d = durs.setdefault(short, [])
+            if rec["dur"]:
+                d.append(rec["dur"])
+            for cname, vs in rec["c"].items():
+                agg = max(vs) if cname.startswith("GRBM") else sum(vs)
+                vals.setdefault(short, {}).setdefault(cname, []).append(agg)
+
+    def med(xs):
+        xs = sorted(xs)
+        return xs[len(xs) // 2] if xs else None
+
+    cols = sorted({c for v in vals.values() for c in v})
+    print("| kernel | dispatches | median us | " + " | ".join(cols) + " | mfma_busy | clock GHz | bf16 TFLOP/s |")
+    print("|---" * (len(cols) + 6) + "|")
+    for k in sorted(vals, key=lambda k: -(med(durs.get(k, [])) or 0) * len(durs.get(k, []))):
+        c = {n: med(v) for n, v in vals[k].items()}
+        dur_ns = med(durs.get(k, []))
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        grbm = c.get("GRBM_GUI_ACTIVE")
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        mb = f"{busy / (grbm * SIMDS):.3f}" if busy is not None and grbm else ""
+        clk = f"{grbm / dur_ns:.2f}" if grbm and dur_ns else ""
+        tf = f"{mops * 512 / (dur_ns * 1e-9) / 1e12:.0f}" if mops and dur_ns else ""
+        cells = " | ".join(f"{c[n]:.4g}" if c.get(n) is not None else "" for n in cols)
+        print(f"| `{k[:90]}` | {len(durs.get(k, []))} | {dur_ns / 1e3 if dur_ns else 0:.1f} | {cells} | {mb} | {clk} | {tf} |")
 
 
 def rocpd_summary(db: str) -> None:
@@ -548,6 +618,9 @@ def main():
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
         return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (each MI355X runs the whole "
               "layer on its own sequences; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
@@ -607,6 +680,8 @@ def main():
                "cold": decode_summary(cfg, *run_decode(L, torch, np, cfg, W, args.steps, 2, cold=True), cold=True),
                "cpu_baseline": None}
         print(json.dumps(rec), flush=True)
+        if args.copy_calibration:
+            copy_calibration()
         return
 
     if chunk:

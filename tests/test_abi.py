@@ -34,6 +34,19 @@ def test_library_exports_every_declared_symbol():
     assert set(_lib.EXPORTED) == set(_declared_functions())
 
 
+def test_library_resolves_all_of_its_own_symbols():
+    """Every kernel the host code launches has its host-side stub in the library: no symbol of the
+    library's own namespace is left undefined (a missing stub would only fail when the library loads)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    own = [l for l in out.splitlines() if "_ZN2ll" in l]
+    assert not own, own[:5]
+
+
 def test_struct_layouts_match_header():
     # ll_rope: 2 x int32 + 4 x double + int64; ll_layer_cfg: 5 x int64 + double + ll_rope + 2 x int32
     assert ctypes.sizeof(_lib.LLRope) == 48

@@ -132,6 +132,30 @@ def test_swiglu_mlp_wide_tiles_sampled_rows(with_residual):
         assert ref.max_rel_err(got, want) <= tol(dtype)
 
 
+@pytest.mark.parametrize("M,H,I", [(2300, 4096, 14208), (2560, 2048, 8192)])
+def test_swiglu_mlp_many_tiles_sampled_rows(M, H, I):
+    """Shapes with several 256 x 256 tiles per compute unit and a ragged last token tile.
+    M = 2300, I = 14208: gate_up has 9 x 111 = 999 tiles (not a multiple of 8: the plain tile order instead of
+    the per-XCD one); M = 2560, H = 2048, I = 8192: gate_up 10 x 64 = 640 tiles (per-XCD order), down 10 x 8 =
+    80 tiles (K split). 24 sampled rows (first, last, the edges of the last token tile, seeded), with the
+    residual."""
+    require_gpu()
+    dtype = "bf16"
+    x = normal(6, 150, (M, H), dtype)
+    wgu = normal(6, 151, (2 * I, H), dtype, std=0.02)
+    wd = normal(6, 152, (H, I), dtype, std=0.02)
+    r = normal(6, 153, (M, H), dtype)
+    out = L.swiglu_mlp(to_dev(x, dtype), to_dev(wgu, dtype), to_dev(wd, dtype), residual=to_dev(r, dtype))
+    last0 = (M - 1) // 256 * 256
+    rows = sorted({0, 255, 256, last0, M - 1, *np.random.default_rng([8, M]).integers(0, M, 19).tolist()})
+    want = ref.linear(ref.swiglu_act(bits_to_f64(x, dtype)[rows], bits_to_f64(wgu, dtype), I), bits_to_f64(wd, dtype))
+    got = to_f64(out)[rows]
+    rr = bits_to_f64(r, dtype)[rows]
+    assert ref.max_rel_err(got, want + rr) <= tol(dtype)
+    bound = tol(dtype) * np.max(np.abs(want)) + 2.0 ** -8 * np.max(np.abs(got))
+    assert np.max(np.abs(got - rr - want)) <= bound
+
+
 # ------------------------------------------------------------------ prefill attention
 PREFILL = [
     # dtype, B, S, nh, nkv, d

@@ -630,6 +630,10 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
         const bf16x8 vfr = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h_[0], h_[1], 0, 1, 2, 3, 4, 5, 6, 7)); \
         oacc[a][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, pfr[0][t], oacc[a][0], 0, 0, 0);          \
         oacc[a][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, pfr[1][t], oacc[a][1], 0, 0, 0);          \
+    }                                                                                                      \
+    if constexpr (MSUM) {                                                                                  \
+        lacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pfr[0][t], lacc[0], 0, 0, 0);              \
+        lacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pfr[1][t], lacc[1], 0, 0, 0);              \
     }
 #define PD_EXP_HALF(SC, t)                                                                                 \
     _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                                     \
@@ -637,7 +641,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
         _Pragma("unroll") for (int u = 0; u < 2; ++u)                                                      \
             _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                                \
                 p_[u][r] = fast_exp2(SC[2 * (t) + u][qf][r]);                                              \
-                ls[qf] += p_[u][r];                                                                        \
+                if constexpr (!MSUM) ls[qf] += p_[u][r];                                                   \
             }                                                                                              \
         uint4 u_;                                                                                          \
         u_.x = pack_bf16x2(p_[0][0], p_[0][1]);                                                            \
@@ -647,7 +651,13 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
         pfr[qf][t] = __builtin_bit_cast(bf16x8, u_);                                                       \
     }
 
+    // D = 64: the row sums of P run on the matrix cores (ones x P^T into lacc, whose every element holds its
+    // query's sum of the bf16 P actually used by P V), which takes 32 vector adds per tile off the
+    // vector-bound loop; D = 128 keeps the vector sums (its registers are full)
+    constexpr bool MSUM = D == 64;
     float m_i[2] = {0.f, 0.f}, l_i[2] = {0.f, 0.f};
+    f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
     f32x4 oacc[C::DF][2];
 #pragma unroll
     for (int a = 0; a < C::DF; ++a) oacc[a][0] = oacc[a][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -673,7 +683,10 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
         /* K(j+2) into the buffer K(j) used, V(j+1) into the buffer V(j-1) used: both free since the */    \
         /* barrier that ended the previous iteration                                                 */    \
         issue_tiles(j + 2, (j - j0) & 1, j + 1, (j - j0 + 1) & 1);                                         \
-        if ((j + 1) * C::BKV - 1 > lo) {                                                                   \
+        /* (branch hints keep these rare paths out of line: predicated, they cost more vector work */     \
+        /*  per tile than the softmax itself)                                                        */     \
+        if (__builtin_expect((j + 1) * C::BKV - 1 > lo, 0)) {                                              \
+            __asm__ volatile("");                                                                          \
             _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                             \
                 _Pragma("unroll") for (int kf = 0; kf < 4; ++kf)                                           \
                     _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                        \
@@ -709,11 +722,13 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
             any_sub_ |= sub_[qf] != 0.f;                                                                   \
         }                                                                                                  \
         /* stage 2 (rare): re-reference tile j's scores, rescale O and l where the reference moved */     \
-        if (__any(any_sub_)) {                                                                             \
+        if (__builtin_expect(__any(any_sub_), 0)) {                                                        \
+            __asm__ volatile("");   /* a side effect: the block cannot be predicated into the hot path */ \
             _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                             \
                 const float alpha = fresh_[qf] ? 1.f : fast_exp2(-shift_[qf]);                             \
                 m_i[qf] = (SPLIT && fresh_[qf] ? 0.f : m_i[qf]) + shift_[qf];                              \
                 l_i[qf] *= alpha;                                                                          \
+                if constexpr (MSUM) lacc[qf] *= alpha;                                                     \
                 _Pragma("unroll") for (int a = 0; a < C::DF; ++a) oacc[a][qf] *= alpha;                    \
                 _Pragma("unroll") for (int kf = 0; kf < 4; ++kf) SC[kf][qf] -= sub_[qf];                   \
             }                                                                                              \
@@ -753,7 +768,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     if constexpr (SPLIT) {
 #pragma unroll
         for (int qf = 0; qf < 2; ++qf) {
-            const float lsum = rows_sum(l_i[qf]);
+            const float lsum = MSUM ? lacc[qf][0] : rows_sum(l_i[qf]);
             const int qi = q0 + qf * 16 + lrow;
             if (qi >= S) continue;
             float* rec = part + ((static_cast<int64_t>(seq0) + qi) * nh + h) * nsplit * (D + 4) +
@@ -770,7 +785,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_direct_kernel(
     }
 #pragma unroll
     for (int qf = 0; qf < 2; ++qf) {
-        const float inv = 1.f / rows_sum(l_i[qf]);
+        const float inv = 1.f / (MSUM ? lacc[qf][0] : rows_sum(l_i[qf]));
         const int qi = q0 + qf * 16 + lrow;
         if (qi >= S) continue;
         bf16_t* op = out + (static_cast<int64_t>(seq0) + qi) * nh * D + static_cast<int64_t>(h) * D;
@@ -1521,7 +1536,10 @@ __global__ __launch_bounds__(DV_THREADS) void attn_decode_bal_kernel(
     }
 }
 
-// One wave per (b, h): log-sum-exp merge of the records of the pieces of h's segment.
+// One wave per (b, h): log-sum-exp merge of the records of the pieces of h's segment. The pieces' weights
+// exp2(m_p - M) are formed once (a lane per piece) and kept in LDS; the weighted sum then loads every
+// piece's o with no branch between loads (pieces of workgroups whose share misses the segment have
+// weight zero; their record slots are in bounds but unwritten, so their values are selected away).
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_bal_combine_kernel(const float* __restrict__ part,
                                                                      const int* __restrict__ seg_prefix, int nseg,
@@ -1529,6 +1547,7 @@ __global__ __launch_bounds__(64) void attn_decode_bal_combine_kernel(const float
                                                                      bf16_t* __restrict__ out) {
     constexpr int REC = D + DV_REC_PAD;
     constexpr int DPL = D / 64;   // dims per lane
+    __shared__ float sw[DV_MAX_WG];
     const int bh = blockIdx.x, lane = threadIdx.x;
     const int b = bh / nh, h = bh - b * nh;
     const int c = h / G, hg = c / HW, hw = c - hg * HW;
@@ -1537,31 +1556,43 @@ __global__ __launch_bounds__(64) void attn_decode_bal_combine_kernel(const float
     const int64_t T = seg_prefix[nseg];
     const int64_t ps = seg_prefix[sg], ns = seg_prefix[sg + 1] - ps;
     const int64_t g_lo = dv_owner(ps, T, NG), g_hi = dv_owner(ps + ns - 1, T, NG);
+    const int np = static_cast<int>(g_hi - g_lo + 1);
     const int SEGH = HW * G;
-    auto live = [&](int64_t g) {
+    const float* rec0 = part + ((g_lo + sg) * SEGH + hh) * REC;   // piece p's record: rec0 + p * SEGH * REC
+    const int64_t pstride = static_cast<int64_t>(SEGH) * REC;
+    auto live = [&](int p) {
         int64_t lo, hi;
-        dv_piece(g, T, NG, ps, ns, &lo, &hi);
+        dv_piece(g_lo + p, T, NG, ps, ns, &lo, &hi);
         return lo < hi;
     };
-    auto recp = [&](int64_t g) { return part + ((g + sg) * SEGH + hh) * REC; };
     float M = -INFINITY;
-    for (int64_t g = g_lo + lane; g <= g_hi; g += 64)
-        if (live(g)) M = fmaxf(M, recp(g)[0]);
+    for (int p = lane; p < np; p += 64)
+        if (live(p)) M = fmaxf(M, rec0[p * pstride]);
     M = wave_max(M);
     float den = 0.f;
-    for (int64_t g = g_lo + lane; g <= g_hi; g += 64)
-        if (live(g)) den += recp(g)[1] * exp2f(recp(g)[0] - M);
+    for (int p = lane; p < np; p += 64) {
+        float w = 0.f;
+        if (live(p)) {
+            w = exp2f(rec0[p * pstride] - M);
+            den += w * rec0[p * pstride + 1];
+        }
+        sw[p] = w;
+    }
     den = wave_sum(den);
     const float inv = 1.f / den;
     float num[DPL];
 #pragma unroll
     for (int i = 0; i < DPL; ++i) num[i] = 0.f;
-    for (int64_t g = g_lo; g <= g_hi; ++g) {
-        if (!live(g)) continue;   // uniform
-        const float* r = recp(g);
-        const float w = exp2f(r[0] - M);
+    // the wave's own LDS writes above are complete for its reads below (one wave, in order)
+#pragma unroll 4
+    for (int p = 0; p < np; ++p) {
+        const float w = sw[p];
+        const float* r = rec0 + p * pstride + DV_REC_PAD + lane;
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) num[i] += w * r[DV_REC_PAD + lane + 64 * i];
+        for (int i = 0; i < DPL; ++i) {
+            const float o = r[64 * i];
+            num[i] += w != 0.f ? w * o : 0.f;
+        }
     }
 #pragma unroll
     for (int i = 0; i < DPL; ++i) out[static_cast<int64_t>(bh) * D + lane + 64 * i] = f2bf(num[i] * inv);
