@@ -1536,19 +1536,22 @@ __global__ __launch_bounds__(DV_THREADS) void attn_decode_bal_kernel(
     }
 }
 
-// One wave per (b, h): log-sum-exp merge of the records of the pieces of h's segment. The pieces' weights
+// One wave per (b, h), four per workgroup: log-sum-exp merge of the records of the pieces of h's segment. The pieces' weights
 // exp2(m_p - M) are formed once (a lane per piece) and kept in LDS; the weighted sum then loads every
 // piece's o with no branch between loads (pieces of workgroups whose share misses the segment have
 // weight zero; their record slots are in bounds but unwritten, so their values are selected away).
 template <int D>
-__global__ __launch_bounds__(64) void attn_decode_bal_combine_kernel(const float* __restrict__ part,
+__global__ __launch_bounds__(256) void attn_decode_bal_combine_kernel(const float* __restrict__ part,
                                                                      const int* __restrict__ seg_prefix, int nseg,
                                                                      int ngroups, int HW, int G, int NG, int nh,
-                                                                     bf16_t* __restrict__ out) {
+                                                                     int nbh, bf16_t* __restrict__ out) {
     constexpr int REC = D + DV_REC_PAD;
     constexpr int DPL = D / 64;   // dims per lane
-    __shared__ float sw[DV_MAX_WG];
-    const int bh = blockIdx.x, lane = threadIdx.x;
+    __shared__ float sws[4][DV_MAX_WG];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int bh = blockIdx.x * 4 + wv;
+    if (bh >= nbh) return;   // whole waves leave; the kernel has no workgroup barrier
+    float* sw = sws[wv];
     const int b = bh / nh, h = bh - b * nh;
     const int c = h / G, hg = c / HW, hw = c - hg * HW;
     const int hh = hw * G + (h - c * G);
@@ -1730,9 +1733,9 @@ static hipError_t decode_go(const void* qkv, const int64_t* pos, const RopeTab* 
                            ngroups, HW, nh, nkv, scale_log2);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_decode_bal_combine_kernel<D>, dim3(B * nh), dim3(64), 0, st,
+        hipLaunchKernelGGL(attn_decode_bal_combine_kernel<D>, dim3((B * nh + 3) / 4), dim3(256), 0, st,
                            static_cast<const float*>(part), static_cast<const int*>(prefix), nseg, ngroups, HW, G, NG,
-                           nh, static_cast<bf16_t*>(o));
+                           nh, B * nh, static_cast<bf16_t*>(o));
         return hipGetLastError();
     }
     const int nsplit = dec_nsplit(B, nh, ctx);
