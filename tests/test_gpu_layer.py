@@ -117,9 +117,21 @@ def test_layer_zero_branches_is_identity():
     assert torch.equal(out, x)
 
 
-@pytest.mark.parametrize("cfg", [scaled(CONFIGS["llama3_8b_decode"], B=5, ctx=1300),
-                                 scaled(CONFIGS["tiny_f32"], B=3, S=1, ctx=40, decode=True)],
-                         ids=lambda c: c.name)
+# Decode shapes of the bf16 projections that sum their K ranges in the kernel (arrival groups of one
+# 64-row block, of two blocks per 128-wide half-split RoPE head, single-range RoPE partials) and of the
+# fp32 path.
+DECODE_SMALL = [
+    scaled(CONFIGS["llama3_8b_decode"], B=5, ctx=1300),
+    scaled(CONFIGS["llama3_8b_decode"], name="8b_decode_interleaved", B=3, ctx=700,
+           rope=RopeCfg(type="llama3", theta=500000.0, factor=8.0, original_max_pos=256, interleaved=True)),
+    scaled(CONFIGS["llama32_1b_prefill"], name="1b_decode", B=7, S=1, ctx=900, decode=True),
+    scaled(CONFIGS["llama32_1b_prefill"], name="d64_odd_heads_decode", B=4, S=1, ctx=300, decode=True, hidden=384,
+           n_heads=6, n_kv_heads=3, intermediate=512),
+    scaled(CONFIGS["tiny_f32"], B=3, S=1, ctx=40, decode=True),
+]
+
+
+@pytest.mark.parametrize("cfg", DECODE_SMALL, ids=lambda c: c.name)
 def test_layer_decode_small(cfg):
     require_gpu()
     W = make_weights(cfg, seed=3)
