@@ -275,10 +275,15 @@ void ll_release_caches(void);
 /* Per-stage timing of llama_layer_forward, for benchmarking. ll_profile_begin() enables HIP event
  * markers between the stages of every later llama_layer_forward on the calling thread, clears the
  * totals and creates the events for reserve_calls calls up front (more are created on demand).
+ * ll_profile_begin_stages() does the same for the stages whose bits are set in stage_mask (bit s =
+ * stage s, 0 .. 6; LL_EINVAL for an empty mask or higher bits): only the markers those stages need
+ * are recorded, since each marker between two kernels delays the second by a few microseconds.
+ * ll_profile_begin(r) is ll_profile_begin_stages(r, 0x7F).
  * ll_profile_end() waits for the recorded events, writes the summed milliseconds and call counts of
- * up to max_stages stages (stage names from ll_profile_stage_name) and disables the markers. It
- * returns the number of stages written, or -1 on error. */
+ * up to max_stages stages (stage names from ll_profile_stage_name; stages not timed report 0 ms in
+ * 0 calls) and disables the markers. It returns the number of stages written, or -1 on error. */
 ll_status   ll_profile_begin(int32_t reserve_calls);
+ll_status   ll_profile_begin_stages(int32_t reserve_calls, uint32_t stage_mask);
 int32_t     ll_profile_end(double* stage_ms, int64_t* stage_calls, int32_t max_stages);
 const char* ll_profile_stage_name(int32_t stage);
 

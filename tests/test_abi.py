@@ -198,6 +198,18 @@ def test_profile_stage_names():
     assert lib.ll_profile_stage_name(7) == b""
 
 
+def test_profile_stage_mask_is_validated_before_any_event():
+    lib = L.load()
+    assert lib.ll_profile_begin_stages(0, 0) == _lib.LL_EINVAL
+    assert lib.ll_profile_begin_stages(0, 1 << 7) == _lib.LL_EINVAL
+    assert lib.ll_profile_begin_stages(-1, 1) == _lib.LL_EINVAL
+    with pytest.raises(ValueError):
+        L.profile_begin(0, stages=["no_such_stage"])
+    # a valid mask with no reserved events touches no device; ending with no calls timed reports nothing
+    assert lib.ll_profile_begin_stages(0, 1 << 5) == _lib.LL_OK
+    assert L.profile_end() == {}
+
+
 def test_product_path_has_no_oracle_or_cpu_fallback():
     """The binding and library sources never reference the oracle or a CPU implementation."""
     pkg = os.path.join(ROOT, "transformer_layer_forward_amd")

@@ -84,6 +84,26 @@ def test_layer_prefill_small(cfg):
     check(got, x64, want["out"], want["attn_proj"] + want["mlp_out"], cfg.dtype, cfg.name)
 
 
+def test_profile_selected_stages_only():
+    """Stage timing restricted to one stage reports that stage alone, once per call, and leaves the output
+    bit-identical to an untimed call."""
+    require_gpu()
+    cfg = scaled(CONFIGS["llama3_8b_prefill"], B=1, S=100)
+    W = dev_weights(make_weights(cfg, seed=6), cfg.dtype)
+    x = to_dev(make_hidden(cfg, seed=6), cfg.dtype)
+    pos = torch.from_numpy(make_prefill_positions(cfg)).to(DEV)
+    lc = layer_cfg(cfg)
+    plain = L.llama_layer_forward(lc, W, x, pos, kv_seq_len=cfg.S)
+    L.profile_begin(4, stages=["gate_up_silu"])
+    outs = [L.llama_layer_forward(lc, W, x, pos, kv_seq_len=cfg.S) for _ in range(3)]
+    st = L.profile_end()
+    assert set(st) == {"gate_up_silu"}
+    ms, n = st["gate_up_silu"]
+    assert n == 3 and ms > 0.0
+    for o in outs:
+        assert torch.equal(o, plain)
+
+
 def test_layer_in_place_and_causality():
     """out may equal hidden; perturbing later tokens leaves earlier rows bit-identical."""
     require_gpu()

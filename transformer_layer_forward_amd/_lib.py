@@ -28,7 +28,8 @@ EXPORTED = (
     "rmsnorm", "rope_apply", "gqa_attn_prefill", "gqa_attn_prefill_chunk_workspace_bytes", "gqa_attn_prefill_chunk",
     "gqa_attn_prefill_varlen",
     "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "swiglu_mlp_workspace_bytes", "swiglu_mlp",
-    "ll_last_error", "ll_release_caches", "ll_profile_begin", "ll_profile_end", "ll_profile_stage_name",
+    "ll_last_error", "ll_release_caches", "ll_profile_begin", "ll_profile_begin_stages", "ll_profile_end",
+    "ll_profile_stage_name",
     "ll_version",
 )
 
@@ -134,6 +135,7 @@ def load() -> ctypes.CDLL:
         "ll_last_error": (ctypes.c_char_p, []),
         "ll_release_caches": (None, []),
         "ll_profile_begin": (c_i32, [c_i32]),
+        "ll_profile_begin_stages": (c_i32, [c_i32, ctypes.c_uint32]),
         "ll_profile_end": (c_i32, [ctypes.POINTER(c_d), ctypes.POINTER(c_i64), c_i32]),
         "ll_profile_stage_name": (ctypes.c_char_p, [c_i32]),
         "ll_version": (ctypes.c_char_p, []),
@@ -436,15 +438,28 @@ def llama_model_forward(cfg: LayerConfig, model: dict, tokens: torch.Tensor, pos
 
 
 # ------------------------------------------------------------------ stage timing
-def profile_begin(reserve_calls: int = 64) -> None:
-    _check(load().ll_profile_begin(int(reserve_calls)), "ll_profile_begin")
+def profile_begin(reserve_calls: int = 64, stages=None) -> None:
+    """Time the stages of later llama_layer_forward calls on this thread: all of them, or only those named
+    in `stages` (names as profile_end reports them)."""
+    lib = load()
+    if stages is None:
+        _check(lib.ll_profile_begin(int(reserve_calls)), "ll_profile_begin")
+        return
+    names = [lib.ll_profile_stage_name(i).decode() for i in range(7)]
+    mask = 0
+    for st in stages:
+        if st not in names:
+            raise ValueError(f"unknown stage {st!r}; stages are {names}")
+        mask |= 1 << names.index(st)
+    _check(lib.ll_profile_begin_stages(int(reserve_calls), mask), "ll_profile_begin_stages")
 
 
 def profile_end() -> dict:
+    """{stage name: (summed ms, calls)} for the timed stages."""
     lib = load()
     ms = (ctypes.c_double * 8)()
     n = (ctypes.c_int64 * 8)()
     k = lib.ll_profile_end(ms, n, 8)
     if k < 0:
         raise RuntimeError(f"ll_profile_end failed: {last_error()}")
-    return {lib.ll_profile_stage_name(i).decode(): (ms[i], n[i]) for i in range(k)}
+    return {lib.ll_profile_stage_name(i).decode(): (ms[i], n[i]) for i in range(k) if n[i] > 0}

@@ -208,6 +208,10 @@ constexpr int kLayerStages = 7;
 
 struct ProfState {
     bool on = false;
+    uint32_t mask = 0;   // stages timed: bit s = stage s
+    // an event at stage boundary b (the start of stage b, the end of stage b-1) is recorded only when
+    // a timed stage needs it
+    bool boundary(int b) const { return ((mask >> b) & 1u) || (b > 0 && ((mask >> (b - 1)) & 1u)); }
     std::vector<hipEvent_t> pool;
     size_t used = 0;
     struct Call { size_t first; };
@@ -305,8 +309,13 @@ void ll_release_caches(void) {
     g_tabs.release_all();
 }
 
-ll_status ll_profile_begin(int32_t reserve_calls) {
+ll_status ll_profile_begin(int32_t reserve_calls) { return ll_profile_begin_stages(reserve_calls, 0x7Fu); }
+
+ll_status ll_profile_begin_stages(int32_t reserve_calls, uint32_t stage_mask) {
     if (reserve_calls < 0) return fail(LL_EINVAL, "reserve_calls must be >= 0");
+    if (stage_mask == 0 || (stage_mask >> kLayerStages) != 0)
+        return fail(LL_EINVAL, "stage_mask must select stages 0 .. %d", kLayerStages - 1);
+    g_prof.mask = stage_mask;
     const size_t want = static_cast<size_t>(reserve_calls) * (kLayerStages + 1);
     while (g_prof.pool.size() < want) {
         hipEvent_t e;
@@ -326,12 +335,15 @@ ll_status ll_profile_begin(int32_t reserve_calls) {
 int32_t ll_profile_end(double* stage_ms, int64_t* stage_calls, int32_t max_stages) {
     g_prof.on = false;
     for (const auto& call : g_prof.calls) {
-        hipEvent_t last = g_prof.pool[call.first + kLayerStages];
+        int lastb = kLayerStages;
+        while (!g_prof.boundary(lastb)) --lastb;   // the mask is non-empty: some boundary is recorded
+        hipEvent_t last = g_prof.pool[call.first + lastb];
         if (hipEventSynchronize(last) != hipSuccess) {
             fail(LL_EHIP, "profile event synchronize failed");
             return -1;
         }
         for (int s = 0; s < kLayerStages; ++s) {
+            if (!((g_prof.mask >> s) & 1u)) continue;
             float ms = 0.f;
             if (hipEventElapsedTime(&ms, g_prof.pool[call.first + s], g_prof.pool[call.first + s + 1]) != hipSuccess) {
                 fail(LL_EHIP, "profile elapsed time failed");
@@ -341,7 +353,7 @@ int32_t ll_profile_end(double* stage_ms, int64_t* stage_calls, int32_t max_stage
             g_prof.n[s] += 1;
         }
     }
-    const int n = std::min<int32_t>(max_stages, kLayerStages);
+    const int n = std::max<int32_t>(0, std::min<int32_t>(max_stages, kLayerStages));
     for (int i = 0; i < n; ++i) {
         if (stage_ms) stage_ms[i] = g_prof.ms[i];
         if (stage_calls) stage_calls[i] = g_prof.n[i];
@@ -641,12 +653,12 @@ static ll_status layer_forward_impl(const ll_layer_cfg* cfg, const ll_layer_weig
         for (int i = 0; i <= kLayerStages; ++i)
             if (!prof_event()) return fail(LL_EHIP, "hipEventCreate failed");
         g_prof.calls.push_back({ev0});
-        LL_CHECK_HIP(hipEventRecord(g_prof.pool[ev0], stream_h), "hipEventRecord");
+        if (g_prof.boundary(0)) LL_CHECK_HIP(hipEventRecord(g_prof.pool[ev0], stream_h), "hipEventRecord");
     }
     int stage = 0;
     auto mark = [&]() -> hipError_t {
         ++stage;
-        return prof ? hipEventRecord(g_prof.pool[ev0 + stage], stream_h) : hipSuccess;
+        return prof && g_prof.boundary(stage) ? hipEventRecord(g_prof.pool[ev0 + stage], stream_h) : hipSuccess;
     };
 
     hipError_t e;
