@@ -423,7 +423,7 @@ __device__ __forceinline__ int vt_phys(int r, int c) {
 }
 
 template <int D, int HPB, bool CACHED, bool SPLIT = false>
-__global__ __launch_bounds__(128 * HPB, (D == 64 && HPB == 2) ? 2 : 1) void attn_prefill_direct_kernel(
+__global__ __launch_bounds__(128 * HPB, HPB == 2 ? 2 : 1) void attn_prefill_direct_kernel(
     const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, bf16_t* __restrict__ out, bf16_t* __restrict__ kc,
     bf16_t* __restrict__ vc, int64_t ctx, int B, int S_max, int nh, int nkv, float scale_log2,
     const int* __restrict__ cu, int total, int nsplit, float* __restrict__ part) {
@@ -1638,10 +1638,10 @@ template <int D>
 static hipError_t prefill_hpb_sel(const void* qkv, const int64_t* pos, const RopeTab* tab, int il, void* o, void* kc,
                                   void* vc, int64_t ctx, int B, int S, int nh, int nkv, hipStream_t st) {
     const int g = nh / nkv;
-    // d = 64: two heads per workgroup and two workgroups per compute unit (the kernel is built for two
-    // waves per SIMD): the two waves on a SIMD then belong to different workgroups, whose tile barriers
-    // do not line them up (3.5% faster than four heads per workgroup; at d = 128 two heads spill)
-    if (g % 4 == 0 && D != 64) return prefill_rope_sel<D, 4>(qkv, pos, tab, il, o, kc, vc, ctx, B, S, nh, nkv, st);
+    // two heads per workgroup and two workgroups per compute unit (the kernel is built for two waves
+    // per SIMD): the two waves on a SIMD then belong to different workgroups, whose tile barriers do not
+    // line them up. In the layer this is 3% faster than four heads per workgroup at d = 128 (the few
+    // spilled registers are touched only outside the tile loop and on the masked tiles) and 18% at d = 64.
     if (g % 2 == 0) return prefill_rope_sel<D, 2>(qkv, pos, tab, il, o, kc, vc, ctx, B, S, nh, nkv, st);
     return prefill_rope_sel<D, 1>(qkv, pos, tab, il, o, kc, vc, ctx, B, S, nh, nkv, st);
 }
