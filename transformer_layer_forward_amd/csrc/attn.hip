@@ -1971,7 +1971,8 @@ template <int D>
 static hipError_t varlen_hpb_sel(const void* qkv, const int* cu, int nseq, int max_seqlen, int total, void* o, int nh,
                                  int nkv, hipStream_t st) {
     const int g = nh / nkv;
-    if (g % 4 == 0) return varlen_go<D, 4>(qkv, cu, nseq, max_seqlen, total, o, nh, nkv, st);
+    // two heads per workgroup, two workgroups per compute unit, as for prefill (0.159 -> 0.142 ms on
+    // nine packed sequences of 64-2048 tokens, 8B shape)
     if (g % 2 == 0) return varlen_go<D, 2>(qkv, cu, nseq, max_seqlen, total, o, nh, nkv, st);
     return varlen_go<D, 1>(qkv, cu, nseq, max_seqlen, total, o, nh, nkv, st);
 }
