@@ -250,6 +250,8 @@ DECODE = [
     ("bf16", 12, 900, 4, 2, 64),
     ("bf16", 48, 2000, 32, 8, 128),  # few key splits per sequence, several 128-key blocks each
     ("bf16", 64, 1200, 32, 8, 64),
+    ("bf16", 3, 700, 32, 16, 128),   # 16 kv heads: two head groups of 8 per sequence
+    ("bf16", 5, 900, 8, 1, 128),     # one kv head: the 8 waves split its tiles by phase and merge
     ("bf16", 2, 300, 4, 2, 96),      # generic kernel
     ("f32", 2, 40, 4, 2, 16),
 ]
