@@ -25,6 +25,7 @@
 //
 // fp32 path: a simple LDS-tiled FMA kernel (no bf16 or reduced-precision step anywhere).
 #include "common.h"
+#include <type_traits>
 
 namespace ll {
 
@@ -425,14 +426,19 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-    // ---- main loop. Two 64-wide K stages. At the top of iteration t every wave waits for its own loads
-    // of stage t and meets the others at a barrier: stage t is then complete in LDS and every wave is
-    // done with stage t-1, whose slot receives stage t+1, its 16 loads spread over the first two k16
-    // quarters of stage t. The last iteration re-reads the final stage into the free slot (never read),
-    // which keeps the loop free of branches.
+    // ---- main loop. Two 64-wide K stages. The prologue issues the loads of stages 0 and 1, so a tile's
+    // second stage does not wait a second memory latency. At the top of iteration t every wave waits for
+    // its own loads of stage t and meets the others at a barrier: stage t is then complete in LDS and
+    // every wave is done with stage t-1, whose slot receives stage t+1 (t >= 1), its loads spread over
+    // the first k16 quarters of stage t. The last iteration re-reads the final stage into the free slot
+    // (never read), which keeps the loop free of branches.
     const int nk = SPLIT ? (min(K, kb + kw) - kb) / MF_K : K / MF_K;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) issue1(0, kb, j);
+    if (nk > 1) {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) issue1(1, kb + MF_K, j);
+    }
     bf16x8 fa[2][FA], fb[2][4];
 #define MF_MMA2(FA, FB, p)                                                                                   \
     {                                                                                                      \
@@ -440,16 +446,11 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
         acc[a_][b_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[a_], FB[b_], acc[a_][b_], 0, 0, 0);       \
         acc[a_][b_ + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[a_], FB[b_ + 1], acc[a_][b_ + 1], 0, 0, 0); \
     }
-    // no scalar load may be outstanding at the loop head: the compiler then waits for just the first
-    // fragments of each stage instead of all of them (LDS returns in order, scalar loads do not)
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    for (int t = 0; t < nk; ++t) {
+    // one stage's matrix work; the first stage issues no loads (the prologue has issued stage 1)
+    auto stage = [&](int t, auto first) {
         const int slot = t & 1;
         const bf16_t* st = smem + slot * STAGE;
         const int kn = kb + min(t + 1, nk - 1) * MF_K;
-        MF_WAITVM0();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
             if (f < FA) fa[0][f] = *reinterpret_cast<const bf16x8*>(st + aoff[f]);
@@ -465,10 +466,28 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
                     fb[(h + 1) & 1][p] = *reinterpret_cast<const bf16x8*>(st + (boff[p] ^ (16 * (h + 1))));
                 }
                 // the next stage's loads over the first quarters (TN = 256: two, TN = 128: three)
-                if (h * PST + p < LPW) issue1(slot ^ 1, kn, h * PST + p);
+                if constexpr (!decltype(first)::value)
+                    if (h * PST + p < LPW) issue1(slot ^ 1, kn, h * PST + p);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+    };
+    // no scalar load may be outstanding at the loop head: the compiler then waits for just the first
+    // fragments of each stage instead of all of them (LDS returns in order, scalar loads do not)
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    // stage 0: its LPW loads are the oldest; the LPW of stage 1 may still be in flight
+    constexpr int W_LPW = 0x0F70 | (LPW & 15) | ((LPW >> 4) << 14);
+    static_assert(LPW < 64, "vmcnt holds 6 bits");
+    if (nk > 1) __builtin_amdgcn_s_waitcnt(W_LPW);
+    else MF_WAITVM0();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    stage(0, std::true_type{});
+    for (int t = 1; t < nk; ++t) {
+        MF_WAITVM0();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        stage(t, std::false_type{});
     }
 #undef MF_MMA2
     // ---- epilogue. Lane holds, for 32x32 block (a, b): token m = 32b + l32 of the wave's 128 and
