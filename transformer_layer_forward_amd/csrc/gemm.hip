@@ -426,12 +426,13 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-    // ---- main loop. Two 64-wide K stages. The prologue issues the loads of stages 0 and 1, so a tile's
-    // second stage does not wait a second memory latency. At the top of iteration t every wave waits for
-    // its own loads of stage t and meets the others at a barrier: stage t is then complete in LDS and
-    // every wave is done with stage t-1, whose slot receives stage t+1 (t >= 1), its loads spread over
-    // the first k16 quarters of stage t. The last iteration re-reads the final stage into the free slot
-    // (never read), which keeps the loop free of branches.
+    // ---- main loop. Two 64-wide K stages; the prologue issues the loads of stages 0 and 1. The barrier
+    // of iteration t sits before its last k16 quarter: each wave first waits for its own loads of stage
+    // t+1 and for its reads of quarter 3 of stage t (already in registers), so after the barrier stage
+    // t+1 is complete in LDS and no wave reads stage t's slot again. Quarter 3's matrix ops then hide
+    // the reads of stage t+1's first fragments, and the first half of stage t+2's loads go into stage
+    // t's slot, one per matrix-op pair; the other half follows in quarter 0 of iteration t+1. Past the
+    // last stage the loads re-read it into a slot nobody reads, which keeps the loop free of branches.
     const int nk = SPLIT ? (min(K, kb + kw) - kb) / MF_K : K / MF_K;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) issue1(0, kb, j);
@@ -446,28 +447,39 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
         acc[a_][b_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[a_], FB[b_], acc[a_][b_], 0, 0, 0);       \
         acc[a_][b_ + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[a_], FB[b_ + 1], acc[a_][b_ + 1], 0, 0, 0); \
     }
-    // one stage's matrix work; the first stage issues no loads (the prologue has issued stage 1)
+    constexpr int LH = LPW / 2;   // loads of a stage issued in the quarter after the barrier
+    // one stage's matrix work; the first issues no loads in quarter 0 (the prologue issued stage 1)
     auto stage = [&](int t, auto first) {
         const int slot = t & 1;
         const bf16_t* st = smem + slot * STAGE;
-        const int kn = kb + min(t + 1, nk - 1) * MF_K;
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            if (f < FA) fa[0][f] = *reinterpret_cast<const bf16x8*>(st + aoff[f]);
-            fb[0][f] = *reinterpret_cast<const bf16x8*>(st + boff[f]);
-        }
+        const bf16_t* stn = smem + (slot ^ 1) * STAGE;
+        const int k1 = kb + min(t + 1, nk - 1) * MF_K, k2 = kb + min(t + 2, nk - 1) * MF_K;
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
+            if (h == 3) {
+                __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int p = 0; p < PST; ++p) {
                 MF_MMA2(fa[h & 1], fb[h & 1], p)
-                if (h < 3 && p < 4) {
-                    if (p < FA) fa[(h + 1) & 1][p] = *reinterpret_cast<const bf16x8*>(st + (aoff[p] ^ (16 * (h + 1))));
-                    fb[(h + 1) & 1][p] = *reinterpret_cast<const bf16x8*>(st + (boff[p] ^ (16 * (h + 1))));
+                if (p < 4) {
+                    if (h < 3) {
+                        if (p < FA) fa[(h + 1) & 1][p] = *reinterpret_cast<const bf16x8*>(st + (aoff[p] ^ (16 * (h + 1))));
+                        fb[(h + 1) & 1][p] = *reinterpret_cast<const bf16x8*>(st + (boff[p] ^ (16 * (h + 1))));
+                    } else {   // stage t+1, quarter 0
+                        if (p < FA) fa[0][p] = *reinterpret_cast<const bf16x8*>(stn + aoff[p]);
+                        fb[0][p] = *reinterpret_cast<const bf16x8*>(stn + boff[p]);
+                    }
                 }
-                // the next stage's loads over the first quarters (TN = 256: two, TN = 128: three)
-                if constexpr (!decltype(first)::value)
-                    if (h * PST + p < LPW) issue1(slot ^ 1, kn, h * PST + p);
+                // loads j of a quarter: [p * LH / PST, (p + 1) * LH / PST)
+#pragma unroll
+                for (int j = p * LH / PST; j < (p + 1) * LH / PST; ++j) {
+                    if (h == 3) issue1(slot, k2, j);   // first half of stage t+2
+                    if constexpr (!decltype(first)::value)
+                        if (h == 0) issue1(slot ^ 1, k1, LH + j);   // second half of stage t+1
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -477,18 +489,18 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     // stage 0: its LPW loads are the oldest; the LPW of stage 1 may still be in flight
     constexpr int W_LPW = 0x0F70 | (LPW & 15) | ((LPW >> 4) << 14);
-    static_assert(LPW < 64, "vmcnt holds 6 bits");
+    static_assert(LPW < 64 && LPW % 2 == 0, "vmcnt holds 6 bits; loads in two halves");
     if (nk > 1) __builtin_amdgcn_s_waitcnt(W_LPW);
     else MF_WAITVM0();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    stage(0, std::true_type{});
-    for (int t = 1; t < nk; ++t) {
-        MF_WAITVM0();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        stage(t, std::false_type{});
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        if (f < FA) fa[0][f] = *reinterpret_cast<const bf16x8*>(smem + aoff[f]);
+        fb[0][f] = *reinterpret_cast<const bf16x8*>(smem + boff[f]);
     }
+    stage(0, std::true_type{});
+    for (int t = 1; t < nk; ++t) stage(t, std::false_type{});
 #undef MF_MMA2
     // ---- epilogue. Lane holds, for 32x32 block (a, b): token m = 32b + l32 of the wave's 128 and
     // weight rows 8*(r/4) + 4*lh + r%4 of block a (r = 0..15). Results are rounded once to bf16,
