@@ -85,6 +85,8 @@ def test_rope_apply(rc, il, dtype, d):
                                          ("bf16", 515, 512, 1032), ("bf16", 20, 200, 1000), ("bf16", 33, 520, 240),
                                          ("bf16", 200, 512, 4096), ("bf16", 96, 256, 1984), ("bf16", 16, 2048, 256),
                                          ("bf16", 64, 384, 1152),
+                                         # K walks of one to five 64-wide stages on the 256 x 256 / 256 x 128 kernels
+                                         ("bf16", 300, 64, 128), ("bf16", 520, 192, 320),
                                          ("f32", 32, 64, 176), ("f32", 45, 96, 200)])
 @pytest.mark.parametrize("with_residual", [False, True])
 def test_swiglu_mlp(dtype, M, H, I, with_residual):
