@@ -99,7 +99,7 @@ def pmc_summary(fetch_db: str, write_db: str) -> None:
         vals = sorted(v for name, vs in d.items() if "copyBuffer" in name for v in vs)
         return vals[-1] if vals else None
 
-    gu_key = "gemm_bf16_mfma32_kernel<2"
+    gu_key = "gemm_bf16_mfma32_silu_persist_kernel"
     f_copy, w_copy = pick_copy(f), pick_copy(w)
     f_gu, w_gu = pick(f, gu_key), pick(w, gu_key)
     kib = COPY_BYTES / 1024.0
@@ -193,16 +193,24 @@ def rocpd_summary(db: str) -> None:
         print(f"| `{name[:110]}` | {n} | {avg / 1e3:.1f} | {lo / 1e3:.1f} | {hi / 1e3:.1f} | {100 * tot / total:.1f}% |")
 
 
+# the fused gate_up kernel at each prefill workload's shape: the persistent kernel where the projection is made
+# of whole tiles with at least two per compute unit, else the one-tile kernel or its K-split form
+GATE_UP_KERNEL = {"llama3_8b_chunk_small": "gemm_bf16_mfma32_kernel<EPI_SILU> (few-tile plan)"}
+
+
 def gemm_source_hash() -> str:
-    """Hash of the code the gate_up kernel is built from: the 32x32 section of gemm.hip, its launcher and the
-    shared header. Other GEMM paths (decode, fp32) may change without invalidating the counters."""
+    """Hash of the code the gate_up kernel is built from: the 32x32 section of gemm.hip (both the one-tile and the
+    persistent kernel), their launchers and the shared header. Other GEMM paths (decode, fp32) may change without
+    invalidating the counters."""
     src = open(GEMM_SRC).read()
     dash = "// " + "-" * 66
     a = src.index(dash + " bf16, large M, 32x32 matrix ops")
     b = src.index(dash + " bf16, small M (decode)")
     la = src.index("static hipError_t mfma32_launch(")
     lb = src.index("\n}\n", la)
-    text = src[a:b] + src[la:lb] + open(COMMON_H).read()
+    pa = src.index("static bool mfp_usable(")
+    pb = src.index("\n}\n", src.index("static hipError_t mfp_launch("))
+    text = src[a:b] + src[la:lb] + src[pa:pb] + open(COMMON_H).read()
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
@@ -520,7 +528,7 @@ def run_model_record(args):
         "layers_ms": round(layers_ms, 4),
         "embedding_norm_head_ms": round(ms - layers_ms, 4),
         "per_layer_stages_ms": {k: round(v, 4) for k, v in per_layer.items()},
-        "roofline": {"kernel": "gemm_bf16_mfma32_kernel<EPI_SILU> (fused gate_up + silu*up), per layer",
+        "roofline": {"kernel": "gemm_bf16_mfma32_silu_persist_kernel (fused gate_up + silu*up), per layer",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_BF16_DENSE_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4), "traffic": None},
         "cpu_baseline": None,
@@ -756,7 +764,8 @@ def main():
         "rmsnorm_hbm_gbs": round(norm_bytes / (norm_ms / 1e3) / 1e9, 1),   # in-layer (warm) stages
         "stages_ms": {k: round(v[0] / v[1], 4) for k, v in stages.items()},
         "roofline": {
-            "kernel": "gemm_bf16_mfma32_kernel<EPI_SILU> (fused gate_up + silu*up)",
+            "kernel": GATE_UP_KERNEL.get(args.workload, "gemm_bf16_mfma32_silu_persist_kernel")
+                      + " (fused gate_up + silu*up)",
             "bound": "mfma",
             "achieved": round(achieved, 1),
             "peak": MI355X_BF16_DENSE_TFLOPS,

@@ -648,6 +648,210 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
 }
 #undef MF_WAITVM0
 
+// Persistent form of the gate_up kernel for shapes made of whole tiles (M % 256 == 0, N % 128 == 0, a
+// tile count divisible by 8, K >= 128): one workgroup per compute unit. Workgroup b walks the tiles its
+// XCD owns in the order the one-tile kernel's dispatch would run them (slot b / 8, then every nper-th
+// slot), and its two-slot stage pipeline runs on across tile boundaries: the next tile's first two
+// stages load during the last two stages of the current one, and no workgroup is dispatched and
+// started per tile. The epilogue stages its rows through 32 KiB of LDS beyond the two slots, 8 KiB
+// per wave in two passes of 64 rows, so it needs no barrier and leaves both slots to the loads in flight.
+constexpr int MFP_EXTRA = 4 * 64 * (MF_N / 4) * 2;   // per wave: 64 rows x 64 output columns, bf16
+constexpr int mfp_lds_bytes() { return MF_NSLOT * (MF_M + MF_N) * MF_K * 2 + MFP_EXTRA; }   // 160 KiB
+
+__global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_silu_persist_kernel(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, int N, int K, int tiles_m,
+    int tiles_n) {
+    constexpr int TN = MF_N, FA = TN / 64, STAGE = (MF_M + TN) * MF_K, LPW = 8 + TN / 32, PST = 2 * FA, LH = LPW / 2;
+    constexpr int OUT_T = TN / 2, OC = TN / 4, GPR = OC / 8;
+    static_assert(LH == PST, "one load per matrix-op pair in the quarters that carry loads");
+    extern __shared__ __align__(16) bf16_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave & 1, wm = wave >> 1;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int T = tiles_m * tiles_n;
+    const int per_x = T >> 3, nper = static_cast<int>(gridDim.x >> 3);
+    const int xcd = static_cast<int>(blockIdx.x & 7u), li = static_cast<int>(blockIdx.x >> 3);
+    if (li >= per_x) return;   // the whole workgroup leaves together
+    const int ntile = (per_x - li + nper - 1) / nper;
+    const int nk = K / MF_K;
+    // first token row and first output column of this workgroup's tile i (the one-tile kernel's order)
+    auto tile_at = [&](int i, int& m0, int& n0) {
+        const int lin = xcd * per_x + li + i * nper;
+        const int group = lin / (8 * tiles_n);
+        const int first_m = group * 8;
+        const int gsz = min(tiles_m - first_m, 8);
+        const int in_g = lin - group * 8 * tiles_n;
+        m0 = (first_m + in_g % gsz) * MF_M;
+        n0 = (in_g / gsz) * OUT_T;
+    };
+    // direct loads as in the one-tile kernel; whole tiles, so the row offsets do not depend on the tile
+    const int rsub = 8 * wave + (lane >> 3);
+    const int cj = (lane & 7) ^ mf_swz(rsub);
+    uint32_t voff[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+        const int r = 32 * (j < 8 ? j : j - 8) + rsub;
+        const int row = j < 8 ? r : (((r >> 4) & 1) ? N : 0) + (r >> 5) * 16 + (r & 15);
+        voff[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>(cj) * 16u;
+    }
+    int m0, n0, m0n = 0, n0n = 0;
+    tile_at(0, m0, n0);
+    bool has_next = ntile > 1;
+    if (has_next) tile_at(1, m0n, n0n);
+    auto rsrc = [&](const bf16_t* base) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), (short)0, -1, 0x00020000);
+    };
+    auto issue1 = [&](int slot, __amdgpu_buffer_rsrc_t rs, int kst, int j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(smem + slot * STAGE + (4 * j + wave) * 8 * MF_K), 16, voff[j],
+            kst * MF_K * 2, 0, 0);
+    };
+    int aoff[FA], boff[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const int ra = wn * (TN / 2) + 32 * f + l32, rb = wm * 128 + 32 * f + l32;
+        if (f < FA) aoff[f] = (MF_M + ra) * MF_K + ((lh ^ mf_swz(ra)) << 3);
+        boff[f] = rb * MF_K + ((lh ^ mf_swz(rb)) << 3);
+    }
+    f32x16 acc[FA][4];
+#pragma unroll
+    for (int a = 0; a < FA; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+    bf16x8 fa[2][FA], fb[2][4];
+#define MF_MMA2(FA, FB, p)                                                                                   \
+    {                                                                                                      \
+        const int a_ = (p) >> 1, b_ = ((p) & 1) * 2;                                                       \
+        acc[a_][b_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[a_], FB[b_], acc[a_][b_], 0, 0, 0);       \
+        acc[a_][b_ + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[a_], FB[b_ + 1], acc[a_][b_ + 1], 0, 0, 0); \
+    }
+    // global stage g = local stage t of the current tile; its quarter 0 issues the W half of stage g+1
+    // (except the very first stage: the prologue issued stages 0 and 1 whole), its quarter 3 the X half of
+    // stage g+2. A stage past the current tile is the next tile's; with no next tile it re-reads the
+    // current tile's last stage into a slot nobody reads.
+    auto stage = [&](int g, int t, auto first, auto last) {
+        const int slot = g & 1;
+        const bf16_t* st = smem + slot * STAGE;
+        const bf16_t* stn = smem + (slot ^ 1) * STAGE;
+        const bool n1 = t + 1 >= nk, n2 = t + 2 >= nk;
+        const int k1 = n1 ? (has_next ? t + 1 - nk : nk - 1) : t + 1;
+        const int k2 = n2 ? (has_next ? t + 2 - nk : nk - 1) : t + 2;
+        const __amdgpu_buffer_rsrc_t rw1 = rsrc(W + static_cast<int64_t>(n1 && has_next ? n0n : n0) * K);
+        const __amdgpu_buffer_rsrc_t rx2 = rsrc(X + static_cast<int64_t>(n2 && has_next ? m0n : m0) * K);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            if (h == 3) {
+                __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int p = 0; p < PST; ++p) {
+                MF_MMA2(fa[h & 1], fb[h & 1], p)
+                if (p < 4) {
+                    if (h < 3) {
+                        if (p < FA) fa[(h + 1) & 1][p] = *reinterpret_cast<const bf16x8*>(st + (aoff[p] ^ (16 * (h + 1))));
+                        fb[(h + 1) & 1][p] = *reinterpret_cast<const bf16x8*>(st + (boff[p] ^ (16 * (h + 1))));
+                    } else if constexpr (!decltype(last)::value) {   // stage g+1, quarter 0
+                        if (p < FA) fa[0][p] = *reinterpret_cast<const bf16x8*>(stn + aoff[p]);
+                        fb[0][p] = *reinterpret_cast<const bf16x8*>(stn + boff[p]);
+                    }
+                }
+                if (h == 3) issue1(slot, rx2, k2, p);
+                if constexpr (!decltype(first)::value)
+                    if (h == 0) issue1(slot ^ 1, rw1, k1, LH + p);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    {
+        const __amdgpu_buffer_rsrc_t rx = rsrc(X + static_cast<int64_t>(m0) * K);
+        const __amdgpu_buffer_rsrc_t rw = rsrc(W + static_cast<int64_t>(n0) * K);
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) issue1(0, j < 8 ? rx : rw, 0, j);
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) issue1(1, j < 8 ? rx : rw, 1, j);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): no scalar load outstanding at the loop head
+    constexpr int W_LPW = 0x0F70 | (LPW & 15) | ((LPW >> 4) << 14);
+    __builtin_amdgcn_s_waitcnt(W_LPW);    // stage 0 landed; stage 1 may be in flight
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        if (f < FA) fa[0][f] = *reinterpret_cast<const bf16x8*>(smem + aoff[f]);
+        fb[0][f] = *reinterpret_cast<const bf16x8*>(smem + boff[f]);
+    }
+    bf16_t* reg = smem + 2 * STAGE + wave * (64 * OC);   // this wave's 8 KiB epilogue region
+    auto lds_at = [&](int m, int c) { return reg + m * OC + (((c >> 3) ^ (m & (GPR - 1))) << 3) + (c & 7); };
+    int g = 0;
+    for (int i = 0; i < ntile; ++i) {
+        // (the last stage of a tile leaves the next tile's first fragments in LDS: read after the epilogue,
+        // they would stay live through it)
+        if (i == 0) stage(g++, 0, std::true_type{}, std::false_type{});
+        for (int t = i == 0 ? 1 : 0; t < nk - 1; ++t) stage(g++, t, std::false_type{}, std::false_type{});
+        stage(g++, nk - 1, std::false_type{}, std::true_type{});
+        // epilogue of tile i: silu(gate) * up rounded once, 64 token rows per pass
+        const int mw = m0 + wm * 128, nw = n0 + wn * OC;
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const int b = 2 * ps + bb, m = 32 * bb + l32;
+#pragma unroll
+                for (int a = 0; a < FA; ++a)
+#pragma unroll
+                    for (int gg = 0; gg < 2; ++gg) {
+                        float o[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float gt = acc[a][b][4 * gg + q], up = acc[a][b][4 * gg + q + 8];
+                            o[q] = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
+                        }
+                        *reinterpret_cast<uint2*>(lds_at(m, 16 * a + 8 * gg + 4 * lh)) =
+                            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                    }
+            }
+            // the wave's LDS instructions run in order: its rows are complete for the reads below, and
+            // these reads finish before the next pass overwrites the region
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e8 = 0; e8 < 64 * GPR / 64; ++e8) {
+                const int e = e8 * 64 + lane, m = e / GPR, gq = e % GPR;
+                const uint4 v = *reinterpret_cast<const uint4*>(lds_at(m, 8 * gq));
+                *reinterpret_cast<uint4*>(C + static_cast<int64_t>(mw + 64 * ps + m) * N + nw + 8 * gq) = v;
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int a = 0; a < FA; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+        m0 = m0n;
+        n0 = n0n;
+        has_next = i + 2 < ntile;
+        if (has_next) tile_at(i + 2, m0n, n0n);
+        if (i + 1 < ntile) {   // the next tile's first stage is complete in its slot since the last barrier
+            const bf16_t* st = smem + (g & 1) * STAGE;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                if (f < FA) fa[0][f] = *reinterpret_cast<const bf16x8*>(st + aoff[f]);
+                fb[0][f] = *reinterpret_cast<const bf16x8*>(st + boff[f]);
+            }
+        }
+    }
+    // the last stages' re-reads must land before the workgroup's LDS is handed to another
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+#undef MF_MMA2
+}
+
 // ------------------------------------------------------------------ bf16, small M (decode)
 // With M <= 64 tokens a projection is bound by streaming W from HBM once. A workgroup of 8 waves
 // owns 128 weight rows (16 per wave; gate_up: 64 gate rows and the 64 matching up rows) over one K
@@ -1284,6 +1488,36 @@ static hipError_t mfma32_launch(const void* X, const void* W, void* C, const voi
     return hipGetLastError();
 }
 
+// workgroups of the persistent gate_up kernel: one per compute unit, a multiple of 8 (the XCDs take
+// workgroups in turn, so each XCD gets the same number of slots)
+static int mfp_workgroups() {
+    static const int n = [] {
+        int dev = 0, cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 8)
+            cu = 256;
+        return cu / 8 * 8;
+    }();
+    return n;
+}
+
+// whole 256 x 128-output tiles, a tile count divisible by 8 and at least two tiles per workgroup
+static bool mfp_usable(int64_t M, int64_t N, int64_t K) {
+    if (M % MF_M != 0 || N % (MF_N / 2) != 0 || K % MF_K != 0 || K < 2 * MF_K) return false;
+    const int64_t T = (M / MF_M) * (N / (MF_N / 2));
+    return T % 8 == 0 && T >= 2 * static_cast<int64_t>(mfp_workgroups());
+}
+
+static hipError_t mfp_launch(const void* X, const void* W, void* C, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+    static const bool attr = allow_lds(&gemm_bf16_mfma32_silu_persist_kernel, mfp_lds_bytes());
+    if (!attr) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(gemm_bf16_mfma32_silu_persist_kernel, dim3(static_cast<unsigned>(mfp_workgroups())),
+                       dim3(MF_THREADS), mfp_lds_bytes(), st, static_cast<const bf16_t*>(X),
+                       static_cast<const bf16_t*>(W), static_cast<bf16_t*>(C), static_cast<int>(N),
+                       static_cast<int>(K), static_cast<int>(M / MF_M), static_cast<int>(N / (MF_N / 2)));
+    return hipGetLastError();
+}
+
 // K ranges of the MFMA kernel into fp32 partials (PE: plain layout, or gate/up apart for silu·up)
 template <int PE, int TN>
 static hipError_t mfma32_partials_launch(const void* X, const void* W, int64_t M, int64_t N, int64_t K,
@@ -1424,7 +1658,9 @@ hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C
             case EPI_ROPE:
                 if (re->d == 128) return mfma32_launch<EPI_ROPE, 128>(X, W, C, R, M, N, K, st, re);
                 return mfma32_launch<EPI_ROPE, 64>(X, W, C, R, M, N, K, st, re);
-            default: return mfma32_launch<EPI_SILU>(X, W, C, R, M, N, K, st);
+            default:
+                if (mfp_usable(M, N, K)) return mfp_launch(X, W, C, M, N, K, st);
+                return mfma32_launch<EPI_SILU>(X, W, C, R, M, N, K, st);
         }
     }
     switch (epi) {
