@@ -200,8 +200,8 @@ GATE_UP_KERNEL = {"llama3_8b_chunk_small": "gemm_bf16_mfma32_kernel<EPI_SILU> (f
 
 def gemm_source_hash() -> str:
     """Hash of the code the gate_up kernel is built from: the 32x32 section of gemm.hip (both the one-tile and the
-    persistent kernel), their launchers and the shared header. Other GEMM paths (decode, fp32) may change without
-    invalidating the counters."""
+    persistent kernel), their launchers and the shared header, without comments. Other GEMM paths (decode, fp32) may
+    change without invalidating the counters."""
     src = open(GEMM_SRC).read()
     dash = "// " + "-" * 66
     a = src.index(dash + " bf16, large M, 32x32 matrix ops")
@@ -211,7 +211,9 @@ def gemm_source_hash() -> str:
     pa = src.index("static bool mfp_usable(")
     pb = src.index("\n}\n", src.index("static hipError_t mfp_launch("))
     text = src[a:b] + src[la:lb] + src[pa:pb] + open(COMMON_H).read()
-    return hashlib.sha256(text.encode()).hexdigest()[:16]
+    # comments and blank lines do not change the machine code
+    code = [ln.split("//", 1)[0].rstrip() for ln in text.splitlines()]
+    return hashlib.sha256("\n".join(ln for ln in code if ln).encode()).hexdigest()[:16]
 
 
 def measured_traffic():

@@ -315,8 +315,9 @@ __global__ __launch_bounds__(GB_THREADS, 1) void gemm_bf16_big_kernel(
 // registers). Larger per-wave blocks than the 8-wave kernel above read a third less operand data
 // from LDS per matrix op. K runs in 64-wide stages through two LDS slots filled by direct
 // global->LDS loads (full 128-byte row segments); operand fragments are double-buffered in
-// registers across the four k16 quarters of a stage, and the loads of the next stage are spread
-// over the first two quarters. The epilogue stages each wave's results through LDS and writes whole
+// registers across the four k16 quarters of a stage, each stage's barrier precedes its last
+// quarter, and the loads of the stage after next are spread over that quarter and the next
+// stage's first. The epilogue stages each wave's results through LDS and writes whole
 // output rows (RoPE rotated in fp32 first, for head sizes 64 and 128). Used when K % 64 == 0 and
 // N % 8 == 0 and the operands fit 32-bit byte offsets; shapes with few tiles use the split / 128-wide
 // forms below.
