@@ -558,15 +558,24 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     auto lds_at = [&](int m, int c) { return reg + m * OC + (((c >> 3) ^ (m & (GPR - 1))) << 3) + (c & 7); };
 
     if constexpr (EPI == EPI_RESIDUAL) {
-        // residual rows of the wave into LDS (coalesced), to be added in fp32 below
-#pragma unroll 4
-        for (int i = 0; i < 128 * GPR / 64; ++i) {
-            const int e = i * 64 + lane, m = e / GPR, g = e % GPR;
-            const int gm = min(mw + m, M - 1), gn = nw + 8 * g;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (gn < N) v = *reinterpret_cast<const uint4*>(R + static_cast<int64_t>(gm) * N + gn);
-            *reinterpret_cast<uint4*>(lds_at(m, 8 * g)) = v;
+        // residual rows of the wave into LDS, to be added in fp32 below: buffer loads straight into LDS,
+        // all in flight at once (loaded through registers a few at a time, the residual cost o_proj 12%
+        // of its time). Load i fills rows RPI*i .. of the region; lane l lands at physical chunk l % GPR
+        // of its row and fetches the logical chunk the row swizzle puts there. Rows past M read row M - 1
+        // and columns past N column N - 8; neither is stored.
+        constexpr int RPI = 64 / GPR;
+        const int mwc = min(mw, M - 1);
+        const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t*>(R + static_cast<int64_t>(mwc) * N), (short)0, -1, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < 128 / RPI; ++i) {
+            const int m = RPI * i + lane / GPR, g = (lane % GPR) ^ (m & (GPR - 1));
+            const int gm = min(mw + m, M - 1) - mwc, gn = min(nw + 8 * g, N - 8);
+            const uint32_t off = (static_cast<uint32_t>(gm) * static_cast<uint32_t>(N) + static_cast<uint32_t>(gn)) * 2u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void*)(reg + RPI * i * OC), 16,
+                                                     off, 0, 0, 0);
         }
+        MF_WAITVM0();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_sched_barrier(0);
     }
