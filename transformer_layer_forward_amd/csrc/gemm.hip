@@ -579,15 +579,42 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (EPI == EPI_ROPE) {
+        // Rotate q/k columns in fp32 before the single rounding. The cos/sin factors of the tile's 256 token
+        // rows (RD/2 pairs a row, 16-byte chunks XOR-swizzled by row) first go into LDS with buffer loads,
+        // all in flight at once: fetched from global memory a pair or two at a time, a memory round trip
+        // each, they cost ~7 us per tile. Load i of wave w fills rows 64w + RPL*i ..; lane l lands at
+        // physical chunk l % CPR of row RPL*i + l / CPR and takes that row's position from the lane that
+        // loaded it (lane h*CPR + i holds the position of row 64w + RPL*i + h).
+        constexpr int CPR = RD / 4, RPL = 64 / CPR, NLD = 64 / RPL;
+        {
+            const int h = lane / CPR, k = lane % CPR;
+            const int mine = static_cast<int>(clamp_pos(rpos[min(m0 + 64 * wave + RPL * k + h, M - 1)], rrows));
+            const __amdgpu_buffer_rsrc_t rt =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(rcs), (short)0, -1, 0x00020000);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int m = 32 * b + l32;
-        if constexpr (EPI == EPI_ROPE) {
-            // rotate q/k columns in fp32 before the single rounding. The wave's 128 columns start on a
-            // head boundary, so block a covers head dims (32a) % RD ..; a lane's register i of block a
-            // is dim 8(i/4) + 4*lh + i%4 of it. Half-split: its partner (dim + RD/2) is the same
-            // register of block a + RD/64; interleaved: the neighbouring register.
-            const float2* cs_row = rcs + clamp_pos(rpos[min(mw + m, M - 1)], rrows) * (RD / 2);
+            for (int i = 0; i < NLD; ++i) {
+                const int pos = __shfl(mine, h * CPR + i, 64);
+                const int row = 64 * wave + RPL * i + h;
+                const int c = k ^ (row & (CPR - 1));
+                const uint32_t off = static_cast<uint32_t>(pos) * (RD / 2 * 8) + static_cast<uint32_t>(c) * 16u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rt, (__attribute__((address_space(3))) void*)(smem + (64 * wave + RPL * i) * (CPR * 8)), 16, off, 0, 0, 0);
+            }
+        }
+        MF_WAITVM0();
+        __builtin_amdgcn_s_barrier();   // every wave's factors have landed
+        __builtin_amdgcn_sched_barrier(0);
+        // The wave's 128 columns start on a head boundary, so block a covers head dims (32a) % RD ..; a
+        // lane's register i of block a is dim 8(i/4) + 4*lh + i%4 of it. Half-split: its partner (dim + RD/2)
+        // is the same register of block a + RD/64; interleaved: the neighbouring register.
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int row = wm * 128 + 32 * b + l32;   // token row within the tile
+            const bf16_t* frow = smem + row * (CPR * 8);
+            auto chunk = [&](int c) {   // factors 2c and 2c + 1 of this row
+                return *reinterpret_cast<const float4*>(frow + ((c ^ (row & (CPR - 1))) << 3));
+            };
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 if (nw + 32 * a >= rope_cols) continue;   // value columns
@@ -596,24 +623,41 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
                     constexpr int PA = RD / 64;
                     if (jb < RD / 2) {
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const float2 t = cs_row[jb + 8 * (i / 4) + 4 * lh + i % 4];
-                            const float x = acc[a][b][i], y = acc[a + PA][b][i];
-                            acc[a][b][i] = x * t.x - y * t.y;
-                            acc[a + PA][b][i] = y * t.x + x * t.y;
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const int d0 = jb + 8 * g4 + 4 * lh;
+                            const float4 u = chunk(d0 / 2), v = chunk(d0 / 2 + 1);
+                            const float2 t[4] = {{u.x, u.y}, {u.z, u.w}, {v.x, v.y}, {v.z, v.w}};
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const int i = 4 * g4 + q;
+                                const float x = acc[a][b][i], y = acc[a + PA][b][i];
+                                acc[a][b][i] = x * t[q].x - y * t[q].y;
+                                acc[a + PA][b][i] = y * t[q].x + x * t[q].y;
+                            }
                         }
                     }
                 } else {
 #pragma unroll
-                    for (int i = 0; i < 16; i += 2) {
-                        const float2 t = cs_row[(jb + 8 * (i / 4) + 4 * lh + i % 4) >> 1];
-                        const float x = acc[a][b][i], y = acc[a][b][i + 1];
-                        acc[a][b][i] = x * t.x - y * t.y;
-                        acc[a][b][i + 1] = y * t.x + x * t.y;
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const float4 u = chunk((jb + 8 * g4 + 4 * lh) / 4);   // pairs (d0, d0+1), (d0+2, d0+3)
+                        const float2 t[2] = {{u.x, u.y}, {u.z, u.w}};
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const int i = 4 * g4 + 2 * q;
+                            const float x = acc[a][b][i], y = acc[a][b][i + 1];
+                            acc[a][b][i] = x * t[q].x - y * t[q].y;
+                            acc[a][b][i + 1] = y * t[q].x + x * t[q].y;
+                        }
                     }
                 }
             }
         }
+        __builtin_amdgcn_s_barrier();   // every wave is done with the factors before the staging below
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int m = 32 * b + l32;
 #pragma unroll
         for (int a = 0; a < FA; ++a) {
             if constexpr (EPI == EPI_SILU) {
