@@ -5,17 +5,18 @@
 //   o[b,i,h] = sum_{j<=i} softmax_j(q'_{b,i,h} . k'_{b,j,c} / sqrt(d)) v_{b,j,c},  c = h / (n_h/n_kv).
 // repeat_kv is never materialised: one workgroup serves every query head of a K/V head.
 //
-// Prefill kernel (bf16, d in {64, 128}): a workgroup owns (sequence b, kv head c, 64 queries) and
+// Prefill kernels (bf16, d in {64, 128}): a workgroup owns (sequence b, kv head c, 64 queries) and
 // runs 2 waves per query head of the group (32 queries each). Each 64-key K tile and V tile is
 // staged once in LDS (double-buffered) and read by all waves of the group. Scores are formed
-// transposed, S^T = K Q^T, with K as the MFMA A operand and Q (in registers) as B: the
-// 16x16 output fragment then holds, per lane, one query column and 4 keys, which after the
-// fp32 online softmax (exp2 with log2(e)/sqrt(d) folded into the scale) is exactly the B-operand
-// layout of O^T += V^T P^T. Two variants stage the tiles: with q and k already rotated (the layer
-// path) K and V go global -> LDS by direct loads, V stays [key][d] and its V^T operand comes from
-// transposing LDS reads, and a per-wave software pipeline overlaps the next tile's Q K^T with the
-// current softmax; with RoPE applied on load (the standalone entry point) tiles pass through
-// registers, are rotated there, and V is transposed into LDS as [d][key] while it is stored.
+// transposed, S^T = K Q^T, with K as the MFMA A operand and Q (in registers) as B: the output
+// fragment then holds, per lane, one query column and a few keys, which after the fp32 online
+// softmax (exp2 with log2(e)/sqrt(d) folded into the scale) is exactly the B-operand layout of
+// O^T += V^T P^T. Three variants: with q and k already rotated, K and V go global -> LDS by direct
+// loads, V stays [key][d] and its V^T operand comes from transposing LDS reads, and a per-wave
+// software pipeline overlaps the next tile's Q K^T with the current softmax; the layer path runs this
+// on 32x32x16 matrix ops (attn_prefill_m32_kernel), the chunked path on 16x16x32
+// (attn_prefill_direct_kernel). With RoPE applied on load (the standalone entry point) tiles pass
+// through registers, are rotated there, and V is transposed into LDS as [d][key] while it is stored.
 // Rows are XOR-swizzled so the lanes of an operand read hit distinct banks.
 // Causality: query block qb only visits key tiles 0..qb; only the diagonal tile is masked.
 // Blocks are issued heaviest-first (largest qb first); consecutive blocks of one qb level
@@ -795,6 +796,278 @@ __global__ __launch_bounds__(128 * HPB, HPB == 2 ? 2 : 1) void attn_prefill_dire
             *reinterpret_cast<uint2*>(op + a * 16 + 4 * lgrp) =
                 make_uint2(pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv));
         }
+    }
+}
+
+// ------------------------------------------------------------------ prefill, 32x32 matrix ops
+// The layer path's causal prefill (q and k already rotated, no cache prefix, no key split; packed
+// sequences through cu) on v_mfma_f32_32x32x16_bf16, which issues at full rate from a single wave,
+// where the 16x16x32 form of the kernel above needs both waves of a SIMD to keep the matrix core fed.
+// Same workgroup layout, LDS tiles, loads and pipeline as above; per wave 32 queries:
+//  * S^T = K Q^T per 32-key block: A = 32 keys x 16 dims of K (one 16-byte LDS read), B = the wave's
+//    Q^T (16 dims x 32 queries, resident). The accumulator gives lane l query l % 32 and keys
+//    8i + 4(l/32) + r in register 4i + r, so a query's scores sit in two lanes (l, l ^ 32): its row
+//    max and row sum take one lane swap.
+//  * Registers 8s .. 8s + 7 of a block are exactly the B operand (16 keys x 32 queries) of
+//    O^T += V^T P^T for keys 16s .. 16s + 15 of the block, in the key order {4h .. 4h+3, 8+4h .. 8+4h+3}
+//    for h = l / 32; the V^T operand (32 dims x those keys) comes from two transposing LDS reads
+//    (each gives a lane 4 consecutive keys of its dim).
+template <int D, int HPB>
+__global__ __launch_bounds__(128 * HPB, HPB == 2 ? 2 : 1) void attn_prefill_m32_kernel(
+    const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, bf16_t* __restrict__ out, bf16_t* __restrict__ kc,
+    bf16_t* __restrict__ vc, int64_t ctx, int B, int S_max, int nh, int nkv, float scale_log2,
+    const int* __restrict__ cu, int total) {
+    constexpr int BQ = 64, BKV = 64;
+    constexpr int KS = D / 16;                       // 16-wide k steps of Q K^T
+    constexpr int KH = KS / 2;
+    constexpr int DB = D / 32;                       // 32-dim blocks of O^T
+    constexpr int NT = 128 * HPB, NW = NT / 64;
+    constexpr int CH = D / 8;                        // 16-byte chunks per row
+    constexpr int RPI = 64 / CH;                     // rows per 1 KiB direct load
+    constexpr int LOADS = BKV / RPI;                 // direct loads per K (or V) tile
+    constexpr int LPW = (2 * LOADS) / NW;            // direct loads per wave per iteration (K and V)
+    static_assert((2 * LOADS) % NW == 0, "loads split evenly over the waves");
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    __shared__ __align__(16) bf16_t sK[2][BKV * D];
+    __shared__ __align__(16) bf16_t sV[2][BKV * D];
+
+    const int g = nh / nkv;
+    const int hchunks = g / HPB;
+    const int nqb = (S_max + BQ - 1) / BQ;
+    const int per_qb = B * nkv * hchunks;
+    const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / per_qb;   // heaviest blocks first
+    int rem = static_cast<int>(blockIdx.x) % per_qb;
+    const int hc = rem % hchunks;
+    rem /= hchunks;
+    const int c = rem % nkv;
+    const int b = rem / nkv;
+
+    int seq0, S;
+    if (cu != nullptr) {   // packed sequences: bounds clamped into range, as in the kernels above
+        const int a0 = min(max(cu[b], 0), total);
+        const int a1 = min(max(cu[b + 1], a0), total);
+        seq0 = a0;
+        S = min(a1 - a0, S_max);
+    } else {
+        seq0 = b * S_max;
+        S = S_max;
+    }
+    if (qb * BQ >= S) return;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int h = c * g + hc * HPB + (wave >> 1);
+    const int64_t rs = static_cast<int64_t>(nh + 2 * nkv) * D;
+    const bf16_t* qkv_b = qkv + static_cast<int64_t>(seq0) * rs;
+    // query i sees keys 0 .. i: the block visits key tiles 0 .. hi / BKV; only the diagonal is masked
+    const int lo = qb * BQ, hi = min(qb * BQ + BQ - 1, S - 1);
+    const int nkt = hi / BKV + 1;
+    const int qi = qb * BQ + (wave & 1) * 32 + l32;
+    const int qlim = min(qi, S - 1);
+
+    // Q^T fragments: lane holds query qi, dims 16k + 8 lh .. + 7, pre-scaled by log2(e)/sqrt(d), bf16
+    bf16x8 qfr[KS];
+    {
+        const bf16_t* qp = qkv_b + static_cast<int64_t>(qlim) * rs + static_cast<int64_t>(h) * D;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            float f[8];
+            unpack8(*reinterpret_cast<const uint4*>(qp + 16 * k + 8 * lh), f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] *= scale_log2;
+            uint4 u = pack8(f);
+            if (qi >= S) u = make_uint4(0, 0, 0, 0);
+            qfr[k] = __builtin_bit_cast(bf16x8, u);
+        }
+    }
+
+    const bf16_t* kbase = qkv_b + static_cast<int64_t>(nh + c) * D;
+    const bf16_t* vbase = qkv_b + static_cast<int64_t>(nh + nkv + c) * D;
+    const uint32_t rs_bytes = static_cast<uint32_t>(rs) * 2u;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kbase), (short)0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vbase), (short)0, -1, 0x00020000);
+
+    // cache append: the first head chunk of each query block copies the block's own keys and values
+    if (kc != nullptr && hc == 0) {
+        const int64_t* pos_b = pos + seq0;
+        for (int job = tid; job < 2 * BQ * CH; job += NT) {
+            const bool isv = job >= BQ * CH;
+            const int jj = isv ? job - BQ * CH : job;
+            const int r = jj / CH, ch = jj % CH;
+            const int key = qb * BQ + r;
+            if (key < S) {
+                const int64_t slot = clamp_pos(pos_b[key], ctx);
+                const uint4 v = *reinterpret_cast<const uint4*>((isv ? vbase : kbase) + static_cast<int64_t>(key) * rs + ch * 8);
+                bf16_t* dst = (isv ? vc : kc) + ((static_cast<int64_t>(b) * ctx + slot) * nkv + c) * D + ch * 8;
+                *reinterpret_cast<uint4*>(dst) = v;
+            }
+        }
+    }
+    // direct loads as in the kernel above
+    auto issue_tiles = [&](int ktile, int kbuf, int vtile, int vbuf) {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int q = wave * LPW + i;
+            const bool isv = q >= LOADS;
+            const int r = (q % LOADS) * RPI + lane / CH, pc = lane % CH;
+            const int key = min((isv ? vtile : ktile) * BKV + r, hi);
+            const int lc = isv ? vt_phys<D>(r, pc) : k_phys<D>(r, pc);
+            const uint32_t off = static_cast<uint32_t>(key) * rs_bytes + static_cast<uint32_t>(lc) * 16u;
+            bf16_t* dst = isv ? &sV[vbuf][(q % LOADS) * RPI * D] : &sK[kbuf][(q % LOADS) * RPI * D];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (__attribute__((address_space(3))) void*)dst, 16,
+                                                     off, 0, 0, 0);
+        }
+    };
+    auto issue_k_only = [&](int ktile, int kbuf) {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int q = wave * LPW + i;
+            if (q < LOADS) {
+                const int r = q * RPI + lane / CH, pc = lane % CH;
+                const int key = min(ktile * BKV + r, hi);
+                const uint32_t off = static_cast<uint32_t>(key) * rs_bytes + static_cast<uint32_t>(k_phys<D>(r, pc)) * 16u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)&sK[kbuf][q * RPI * D],
+                                                         16, off, 0, 0, 0);
+            }
+        }
+    };
+
+    // k steps [k0, k0 + KH) of the scores of the tile in K buffer kb, both 32-key blocks
+#define PM_QK(SN, kb, k0)                                                                                  \
+    _Pragma("unroll") for (int k = (k0); k < (k0) + KH; ++k) {                                             \
+        _Pragma("unroll") for (int kf = 0; kf < 2; ++kf) {                                                 \
+            const int r = kf * 32 + l32;                                                                   \
+            const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&sK[kb][r * D + k_phys<D>(r, 2 * k + lh) * 8]); \
+            SN[kf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qfr[k], SN[kf], 0, 0, 0);                \
+        }                                                                                                  \
+    }
+    // O^T += V^T P^T over the 32 keys of block t (V buffer vb)
+#define PM_PV_HALF(vb, t)                                                                                  \
+    _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                                        \
+        _Pragma("unroll") for (int db = 0; db < DB; ++db) {                                                \
+            s16x4 h_[2];                                                                                   \
+            _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                \
+                const int r = 32 * (t) + 16 * s + 8 * u + 4 * lh + ((lane & 15) >> 2);                     \
+                const int cc = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);                         \
+                h_[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(  \
+                    &sV[vb][r * D + vt_phys<D>(r, cc) * 8 + (lane & 1) * 4]));                             \
+            }                                                                                              \
+            const bf16x8 vfr = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h_[0], h_[1], 0, 1, 2, 3, 4, 5, 6, 7)); \
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, pfr[2 * (t) + s], oacc[db], 0, 0, 0);  \
+        }                                                                                                  \
+    }
+#define PM_EXP_HALF(SC, t)                                                                                 \
+    _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                                        \
+        float p_[8];                                                                                       \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                                    \
+            p_[e] = fast_exp2(SC[t][8 * s + e]);                                                           \
+            ls += p_[e];                                                                                   \
+        }                                                                                                  \
+        pfr[2 * (t) + s] = __builtin_bit_cast(bf16x8, pack8(p_));                                          \
+    }
+
+    float m_i = 0.f, l_i = 0.f, mbA = 0.f, mbB = 0.f;
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    f32x16 sA[2], sB[2];
+    bf16x8 pfr[4];
+
+    issue_tiles(0, 0, 0, 0);
+    issue_k_only(1, 1);
+    __syncthreads();
+    sA[0] = sA[1] = f32x16{};
+    PM_QK(sA, 0, 0)
+    PM_QK(sA, 0, KH)
+    __syncthreads();   // K buffer 0 is refilled by the first iteration
+
+#define PM_ITER(SC, MBC, SN, MBN)                                                                          \
+    {                                                                                                      \
+        issue_tiles(j + 2, j & 1, j + 1, (j + 1) & 1);                                                     \
+        if (__builtin_expect((j + 1) * BKV - 1 > lo, 0)) {                                                 \
+            __asm__ volatile("");                                                                          \
+            _Pragma("unroll") for (int kf = 0; kf < 2; ++kf)                                               \
+                _Pragma("unroll") for (int e = 0; e < 16; ++e) {                                           \
+                    const int key = j * BKV + kf * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);                   \
+                    if (key > qlim) SC[kf][e] = -INFINITY;                                                 \
+                }                                                                                          \
+        }                                                                                                  \
+        /* stage 1: first half of tile j+1's scores || row max of tile j */                               \
+        MBN = j != 0 ? m_i : 0.f;                                                                          \
+        {                                                                                                  \
+            f32x16 z_;                                                                                     \
+            _Pragma("unroll") for (int e = 0; e < 16; ++e) z_[e] = -MBN;                                   \
+            SN[0] = SN[1] = z_;                                                                            \
+        }                                                                                                  \
+        PM_QK(SN, (j + 1) & 1, 0)                                                                          \
+        float mx = -INFINITY;                                                                              \
+        _Pragma("unroll") for (int kf = 0; kf < 2; ++kf)                                                   \
+            _Pragma("unroll") for (int e = 0; e < 16; ++e) mx = fmaxf(mx, SC[kf][e]);                      \
+        {                                                                                                  \
+            const auto a_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false); \
+            mx = fmaxf(__uint_as_float(a_[0]), __uint_as_float(a_[1]));                                    \
+        }                                                                                                  \
+        const float delta_ = m_i - MBC;                                                                    \
+        const float rel_ = mx - delta_;                                                                    \
+        const float shift_ = (j == 0 || rel_ > kSlack) ? rel_ : 0.f;                                       \
+        const float sub_ = delta_ + shift_;                                                                \
+        /* stage 2 (rare): re-reference tile j's scores, rescale O and l where the reference moved */     \
+        if (__builtin_expect(__any(sub_ != 0.f), 0)) {                                                     \
+            __asm__ volatile("");                                                                          \
+            const float alpha = j == 0 ? 1.f : fast_exp2(-shift_);                                         \
+            m_i += shift_;                                                                                 \
+            l_i *= alpha;                                                                                  \
+            _Pragma("unroll") for (int db = 0; db < DB; ++db) oacc[db] *= alpha;                           \
+            SC[0] -= sub_;                                                                                 \
+            SC[1] -= sub_;                                                                                 \
+        }                                                                                                  \
+        float ls = 0.f;                                                                                    \
+        /* stage 3: second half of tile j+1's scores || exponentials of keys 0..31 */                      \
+        PM_QK(SN, (j + 1) & 1, KH)                                                                         \
+        PM_EXP_HALF(SC, 0)                                                                                 \
+        /* stage 4: P V of keys 0..31 || exponentials of keys 32..63 */                                    \
+        PM_PV_HALF(j & 1, 0)                                                                               \
+        PM_EXP_HALF(SC, 1)                                                                                 \
+        /* stage 5: P V of keys 32..63 */                                                                  \
+        PM_PV_HALF(j & 1, 1)                                                                               \
+        l_i += ls;                                                                                         \
+        __syncthreads();                                                                                   \
+    }
+    for (int j = 0; j < nkt; j += 2) {
+        PM_ITER(sA, mbA, sB, mbB)
+        if (j + 1 >= nkt) break;
+        {
+            const int j_ = j;
+            {
+                const int j = j_ + 1;
+                PM_ITER(sB, mbB, sA, mbA)
+            }
+        }
+    }
+#undef PM_ITER
+#undef PM_QK
+#undef PM_PV_HALF
+#undef PM_EXP_HALF
+
+    // lane holds dims 32 db + 8 i + 4 lh + {0..3} of query qi
+    float lsum;
+    {
+        const auto a_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_i), __float_as_uint(l_i), false, false);
+        lsum = __uint_as_float(a_[0]) + __uint_as_float(a_[1]);
+    }
+    const float inv = 1.f / lsum;
+    if (qi < S) {
+        bf16_t* op = out + (static_cast<int64_t>(seq0) + qi) * nh * D + static_cast<int64_t>(h) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x16& v = oacc[db];
+                *reinterpret_cast<uint2*>(op + 32 * db + 8 * i + 4 * lh) =
+                    make_uint2(pack_bf16x2(v[4 * i] * inv, v[4 * i + 1] * inv),
+                               pack_bf16x2(v[4 * i + 2] * inv, v[4 * i + 3] * inv));
+            }
     }
 }
 
@@ -1613,16 +1886,10 @@ static hipError_t prefill_go(const void* qkv, const int64_t* pos, const RopeTab*
     const int nqb = (S + 63) / 64;
     const unsigned blocks = static_cast<unsigned>(nqb) * B * nkv * (g / HPB);
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
-    const bool offsets_ok = static_cast<int64_t>(S) * (nh + 2 * nkv) * D * 2 < (int64_t(1) << 32);
-    if (!ROPE && offsets_ok)
-        hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, false>), dim3(blocks), dim3(128 * HPB), 0, st,
-                           static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
-                           static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2, nullptr, 0, 1, nullptr);
-    else
-        hipLaunchKernelGGL((attn_prefill_mfma_kernel<D, HPB, ROPE, IL>), dim3(blocks), dim3(128 * HPB), 0, st,
-                           static_cast<const bf16_t*>(qkv), pos, tab ? tab->cs : nullptr, tab ? tab->rows : 1,
-                           static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, B, S, nh,
-                           nkv, scale_log2);
+    hipLaunchKernelGGL((attn_prefill_mfma_kernel<D, HPB, ROPE, IL>), dim3(blocks), dim3(128 * HPB), 0, st,
+                       static_cast<const bf16_t*>(qkv), pos, tab ? tab->cs : nullptr, tab ? tab->rows : 1,
+                       static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, B, S, nh,
+                       nkv, scale_log2);
     return hipGetLastError();
 }
 
@@ -1634,14 +1901,38 @@ static hipError_t prefill_rope_sel(const void* qkv, const int64_t* pos, const Ro
     return prefill_go<D, HPB, true, false>(qkv, pos, tab, o, kc, vc, ctx, B, S, nh, nkv, st);
 }
 
+// q and k already rotated: the 32x32 matrix-op kernel, HPB heads per workgroup
+template <int D, int HPB>
+static hipError_t m32_go(const void* qkv, const int64_t* pos, void* o, void* kc, void* vc, int64_t ctx, int B,
+                         int S_max, int nh, int nkv, const int* cu, int total, hipStream_t st) {
+    const int g = nh / nkv;
+    const unsigned blocks = static_cast<unsigned>((S_max + 63) / 64) * B * nkv * (g / HPB);
+    const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
+    hipLaunchKernelGGL((attn_prefill_m32_kernel<D, HPB>), dim3(blocks), dim3(128 * HPB), 0, st,
+                       static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
+                       static_cast<bf16_t*>(vc), ctx, B, S_max, nh, nkv, scale_log2, cu, total);
+    return hipGetLastError();
+}
+
+// two heads per workgroup and two workgroups per compute unit when the group size allows (see below)
+template <int D>
+static hipError_t m32_sel(const void* qkv, const int64_t* pos, void* o, void* kc, void* vc, int64_t ctx, int B,
+                          int S_max, int nh, int nkv, const int* cu, int total, hipStream_t st) {
+    if ((nh / nkv) % 2 == 0) return m32_go<D, 2>(qkv, pos, o, kc, vc, ctx, B, S_max, nh, nkv, cu, total, st);
+    return m32_go<D, 1>(qkv, pos, o, kc, vc, ctx, B, S_max, nh, nkv, cu, total, st);
+}
+
 template <int D>
 static hipError_t prefill_hpb_sel(const void* qkv, const int64_t* pos, const RopeTab* tab, int il, void* o, void* kc,
                                   void* vc, int64_t ctx, int B, int S, int nh, int nkv, hipStream_t st) {
     const int g = nh / nkv;
-    // two heads per workgroup and two workgroups per compute unit (the kernel is built for two waves
-    // per SIMD): the two waves on a SIMD then belong to different workgroups, whose tile barriers do not
-    // line them up. In the layer this is 3% faster than four heads per workgroup at d = 128 (the few
-    // spilled registers are touched only outside the tile loop and on the masked tiles) and 18% at d = 64.
+    // q and k already rotated (the layer path): the 32x32 matrix-op kernel (3.6% faster than the 16x16
+    // direct-load kernel at d = 128 and 4.6% at d = 64 in the layer). Its byte offsets are 32-bit.
+    if (!tab && static_cast<int64_t>(S) * (nh + 2 * nkv) * D * 2 < (int64_t(1) << 32))
+        return m32_sel<D>(qkv, pos, o, kc, vc, ctx, B, S, nh, nkv, nullptr, 0, st);
+    // RoPE on load (or offsets past 32 bits): two heads per workgroup and two workgroups per compute unit
+    // (the kernel is built for two waves per SIMD), so the two waves on a SIMD belong to different
+    // workgroups, whose tile barriers do not line them up.
     if (g % 2 == 0) return prefill_rope_sel<D, 2>(qkv, pos, tab, il, o, kc, vc, ctx, B, S, nh, nkv, st);
     return prefill_rope_sel<D, 1>(qkv, pos, tab, il, o, kc, vc, ctx, B, S, nh, nkv, st);
 }
@@ -1953,37 +2244,15 @@ hipError_t launch_attn_prefill_chunk(int dtype, const void* qkv, const int64_t* 
 }
 
 // Packed (varlen) prefill: sequence i is tokens cu[i] .. cu[i+1]-1 of `total`; causal attention within
-// each sequence; q and k already rotated.
-template <int D, int HPB>
-static hipError_t varlen_go(const void* qkv, const int* cu, int nseq, int max_seqlen, int total, void* o, int nh,
-                            int nkv, hipStream_t st) {
-    const int g = nh / nkv;
-    const int nqb = (max_seqlen + 63) / 64;
-    const unsigned blocks = static_cast<unsigned>(nqb) * nseq * nkv * (g / HPB);
-    const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
-    hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, false>), dim3(blocks), dim3(128 * HPB), 0, st,
-                       static_cast<const bf16_t*>(qkv), nullptr, static_cast<bf16_t*>(o), nullptr, nullptr, 1, nseq,
-                       max_seqlen, nh, nkv, scale_log2, cu, total, 1, nullptr);
-    return hipGetLastError();
-}
-
-template <int D>
-static hipError_t varlen_hpb_sel(const void* qkv, const int* cu, int nseq, int max_seqlen, int total, void* o, int nh,
-                                 int nkv, hipStream_t st) {
-    const int g = nh / nkv;
-    // two heads per workgroup, two workgroups per compute unit, as for prefill (0.159 -> 0.142 ms on
-    // nine packed sequences of 64-2048 tokens, 8B shape)
-    if (g % 2 == 0) return varlen_go<D, 2>(qkv, cu, nseq, max_seqlen, total, o, nh, nkv, st);
-    return varlen_go<D, 1>(qkv, cu, nseq, max_seqlen, total, o, nh, nkv, st);
-}
-
+// each sequence; q and k already rotated. The 32x32 matrix-op kernel with per-sequence bounds (two heads per
+// workgroup, two workgroups per compute unit, as for prefill).
 hipError_t launch_attn_prefill_varlen(int dtype, const void* qkv, const int* cu, int nseq, int max_seqlen, int total,
                                       void* o, int nh, int nkv, int d, hipStream_t st) {
     if (nseq == 0 || total == 0 || max_seqlen == 0) return hipSuccess;
     const bool offsets_ok = static_cast<int64_t>(max_seqlen) * (nh + 2 * nkv) * d * 2 < (int64_t(1) << 32);
     if (attn_mfma_supported(dtype, d, nh, nkv) && offsets_ok) {
-        if (d == 128) return varlen_hpb_sel<128>(qkv, cu, nseq, max_seqlen, total, o, nh, nkv, st);
-        return varlen_hpb_sel<64>(qkv, cu, nseq, max_seqlen, total, o, nh, nkv, st);
+        if (d == 128) return m32_sel<128>(qkv, nullptr, o, nullptr, nullptr, 1, nseq, max_seqlen, nh, nkv, cu, total, st);
+        return m32_sel<64>(qkv, nullptr, o, nullptr, nullptr, 1, nseq, max_seqlen, nh, nkv, cu, total, st);
     }
     const unsigned blocks = static_cast<unsigned>((static_cast<int64_t>(total) * nh + 3) / 4);
     const float scale = 1.f / sqrtf(static_cast<float>(d));
