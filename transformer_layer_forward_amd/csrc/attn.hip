@@ -812,8 +812,10 @@ __global__ __launch_bounds__(128 * HPB, HPB == 2 ? 2 : 1) void attn_prefill_dire
 //    O^T += V^T P^T for keys 16s .. 16s + 15 of the block, in the key order {4h .. 4h+3, 8+4h .. 8+4h+3}
 //    for h = l / 32; the V^T operand (32 dims x those keys) comes from two transposing LDS reads
 //    (each gives a lane 4 consecutive keys of its dim).
-//  * OCC waves per SIMD (the register budget is 512 / OCC).
-template <int D, int HPB, int OCC>
+//  * OCC waves per SIMD (the register budget is 512 / OCC). With PIPE a wave overlaps tile j+1's scores
+//    with tile j's softmax (two score sets); without, it runs scores, softmax and P V of one tile in turn
+//    (one set, fewer registers), leaving the overlap to the other waves of its SIMD.
+template <int D, int HPB, int OCC, bool PIPE>
 __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
     const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, bf16_t* __restrict__ out, bf16_t* __restrict__ kc,
     bf16_t* __restrict__ vc, int64_t ctx, int B, int S_max, int nh, int nkv, float scale_log2,
@@ -970,13 +972,74 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
         pfr[ks] = __builtin_bit_cast(bf16x8, pack8(p_));                                                   \
     }
 
-    float m_i = 0.f, l_i = 0.f, mbA = 0.f, mbB = 0.f;
+    float m_i = 0.f, l_i = 0.f;
     f32x16 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-    f32x16 sA[NKF], sB[NKF];
+    f32x16 sA[NKF];
     bf16x8 pfr[NKS];
 
+    if constexpr (!PIPE) {
+        // tile j's K and V load during tile j-1; both buffers of tile j-1 are free after its barrier
+        issue_tiles(0, 0, 0, 0);
+        __syncthreads();
+        for (int j = 0; j < nkt; ++j) {
+            issue_tiles(j + 1, (j + 1) & 1, j + 1, (j + 1) & 1);
+            {
+                f32x16 z_;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) z_[e] = -m_i;
+#pragma unroll
+                for (int kf = 0; kf < NKF; ++kf) sA[kf] = z_;
+            }
+            PM_QK(sA, j & 1, 0)
+            PM_QK(sA, j & 1, KH)
+            if (__builtin_expect((j + 1) * BKV - 1 > lo, 0)) {
+                __asm__ volatile("");
+#pragma unroll
+                for (int kf = 0; kf < NKF; ++kf)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = j * BKV + kf * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+                        if (key > qlim) sA[kf][e] = -INFINITY;
+                    }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kf = 0; kf < NKF; ++kf)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sA[kf][e]);
+            {
+                const auto a_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(a_[0]), __uint_as_float(a_[1]));
+            }
+            // the scores are relative to m_i: move the reference on the first tile or by more than kSlack
+            const float shift_ = (j == 0 || mx > kSlack) ? mx : 0.f;
+            if (__builtin_expect(__any(shift_ != 0.f), 0)) {
+                __asm__ volatile("");
+                const float alpha = j == 0 ? 1.f : fast_exp2(-shift_);
+                m_i += shift_;
+                l_i *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+#pragma unroll
+                for (int kf = 0; kf < NKF; ++kf) sA[kf] -= shift_;
+            }
+            float ls = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < HS; ++ks) PM_EXP_STEP(sA, ks)
+#pragma unroll
+            for (int ks = 0; ks < HS; ++ks) PM_PV_STEP(j & 1, ks)
+#pragma unroll
+            for (int ks = HS; ks < NKS; ++ks) PM_EXP_STEP(sA, ks)
+#pragma unroll
+            for (int ks = HS; ks < NKS; ++ks) PM_PV_STEP(j & 1, ks)
+            l_i += ls;
+            __syncthreads();
+        }
+    } else {
+    float mbA = 0.f, mbB = 0.f;
+    f32x16 sB[NKF];
     issue_tiles(0, 0, 0, 0);
     issue_k_only(1, 1);
     __syncthreads();
@@ -1047,6 +1110,7 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
                 PM_ITER(sB, mbB, sA, mbA)
             }
         }
+    }
     }
 #undef PM_ITER
 #undef PM_QK
@@ -1911,11 +1975,13 @@ static hipError_t m32_go(const void* qkv, const int64_t* pos, void* o, void* kc,
     const int g = nh / nkv;
     const unsigned blocks = static_cast<unsigned>((S_max + 63) / 64) * B * nkv * (g / HPB);
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
-    // 64-key tiles; two waves per SIMD at d = 128 (~230 registers), three at d = 64 (150 registers; 12%
-    // faster than two in the 1B layer, 0.108 -> 0.095 ms). 32-key tiles measured slower: 4% at d = 128
-    // (two waves per SIMD), 2% at d = 64 (four).
-    constexpr int OCC = HPB == 2 ? (D == 64 ? 3 : 2) : 1;
-    hipLaunchKernelGGL((attn_prefill_m32_kernel<D, HPB, OCC>), dim3(blocks), dim3(128 * HPB), 0, st,
+    // d = 128: the pipelined form at two waves per SIMD (~230 registers). d = 64: the plain form at four
+    // waves per SIMD (117 registers): in the 1B layer 0.108 ms pipelined at two, 0.095 at three (150
+    // registers), 0.090 plain at four. 32-key tiles measured slower: 4% at d = 128 (pipelined, two waves
+    // per SIMD, or plain at three), 2% at d = 64.
+    constexpr bool PIPE = D != 64;
+    constexpr int OCC = HPB == 2 ? (PIPE ? 2 : 4) : 1;
+    hipLaunchKernelGGL((attn_prefill_m32_kernel<D, HPB, OCC, PIPE>), dim3(blocks), dim3(128 * HPB), 0, st,
                        static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
                        static_cast<bf16_t*>(vc), ctx, B, S_max, nh, nkv, scale_log2, cu, total);
     return hipGetLastError();
