@@ -11,12 +11,11 @@
 // transposed, S^T = K Q^T, with K as the MFMA A operand and Q (in registers) as B: the output
 // fragment then holds, per lane, one query column and a few keys, which after the fp32 online
 // softmax (exp2 with log2(e)/sqrt(d) folded into the scale) is exactly the B-operand layout of
-// O^T += V^T P^T. Three variants: with q and k already rotated, K and V go global -> LDS by direct
-// loads, V stays [key][d] and its V^T operand comes from transposing LDS reads, and a per-wave
-// software pipeline overlaps the next tile's Q K^T with the current softmax; the layer path runs this
-// on 32x32x16 matrix ops (attn_prefill_m32_kernel), the chunked path on 16x16x32
-// (attn_prefill_direct_kernel). With RoPE applied on load (the standalone entry point) tiles pass
-// through registers, are rotated there, and V is transposed into LDS as [d][key] while it is stored.
+// O^T += V^T P^T. Two variants: with q and k already rotated (the layer, varlen and chunked paths:
+// attn_prefill_m32_kernel, on 32x32x16 matrix ops) K and V go global -> LDS by direct loads, V stays
+// [key][d] and its V^T operand comes from transposing LDS reads; with RoPE applied on load (the
+// standalone entry point: attn_prefill_mfma_kernel, 16x16x32) tiles pass through registers, are
+// rotated there, and V is transposed into LDS as [d][key] while it is stored.
 // Rows are XOR-swizzled so the lanes of an operand read hit distinct banks.
 // Causality: query block qb only visits key tiles 0..qb; only the diagonal tile is masked.
 // Blocks are issued heaviest-first (largest qb first); consecutive blocks of one qb level
@@ -389,19 +388,7 @@ __global__ __launch_bounds__(128 * HPB) void attn_prefill_mfma_kernel(
     }
 }
 
-// ------------------------------------------------------------------ prefill, matrix cores, direct tile loads
-// Used when no RoPE is applied inside attention (the layer path: q and k arrive rotated). Workgroup
-// and wave layout as above; differences:
-//  * K and V tiles go global -> LDS with global_load_lds_dwordx4 (no register staging, no vector ALU
-//    work); both are stored row-major [key][dim] with 16-byte chunks XOR-swizzled by row.
-//  * V^T fragments are read with the transposing ds_read_b64_tr_b16: within each 16-lane group,
-//    lane i receives element i % 4 of the 8-byte words addressed by lanes 4e + i/4 (e = 0..3), so
-//    lanes addressing 4 consecutive key rows x 4 dim groups hand every lane 4 keys of one dim. Two
-//    such reads give the 8 keys {32t + 4g + 0..3, 32t + 16 + 4g + 0..3} that the P^T operand holds.
-//  * per-wave software pipeline: tile j+1's score matrix ops overlap tile j's softmax, tile j's P V
-//    overlaps its second half of exponentials; K runs one tile ahead of V (two buffers each). Score
-//    accumulators start at minus the reference max the wave held when they were issued; a moved
-//    reference (rare: only by more than kSlack) is corrected under a wave-uniform branch.
+// ------------------------------------------------------------------ prefill, direct tile loads: helpers
 // max / sum over lanes l, l^16, l^32, l^48 (the four 16-lane rows of a wave) with the gfx950 lane
 // swaps: vector ALU only, so unlike an LDS-routed shuffle it does not wait behind pending LDS reads
 __device__ __forceinline__ float rows_max(float x) {
@@ -423,403 +410,39 @@ __device__ __forceinline__ int vt_phys(int r, int c) {
     else return c ^ (2 * ((r >> 1) & 1)) ^ (4 * ((r >> 2) & 1));
 }
 
-template <int D, int HPB, bool CACHED, bool SPLIT = false>
-__global__ __launch_bounds__(128 * HPB, HPB == 2 ? 2 : 1) void attn_prefill_direct_kernel(
-    const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, bf16_t* __restrict__ out, bf16_t* __restrict__ kc,
-    bf16_t* __restrict__ vc, int64_t ctx, int B, int S_max, int nh, int nkv, float scale_log2,
-    const int* __restrict__ cu, int total, int nsplit, float* __restrict__ part) {
-    using C = PrefillCfg<D>;
-    constexpr int NT = 128 * HPB, NW = NT / 64;
-    constexpr int CH = D / 8;                        // 16-byte chunks per row
-    constexpr int RPI = 64 / CH;                     // rows per 1 KiB direct load
-    constexpr int LOADS = C::BKV / RPI;              // direct loads per K (or V) tile
-    constexpr int LPW = (2 * LOADS) / NW;            // direct loads per wave per iteration (K and V)
-    static_assert((2 * LOADS) % NW == 0, "loads split evenly over the waves");
-    constexpr int KH = C::KC32 / 2;
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    __shared__ __align__(16) bf16_t sK[2][C::K_ELEMS];
-    __shared__ __align__(16) bf16_t sV[2][C::V_ELEMS];
-
-    const int g = nh / nkv;
-    const int hchunks = g / HPB;
-    const int nqb = (S_max + C::BQ - 1) / C::BQ;
-    if constexpr (!SPLIT) nsplit = 1;
-    const int per_qb = B * nkv * hchunks * nsplit;
-    const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / per_qb;
-    int rem = static_cast<int>(blockIdx.x) % per_qb;
-    const int split = rem % nsplit;
-    rem /= nsplit;
-    const int hc = rem % hchunks;
-    rem /= hchunks;
-    const int c = rem % nkv;
-    const int b = rem / nkv;
-
-    // ---- the sequence: B sequences of S_max tokens, or (packed, cu given) sequence b = tokens
-    // cu[b] .. cu[b+1]-1 of `total`, clamped into range so any cu contents stay in bounds. Query blocks
-    // past the sequence's end have nothing to do.
-    int seq0, S;
-    if (cu != nullptr) {
-        const int a0 = min(max(cu[b], 0), total);
-        const int a1 = min(max(cu[b + 1], a0), total);
-        seq0 = a0;
-        S = min(a1 - a0, S_max);
-    } else {
-        seq0 = b * S_max;
-        S = S_max;
-    }
-    if (qb * C::BQ >= S) return;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar descriptor choice
-    const int lrow = lane & 15, lgrp = lane >> 4;
-    const int h = c * g + hc * HPB + (wave >> 1);
-    const int64_t rs = static_cast<int64_t>(nh + 2 * nkv) * D;  // packed row stride
-    const bf16_t* qkv_b = qkv + static_cast<int64_t>(seq0) * rs;
-    const int q0 = qb * C::BQ + (wave & 1) * 32;
-
-    // ---- visibility: query i sees keys 0 .. lim(i). Over the call's own tokens lim(i) = i; over a
-    // cache (chunked prefill on a prefix) the keys are cache slots and lim(i) = position_ids[b, i]
-    // (clamped to the cache). The block's smallest and largest limits give the key tiles it visits
-    // (0 .. hi / 64) and the first one that needs the mask.
-    const int64_t* pos_b = CACHED ? pos + seq0 : nullptr;
-    auto lim_of = [&](int qi) -> int {
-        if constexpr (CACHED) return static_cast<int>(clamp_pos(pos_b[qi], ctx));
-        else return qi;
-    };
-    int lo, hi;
-    {
-        const int qi = qb * C::BQ + lane;
-        const int qv = qi < S ? qi : S - 1;
-        int l = lim_of(qv);
-        int m = l;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            l = min(l, __shfl_xor(l, o, 64));
-            m = max(m, __shfl_xor(m, o, 64));
-        }
-        lo = __builtin_amdgcn_readfirstlane(l);
-        hi = __builtin_amdgcn_readfirstlane(m);
-    }
-    // key tiles of this split: the visible tiles 0 .. hi / 64 shared out evenly over nsplit workgroups
-    const int nkt_all = hi / C::BKV + 1;
-    const int j0 = SPLIT ? split * nkt_all / nsplit : 0;
-    const int j1 = SPLIT ? (split + 1) * nkt_all / nsplit : nkt_all;
-    if (SPLIT && j0 >= j1) {   // nothing visible here: an empty record (weight zero in the combine)
-        {
-#pragma unroll
-            for (int qf = 0; qf < 2; ++qf) {
-                const int qi = q0 + qf * 16 + lrow;
-                if (qi >= S) continue;
-                float* rec = part + ((static_cast<int64_t>(seq0) + qi) * nh + h) * nsplit * (D + 4) +
-                             static_cast<int64_t>(split) * (D + 4);
-                if (lgrp == 0) {
-                    rec[0] = -INFINITY;
-                    rec[1] = 0.f;
-                }
-#pragma unroll
-                for (int a = 0; a < C::DF; ++a)
-                    *reinterpret_cast<f32x4*>(rec + 4 + a * 16 + 4 * lgrp) = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-        return;
-    }
-    int qlim[2];
-#pragma unroll
-    for (int qf = 0; qf < 2; ++qf) {
-        const int qi = q0 + qf * 16 + lrow;
-        qlim[qf] = lim_of(qi < S ? qi : S - 1);
-    }
-
-    // ---- Q fragments (B operand of S^T = K Q^T): lane holds query q0 + qf*16 + lrow, dims k*32 + lgrp*8 ..
-    bf16x8 qfr[2][C::KC32];
-#pragma unroll
-    for (int qf = 0; qf < 2; ++qf) {
-        const int qi = q0 + qf * 16 + lrow;
-        const int qs = qi < S ? qi : S - 1;
-        const bf16_t* qp = qkv_b + static_cast<int64_t>(qs) * rs + static_cast<int64_t>(h) * D;
-#pragma unroll
-        for (int k = 0; k < C::KC32; ++k) {
-            float f[8];
-            unpack8(*reinterpret_cast<const uint4*>(qp + k * 32 + lgrp * 8), f);
-            // fold log2(e)/sqrt(d) into q: the scores come out in log2 units, ready for exp2
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] *= scale_log2;
-            uint4 u = pack8(f);
-            if (qi >= S) u = make_uint4(0, 0, 0, 0);
-            qfr[qf][k] = __builtin_bit_cast(bf16x8, u);
-        }
-    }
-
-    // ---- direct tile loads. Load q (0 .. 2*LOADS-1; q < LOADS: K, else V) covers rows (q % LOADS)*RPI ..
-    // + RPI-1 of the tile; lane l lands at physical chunk l % CH of row l / CH and fetches the logical
-    // chunk the swizzle puts there. Keys past S read the clamped row S-1 (masked, zero weight). Buffer
-    // (MUBUF) loads based at this kv head's first K and V element, with 32-bit byte offsets (the
-    // caller checks S * row stride fits); unlike the flat-segment form they let the compiler wait for
-    // individual LDS reads rather than all of them.
-    const int64_t cache_b = (static_cast<int64_t>(b) * ctx * nkv + c) * D;
-    const bf16_t* kbase = CACHED ? kc + cache_b : qkv_b + static_cast<int64_t>(nh + c) * D;
-    const bf16_t* vbase = CACHED ? vc + cache_b : qkv_b + static_cast<int64_t>(nh + nkv + c) * D;
-    const uint32_t rs_bytes = static_cast<uint32_t>(CACHED ? static_cast<int64_t>(nkv) * D : rs) * 2u;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kbase), (short)0, -1, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vbase), (short)0, -1, 0x00020000);
-
-    // ---- cache append: the first head chunk of each query block copies the block's own keys and
-    // values (its diagonal tile) to their slots, so every token is written exactly once
-    if (!CACHED && kc != nullptr && hc == 0 && split == 0) {
-        const int64_t* pos_b = pos + seq0;
-        for (int job = tid; job < 2 * C::BKV * CH; job += NT) {
-            const bool isv = job >= C::BKV * CH;
-            const int jj = isv ? job - C::BKV * CH : job;
-            const int r = jj / CH, ch = jj % CH;
-            const int key = qb * C::BKV + r;
-            if (key < S) {
-                const int64_t slot = clamp_pos(pos_b[key], ctx);
-                const uint4 v = *reinterpret_cast<const uint4*>((isv ? vbase : kbase) + static_cast<int64_t>(key) * rs + ch * 8);
-                bf16_t* dst = (isv ? vc : kc) + ((static_cast<int64_t>(b) * ctx + slot) * nkv + c) * D + ch * 8;
-                *reinterpret_cast<uint4*>(dst) = v;
-            }
-        }
-    }
-    auto issue_tiles = [&](int ktile, int kbuf, int vtile, int vbuf) {
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int q = wave * LPW + i;
-            const bool isv = q >= LOADS;
-            const int r = (q % LOADS) * RPI + lane / CH, pc = lane % CH;
-            const int key = min((isv ? vtile : ktile) * C::BKV + r, hi);
-            const int lc = isv ? vt_phys<D>(r, pc) : k_phys<D>(r, pc);
-            const uint32_t off = static_cast<uint32_t>(key) * rs_bytes + static_cast<uint32_t>(lc) * 16u;
-            bf16_t* dst = isv ? &sV[vbuf][(q % LOADS) * RPI * D] : &sK[kbuf][(q % LOADS) * RPI * D];
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (__attribute__((address_space(3))) void*)dst, 16,
-                                                     off, 0, 0, 0);
-        }
-    };
-    auto issue_k_only = [&](int ktile, int kbuf) {   // prologue: K of tile 1
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int q = wave * LPW + i;
-            if (q < LOADS) {
-                const int r = q * RPI + lane / CH, pc = lane % CH;
-                const int key = min(ktile * C::BKV + r, hi);
-                const uint32_t off = static_cast<uint32_t>(key) * rs_bytes + static_cast<uint32_t>(k_phys<D>(r, pc)) * 16u;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)&sK[kbuf][q * RPI * D],
-                                                         16, off, 0, 0, 0);
-            }
-        }
-    };
-
-    // Q K^T k steps [k0, k0 + KH) of the tile in K buffer kb into accumulators SN
-#define PD_QK_HALF(SN, kb, k0)                                                                             \
-    _Pragma("unroll") for (int k = (k0); k < (k0) + KH; ++k) {                                             \
-        _Pragma("unroll") for (int kf = 0; kf < 4; ++kf) {                                                 \
-            const int r = kf * 16 + lrow;                                                                  \
-            const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&sK[kb][r * D + k_phys<D>(r, k * 4 + lgrp) * 8]); \
-            SN[kf][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qfr[0][k], SN[kf][0], 0, 0, 0);        \
-            SN[kf][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, qfr[1][k], SN[kf][1], 0, 0, 0);        \
-        }                                                                                                  \
-    }
-    // O^T += V^T P^T for the 32 keys of half t (V buffer vb); V^T fragments by two transposing reads
-#define PD_PV_HALF(vb, t)                                                                                  \
-    _Pragma("unroll") for (int a = 0; a < C::DF; ++a) {                                                    \
-        s16x4 h_[2];                                                                                       \
-        _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                    \
-            const int r = 32 * (t) + 16 * u + 4 * lgrp + (lrow >> 2);                                      \
-            const int cc = 2 * a + ((lrow & 3) >> 1);                                                      \
-            h_[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(      \
-                &sV[vb][r * D + vt_phys<D>(r, cc) * 8 + (lrow & 1) * 4]));                                 \
-        }                                                                                                  \
-        const bf16x8 vfr = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h_[0], h_[1], 0, 1, 2, 3, 4, 5, 6, 7)); \
-        oacc[a][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, pfr[0][t], oacc[a][0], 0, 0, 0);          \
-        oacc[a][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr, pfr[1][t], oacc[a][1], 0, 0, 0);          \
-    }                                                                                                      \
-    if constexpr (MSUM) {                                                                                  \
-        lacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pfr[0][t], lacc[0], 0, 0, 0);              \
-        lacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pfr[1][t], lacc[1], 0, 0, 0);              \
-    }
-#define PD_EXP_HALF(SC, t)                                                                                 \
-    _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                                     \
-        float p_[2][4];                                                                                    \
-        _Pragma("unroll") for (int u = 0; u < 2; ++u)                                                      \
-            _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                                \
-                p_[u][r] = fast_exp2(SC[2 * (t) + u][qf][r]);                                              \
-                if constexpr (!MSUM) ls[qf] += p_[u][r];                                                   \
-            }                                                                                              \
-        uint4 u_;                                                                                          \
-        u_.x = pack_bf16x2(p_[0][0], p_[0][1]);                                                            \
-        u_.y = pack_bf16x2(p_[0][2], p_[0][3]);                                                            \
-        u_.z = pack_bf16x2(p_[1][0], p_[1][1]);                                                            \
-        u_.w = pack_bf16x2(p_[1][2], p_[1][3]);                                                            \
-        pfr[qf][t] = __builtin_bit_cast(bf16x8, u_);                                                       \
-    }
-
-    // D = 64: the row sums of P run on the matrix cores (ones x P^T into lacc, whose every element holds its
-    // query's sum of the bf16 P actually used by P V), which takes 32 vector adds per tile off the
-    // vector-bound loop; D = 128 keeps the vector sums (its registers are full)
-    constexpr bool MSUM = D == 64;
-    float m_i[2] = {0.f, 0.f}, l_i[2] = {0.f, 0.f};
-    f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
-    f32x4 oacc[C::DF][2];
-#pragma unroll
-    for (int a = 0; a < C::DF; ++a) oacc[a][0] = oacc[a][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 sA[4][2], sB[4][2];
-    float mbA[2] = {0.f, 0.f}, mbB[2] = {0.f, 0.f};   // reference max each accumulator set started from
-    if constexpr (SPLIT) m_i[0] = m_i[1] = -INFINITY;   // no reference yet (a split may start wholly masked)
-    bf16x8 pfr[2][2];
-
-    issue_tiles(j0, 0, j0, 0);
-    issue_k_only(j0 + 1, 1);
-    __syncthreads();
-#pragma unroll
-    for (int kf = 0; kf < 4; ++kf) sA[kf][0] = sA[kf][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    PD_QK_HALF(sA, 0, 0)
-    PD_QK_HALF(sA, 0, KH)
-    __syncthreads();   // K buffer 0 is refilled by the first iteration
-
-    // One iteration: tile j's scores are in SC (started from MBC); SN/MBN receive tile j+1. Every
-    // iteration issues the same work (past the end: clamped rows into buffers nobody reads), so each
-    // stage is one basic block in which matrix ops and vector work interleave.
-#define PD_ITER(SC, MBC, SN, MBN)                                                                          \
-    {                                                                                                      \
-        /* K(j+2) into the buffer K(j) used, V(j+1) into the buffer V(j-1) used: both free since the */    \
-        /* barrier that ended the previous iteration                                                 */    \
-        issue_tiles(j + 2, (j - j0) & 1, j + 1, (j - j0 + 1) & 1);                                         \
-        /* (branch hints keep these rare paths out of line: predicated, they cost more vector work */     \
-        /*  per tile than the softmax itself)                                                        */     \
-        if (__builtin_expect((j + 1) * C::BKV - 1 > lo, 0)) {                                              \
-            __asm__ volatile("");                                                                          \
-            _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                             \
-                _Pragma("unroll") for (int kf = 0; kf < 4; ++kf)                                           \
-                    _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                        \
-                        const int key = j * C::BKV + kf * 16 + 4 * lgrp + r;                               \
-                        if (key > qlim[qf]) SC[kf][qf][r] = -INFINITY;                                     \
-                    }                                                                                      \
-            }                                                                                              \
-        }                                                                                                  \
-        /* stage 1: first half of tile j+1's scores || column max of tile j */                            \
-        _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                                 \
-            MBN[qf] = (SPLIT ? m_i[qf] > -INFINITY : j != 0) ? m_i[qf] : 0.f;                              \
-            _Pragma("unroll") for (int kf = 0; kf < 4; ++kf) SN[kf][qf] = f32x4{-MBN[qf], -MBN[qf], -MBN[qf], -MBN[qf]}; \
-        }                                                                                                  \
-        PD_QK_HALF(SN, (j - j0 + 1) & 1, 0)                                                                \
-        float sub_[2], shift_[2];                                                                          \
-        bool fresh_[2];                                                                                    \
-        bool any_sub_ = false;                                                                             \
-        _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                                 \
-            float mx = -INFINITY;                                                                          \
-            _Pragma("unroll") for (int kf = 0; kf < 4; ++kf)                                               \
-                _Pragma("unroll") for (int r = 0; r < 4; ++r) mx = fmaxf(mx, SC[kf][qf][r]);               \
-            mx = rows_max(mx);                                                                             \
-            if constexpr (SPLIT) fresh_[qf] = m_i[qf] == -INFINITY;                                        \
-            const float delta = (SPLIT && fresh_[qf]) ? 0.f : m_i[qf] - MBC[qf];                           \
-            const float rel = mx - delta;                                                                  \
-            if constexpr (SPLIT) {                                                                         \
-                shift_[qf] = (fresh_[qf] ? rel > -INFINITY : rel > kSlack) ? rel : 0.f;                    \
-            } else {                                                                                       \
-                fresh_[qf] = j == 0;                                                                       \
-                shift_[qf] = (fresh_[qf] || rel > kSlack) ? rel : 0.f;                                     \
-            }                                                                                              \
-            sub_[qf] = delta + shift_[qf];                                                                 \
-            any_sub_ |= sub_[qf] != 0.f;                                                                   \
-        }                                                                                                  \
-        /* stage 2 (rare): re-reference tile j's scores, rescale O and l where the reference moved */     \
-        if (__builtin_expect(__any(any_sub_), 0)) {                                                        \
-            __asm__ volatile("");   /* a side effect: the block cannot be predicated into the hot path */ \
-            _Pragma("unroll") for (int qf = 0; qf < 2; ++qf) {                                             \
-                const float alpha = fresh_[qf] ? 1.f : fast_exp2(-shift_[qf]);                             \
-                m_i[qf] = (SPLIT && fresh_[qf] ? 0.f : m_i[qf]) + shift_[qf];                              \
-                l_i[qf] *= alpha;                                                                          \
-                if constexpr (MSUM) lacc[qf] *= alpha;                                                     \
-                _Pragma("unroll") for (int a = 0; a < C::DF; ++a) oacc[a][qf] *= alpha;                    \
-                _Pragma("unroll") for (int kf = 0; kf < 4; ++kf) SC[kf][qf] -= sub_[qf];                   \
-            }                                                                                              \
-        }                                                                                                  \
-        float ls[2] = {0.f, 0.f};                                                                          \
-        /* stage 3: second half of tile j+1's scores || exponentials of keys 0..31 */                      \
-        PD_QK_HALF(SN, (j - j0 + 1) & 1, KH)                                                               \
-        PD_EXP_HALF(SC, 0)                                                                                 \
-        /* stage 4: P V of keys 0..31 || exponentials of keys 32..63 */                                    \
-        PD_PV_HALF((j - j0) & 1, 0)                                                                        \
-        PD_EXP_HALF(SC, 1)                                                                                 \
-        /* stage 5: P V of keys 32..63 */                                                                  \
-        PD_PV_HALF((j - j0) & 1, 1)                                                                        \
-        l_i[0] += ls[0];                                                                                   \
-        l_i[1] += ls[1];                                                                                   \
-        __syncthreads();                                                                                   \
-    }
-    for (int j = j0; j < j1; j += 2) {
-        PD_ITER(sA, mbA, sB, mbB)
-        if (j + 1 >= j1) break;
-        {
-            const int j_ = j;
-            {
-                const int j = j_ + 1;
-                PD_ITER(sB, mbB, sA, mbA)
-            }
-        }
-    }
-#undef PD_ITER
-#undef PD_QK_HALF
-#undef PD_PV_HALF
-#undef PD_EXP_HALF
-
-    // ---- lane holds dims a*16 + 4 lgrp + {0..3} of query q0 + qf*16 + lrow. With key splits: this
-    // split's record for the combine kernel ([0] reference max, log2 units; [1] sum; [4..4+D) unnormalised
-    // o); else normalise and store.
-    if constexpr (SPLIT) {
-#pragma unroll
-        for (int qf = 0; qf < 2; ++qf) {
-            const float lsum = MSUM ? lacc[qf][0] : rows_sum(l_i[qf]);
-            const int qi = q0 + qf * 16 + lrow;
-            if (qi >= S) continue;
-            float* rec = part + ((static_cast<int64_t>(seq0) + qi) * nh + h) * nsplit * (D + 4) +
-                         static_cast<int64_t>(split) * (D + 4);
-            if (lgrp == 0) {
-                rec[0] = m_i[qf];
-                rec[1] = lsum;
-            }
-#pragma unroll
-            for (int a = 0; a < C::DF; ++a)
-                *reinterpret_cast<f32x4*>(rec + 4 + a * 16 + 4 * lgrp) = oacc[a][qf];
-        }
-        return;
-    }
-#pragma unroll
-    for (int qf = 0; qf < 2; ++qf) {
-        const float inv = 1.f / (MSUM ? lacc[qf][0] : rows_sum(l_i[qf]));
-        const int qi = q0 + qf * 16 + lrow;
-        if (qi >= S) continue;
-        bf16_t* op = out + (static_cast<int64_t>(seq0) + qi) * nh * D + static_cast<int64_t>(h) * D;
-#pragma unroll
-        for (int a = 0; a < C::DF; ++a) {
-            const f32x4 v = oacc[a][qf];
-            *reinterpret_cast<uint2*>(op + a * 16 + 4 * lgrp) =
-                make_uint2(pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv));
-        }
-    }
-}
-
 // ------------------------------------------------------------------ prefill, 32x32 matrix ops
-// The layer path's causal prefill (q and k already rotated, no cache prefix, no key split; packed
-// sequences through cu) on v_mfma_f32_32x32x16_bf16, which issues at full rate from a single wave,
-// where the 16x16x32 form of the kernel above needs both waves of a SIMD to keep the matrix core fed.
-// Same workgroup layout, LDS tiles, loads and pipeline as above; per wave 32 queries:
+// Causal prefill with q and k already rotated: the layer and varlen paths, and chunked prefill over a
+// cache prefix (CACHED, with an optional key split, SPLIT). Workgroup = (sequence, kv head, 64 queries)
+// with 2 waves per query head of the group (HPB heads), 32 queries per wave. On
+// v_mfma_f32_32x32x16_bf16, which issues at full rate from one wave (the 16x16x32 form needs two
+// waves per SIMD to keep the matrix core fed).
+//  * K and V tiles (64 keys) go global -> LDS by buffer loads straight into LDS (no register staging),
+//    both row-major [key][dim] with 16-byte chunks XOR-swizzled by row; double-buffered, V one tile
+//    behind K; every wave of the group reads them.
 //  * S^T = K Q^T per 32-key block: A = 32 keys x 16 dims of K (one 16-byte LDS read), B = the wave's
-//    Q^T (16 dims x 32 queries, resident). The accumulator gives lane l query l % 32 and keys
+//    resident Q^T (16 dims x 32 queries). The accumulator gives lane l query l % 32 and keys
 //    8i + 4(l/32) + r in register 4i + r, so a query's scores sit in two lanes (l, l ^ 32): its row
-//    max and row sum take one lane swap.
+//    max and row sum take one lane swap (v_permlane32_swap, no LDS round trip).
 //  * Registers 8s .. 8s + 7 of a block are exactly the B operand (16 keys x 32 queries) of
 //    O^T += V^T P^T for keys 16s .. 16s + 15 of the block, in the key order {4h .. 4h+3, 8+4h .. 8+4h+3}
-//    for h = l / 32; the V^T operand (32 dims x those keys) comes from two transposing LDS reads
-//    (each gives a lane 4 consecutive keys of its dim).
+//    for h = l / 32. The V^T operand (32 dims x those keys) comes from two transposing LDS reads
+//    (ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the 8-byte words
+//    addressed by lanes 4e + i/4, e = 0..3, so lanes addressing 4 consecutive key rows x 4 dim groups
+//    hand every lane 4 consecutive keys of one dim).
+//  * Online softmax in log2 units (q pre-scaled by log2(e)/sqrt(d)); score accumulators start at minus
+//    the running reference max, which moves only when a tile max exceeds it by more than kSlack (rare:
+//    corrected under a wave-uniform branch). Only the tiles crossing the diagonal are masked.
 //  * OCC waves per SIMD (the register budget is 512 / OCC). With PIPE a wave overlaps tile j+1's scores
 //    with tile j's softmax (two score sets); without, it runs scores, softmax and P V of one tile in turn
 //    (one set, fewer registers), leaving the overlap to the other waves of its SIMD.
-template <int D, int HPB, int OCC, bool PIPE>
+//  * CACHED: chunked prefill over a cache prefix (keys are cache slots, query i sees slots
+//    0 .. position_ids[b, i], clamped to the cache); SPLIT: the block's key tiles shared out over nsplit workgroups,
+//    each writing a (max, sum, unnormalised o) record per query for the combine kernel.
+template <int D, int HPB, int OCC, bool PIPE, bool CACHED = false, bool SPLIT = false>
 __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
     const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, bf16_t* __restrict__ out, bf16_t* __restrict__ kc,
     bf16_t* __restrict__ vc, int64_t ctx, int B, int S_max, int nh, int nkv, float scale_log2,
-    const int* __restrict__ cu, int total) {
+    const int* __restrict__ cu, int total, int nsplit, float* __restrict__ part) {
     constexpr int BQ = 64, BKV = 64;
     constexpr int NKF = BKV / 32;                    // 32-key blocks per tile
     constexpr int NKS = BKV / 16;                    // 16-key steps of P V per tile
@@ -840,16 +463,19 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
     const int g = nh / nkv;
     const int hchunks = g / HPB;
     const int nqb = (S_max + BQ - 1) / BQ;
-    const int per_qb = B * nkv * hchunks;
+    if constexpr (!SPLIT) nsplit = 1;
+    const int per_qb = B * nkv * hchunks * nsplit;
     const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / per_qb;   // heaviest blocks first
     int rem = static_cast<int>(blockIdx.x) % per_qb;
+    const int split = rem % nsplit;
+    rem /= nsplit;
     const int hc = rem % hchunks;
     rem /= hchunks;
     const int c = rem % nkv;
     const int b = rem / nkv;
 
     int seq0, S;
-    if (cu != nullptr) {   // packed sequences: bounds clamped into range, as in the kernels above
+    if (cu != nullptr) {   // packed sequences: bounds clamped into range, so any cu contents stay in bounds
         const int a0 = min(max(cu[b], 0), total);
         const int a1 = min(max(cu[b + 1], a0), total);
         seq0 = a0;
@@ -866,16 +492,56 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
     const int h = c * g + hc * HPB + (wave >> 1);
     const int64_t rs = static_cast<int64_t>(nh + 2 * nkv) * D;
     const bf16_t* qkv_b = qkv + static_cast<int64_t>(seq0) * rs;
-    // query i sees keys 0 .. i: the block visits key tiles 0 .. hi / BKV; only the diagonal is masked
-    const int lo = qb * BQ, hi = min(qb * BQ + BQ - 1, S - 1);
-    const int nkt = hi / BKV + 1;
+    // visibility: query i sees keys 0 .. lim(i): lim(i) = i over the call's own tokens, position_ids[b, i]
+    // (clamped to the cache) over a cache. The block's smallest and largest limits give the key tiles it
+    // visits (0 .. hi / BKV) and the first one that needs the mask.
+    const int64_t* pos_b = CACHED ? pos + seq0 : nullptr;
+    auto lim_of = [&](int q) -> int {
+        if constexpr (CACHED) return static_cast<int>(clamp_pos(pos_b[q], ctx));
+        else return q;
+    };
+    int lo, hi;
+    if constexpr (CACHED) {
+        int l = lim_of(min(qb * BQ + lane, S - 1));
+        int m = l;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            l = min(l, __shfl_xor(l, o, 64));
+            m = max(m, __shfl_xor(m, o, 64));
+        }
+        lo = __builtin_amdgcn_readfirstlane(l);
+        hi = __builtin_amdgcn_readfirstlane(m);
+    } else {
+        lo = qb * BQ;
+        hi = min(qb * BQ + BQ - 1, S - 1);
+    }
+    const int nkt_all = hi / BKV + 1;
+    const int j0 = SPLIT ? split * nkt_all / nsplit : 0;
+    const int j1 = SPLIT ? (split + 1) * nkt_all / nsplit : nkt_all;
     const int qi = qb * BQ + (wave & 1) * 32 + l32;
-    const int qlim = min(qi, S - 1);
+    const int qrow = min(qi, S - 1);
+    const int qlim = lim_of(qrow);
+    auto record = [&](int q) {   // this split's record of query q: [0] max (log2 units), [1] sum, [4..) o
+        return part + ((static_cast<int64_t>(seq0) + q) * nh + h) * nsplit * (D + 4) + static_cast<int64_t>(split) * (D + 4);
+    };
+    if (SPLIT && j0 >= j1) {   // no visible key tile here: an empty record (weight zero in the combine)
+        if (qi < S) {
+            float* rec = record(qi);
+            if (lh == 0) {
+                rec[0] = -INFINITY;
+                rec[1] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < D / 8; ++e)
+                *reinterpret_cast<f32x4*>(rec + 4 + 8 * e + 4 * lh) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        return;
+    }
 
     // Q^T fragments: lane holds query qi, dims 16k + 8 lh .. + 7, pre-scaled by log2(e)/sqrt(d), bf16
     bf16x8 qfr[KS];
     {
-        const bf16_t* qp = qkv_b + static_cast<int64_t>(qlim) * rs + static_cast<int64_t>(h) * D;
+        const bf16_t* qp = qkv_b + static_cast<int64_t>(qrow) * rs + static_cast<int64_t>(h) * D;
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
             float f[8];
@@ -888,14 +554,15 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
         }
     }
 
-    const bf16_t* kbase = qkv_b + static_cast<int64_t>(nh + c) * D;
-    const bf16_t* vbase = qkv_b + static_cast<int64_t>(nh + nkv + c) * D;
-    const uint32_t rs_bytes = static_cast<uint32_t>(rs) * 2u;
+    const int64_t cache_b = (static_cast<int64_t>(b) * ctx * nkv + c) * D;
+    const bf16_t* kbase = CACHED ? kc + cache_b : qkv_b + static_cast<int64_t>(nh + c) * D;
+    const bf16_t* vbase = CACHED ? vc + cache_b : qkv_b + static_cast<int64_t>(nh + nkv + c) * D;
+    const uint32_t rs_bytes = static_cast<uint32_t>(CACHED ? static_cast<int64_t>(nkv) * D : rs) * 2u;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kbase), (short)0, -1, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vbase), (short)0, -1, 0x00020000);
 
     // cache append: the first head chunk of each query block copies the block's own keys and values
-    if (kc != nullptr && hc == 0) {
+    if (!CACHED && kc != nullptr && hc == 0 && split == 0) {
         const int64_t* pos_b = pos + seq0;
         for (int job = tid; job < 2 * BQ * CH; job += NT) {
             const bool isv = job >= BQ * CH;
@@ -910,7 +577,11 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
             }
         }
     }
-    // direct loads as in the kernel above
+    // direct loads. Load q (0 .. 2 LOADS - 1; q < LOADS: K, else V) covers rows (q % LOADS) * RPI .. + RPI - 1
+    // of the tile; lane l lands at physical chunk l % CH of row l / CH and fetches the logical chunk the
+    // swizzle puts there. Keys past the block's last visible key read that key's row (masked, zero weight).
+    // Buffer loads based at this kv head's first K and V element, with 32-bit byte offsets (the caller checks
+    // that the rows fit).
     auto issue_tiles = [&](int ktile, int kbuf, int vtile, int vbuf) {
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
@@ -981,19 +652,23 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
 
     if constexpr (!PIPE) {
         // tile j's K and V load during tile j-1; both buffers of tile j-1 are free after its barrier
-        issue_tiles(0, 0, 0, 0);
+        if constexpr (SPLIT) m_i = -INFINITY;   // no reference yet (a split may start wholly masked)
+        issue_tiles(j0, 0, j0, 0);
         __syncthreads();
-        for (int j = 0; j < nkt; ++j) {
-            issue_tiles(j + 1, (j + 1) & 1, j + 1, (j + 1) & 1);
+        for (int j = j0; j < j1; ++j) {
+            const int bf = (j - j0) & 1;
+            issue_tiles(j + 1, bf ^ 1, j + 1, bf ^ 1);
+            const bool fresh = SPLIT ? m_i == -INFINITY : j == j0;
             {
+                const float ref = fresh ? 0.f : m_i;
                 f32x16 z_;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) z_[e] = -m_i;
+                for (int e = 0; e < 16; ++e) z_[e] = -ref;
 #pragma unroll
                 for (int kf = 0; kf < NKF; ++kf) sA[kf] = z_;
             }
-            PM_QK(sA, j & 1, 0)
-            PM_QK(sA, j & 1, KH)
+            PM_QK(sA, bf, 0)
+            PM_QK(sA, bf, KH)
             if (__builtin_expect((j + 1) * BKV - 1 > lo, 0)) {
                 __asm__ volatile("");
 #pragma unroll
@@ -1013,12 +688,14 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
                 const auto a_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
                 mx = fmaxf(__uint_as_float(a_[0]), __uint_as_float(a_[1]));
             }
-            // the scores are relative to m_i: move the reference on the first tile or by more than kSlack
-            const float shift_ = (j == 0 || mx > kSlack) ? mx : 0.f;
-            if (__builtin_expect(__any(shift_ != 0.f), 0)) {
+            // the scores are relative to the reference: set it on the first tile with a visible key, move it
+            // when a tile max exceeds it by more than kSlack
+            const bool upd = fresh ? mx > -INFINITY : mx > kSlack;
+            const float shift_ = upd ? mx : 0.f;
+            if (__builtin_expect(__any(upd), 0)) {
                 __asm__ volatile("");
-                const float alpha = j == 0 ? 1.f : fast_exp2(-shift_);
-                m_i += shift_;
+                const float alpha = fresh ? 1.f : fast_exp2(-shift_);
+                if (upd) m_i = (fresh ? 0.f : m_i) + shift_;
                 l_i *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
@@ -1029,19 +706,20 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
 #pragma unroll
             for (int ks = 0; ks < HS; ++ks) PM_EXP_STEP(sA, ks)
 #pragma unroll
-            for (int ks = 0; ks < HS; ++ks) PM_PV_STEP(j & 1, ks)
+            for (int ks = 0; ks < HS; ++ks) PM_PV_STEP(bf, ks)
 #pragma unroll
             for (int ks = HS; ks < NKS; ++ks) PM_EXP_STEP(sA, ks)
 #pragma unroll
-            for (int ks = HS; ks < NKS; ++ks) PM_PV_STEP(j & 1, ks)
+            for (int ks = HS; ks < NKS; ++ks) PM_PV_STEP(bf, ks)
             l_i += ls;
             __syncthreads();
         }
     } else {
     float mbA = 0.f, mbB = 0.f;
     f32x16 sB[NKF];
-    issue_tiles(0, 0, 0, 0);
-    issue_k_only(1, 1);
+    if constexpr (SPLIT) m_i = -INFINITY;   // no reference yet (a split may start wholly masked)
+    issue_tiles(j0, 0, j0, 0);
+    issue_k_only(j0 + 1, 1);
     __syncthreads();
 #pragma unroll
     for (int kf = 0; kf < NKF; ++kf) sA[kf] = f32x16{};
@@ -1051,7 +729,7 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
 
 #define PM_ITER(SC, MBC, SN, MBN)                                                                          \
     {                                                                                                      \
-        issue_tiles(j + 2, j & 1, j + 1, (j + 1) & 1);                                                     \
+        issue_tiles(j + 2, (j - j0) & 1, j + 1, (j - j0 + 1) & 1);                                         \
         if (__builtin_expect((j + 1) * BKV - 1 > lo, 0)) {                                                 \
             __asm__ volatile("");                                                                          \
             _Pragma("unroll") for (int kf = 0; kf < NKF; ++kf)                                             \
@@ -1061,13 +739,13 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
                 }                                                                                          \
         }                                                                                                  \
         /* stage 1: first half of tile j+1's scores || row max of tile j */                               \
-        MBN = j != 0 ? m_i : 0.f;                                                                          \
+        MBN = (SPLIT ? m_i > -INFINITY : j != j0) ? m_i : 0.f;                                             \
         {                                                                                                  \
             f32x16 z_;                                                                                     \
             _Pragma("unroll") for (int e = 0; e < 16; ++e) z_[e] = -MBN;                                   \
             _Pragma("unroll") for (int kf = 0; kf < NKF; ++kf) SN[kf] = z_;                                \
         }                                                                                                  \
-        PM_QK(SN, (j + 1) & 1, 0)                                                                          \
+        PM_QK(SN, (j - j0 + 1) & 1, 0)                                                                     \
         float mx = -INFINITY;                                                                              \
         _Pragma("unroll") for (int kf = 0; kf < NKF; ++kf)                                                 \
             _Pragma("unroll") for (int e = 0; e < 16; ++e) mx = fmaxf(mx, SC[kf][e]);                      \
@@ -1075,34 +753,36 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
             const auto a_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false); \
             mx = fmaxf(__uint_as_float(a_[0]), __uint_as_float(a_[1]));                                    \
         }                                                                                                  \
-        const float delta_ = m_i - MBC;                                                                    \
+        const bool fresh_ = SPLIT ? m_i == -INFINITY : j == j0;                                            \
+        const float delta_ = (SPLIT && fresh_) ? 0.f : m_i - MBC;                                          \
         const float rel_ = mx - delta_;                                                                    \
-        const float shift_ = (j == 0 || rel_ > kSlack) ? rel_ : 0.f;                                       \
+        const float shift_ = (SPLIT ? (fresh_ ? rel_ > -INFINITY : rel_ > kSlack)                          \
+                                    : (fresh_ || rel_ > kSlack)) ? rel_ : 0.f;                             \
         const float sub_ = delta_ + shift_;                                                                \
         /* stage 2 (rare): re-reference tile j's scores, rescale O and l where the reference moved */     \
         if (__builtin_expect(__any(sub_ != 0.f), 0)) {                                                     \
             __asm__ volatile("");                                                                          \
-            const float alpha = j == 0 ? 1.f : fast_exp2(-shift_);                                         \
-            m_i += shift_;                                                                                 \
+            const float alpha = fresh_ ? 1.f : fast_exp2(-shift_);                                         \
+            m_i = (SPLIT && fresh_ ? 0.f : m_i) + shift_;                                                  \
             l_i *= alpha;                                                                                  \
             _Pragma("unroll") for (int db = 0; db < DB; ++db) oacc[db] *= alpha;                           \
             _Pragma("unroll") for (int kf = 0; kf < NKF; ++kf) SC[kf] -= sub_;                             \
         }                                                                                                  \
         float ls = 0.f;                                                                                    \
         /* stage 3: second half of tile j+1's scores || exponentials of the first half of the keys */     \
-        PM_QK(SN, (j + 1) & 1, KH)                                                                         \
+        PM_QK(SN, (j - j0 + 1) & 1, KH)                                                                    \
         _Pragma("unroll") for (int ks = 0; ks < HS; ++ks) PM_EXP_STEP(SC, ks)                              \
         /* stage 4: P V of the first half || exponentials of the second half */                            \
-        _Pragma("unroll") for (int ks = 0; ks < HS; ++ks) PM_PV_STEP(j & 1, ks)                            \
+        _Pragma("unroll") for (int ks = 0; ks < HS; ++ks) PM_PV_STEP((j - j0) & 1, ks)                     \
         _Pragma("unroll") for (int ks = HS; ks < NKS; ++ks) PM_EXP_STEP(SC, ks)                            \
         /* stage 5: P V of the second half */                                                              \
-        _Pragma("unroll") for (int ks = HS; ks < NKS; ++ks) PM_PV_STEP(j & 1, ks)                          \
+        _Pragma("unroll") for (int ks = HS; ks < NKS; ++ks) PM_PV_STEP((j - j0) & 1, ks)                   \
         l_i += ls;                                                                                         \
         __syncthreads();                                                                                   \
     }
-    for (int j = 0; j < nkt; j += 2) {
+    for (int j = j0; j < j1; j += 2) {
         PM_ITER(sA, mbA, sB, mbB)
-        if (j + 1 >= nkt) break;
+        if (j + 1 >= j1) break;
         {
             const int j_ = j;
             {
@@ -1122,6 +802,24 @@ __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
     {
         const auto a_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_i), __float_as_uint(l_i), false, false);
         lsum = __uint_as_float(a_[0]) + __uint_as_float(a_[1]);
+    }
+    if constexpr (SPLIT) {
+        if (qi < S) {
+            float* rec = record(qi);
+            if (lh == 0) {
+                rec[0] = m_i;
+                rec[1] = lsum;
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x16& v = oacc[db];
+                    *reinterpret_cast<f32x4*>(rec + 4 + 32 * db + 8 * i + 4 * lh) =
+                        f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+                }
+        }
+        return;
     }
     const float inv = 1.f / lsum;
     if (qi < S) {
@@ -1968,6 +1666,12 @@ static hipError_t prefill_rope_sel(const void* qkv, const int64_t* pos, const Ro
     return prefill_go<D, HPB, true, false>(qkv, pos, tab, o, kc, vc, ctx, B, S, nh, nkv, st);
 }
 
+// the 32x32 prefill kernel's tile loop (pipelined at d = 128, plain at d = 64) and waves per SIMD
+template <int D>
+constexpr bool m32_pipe() { return D != 64; }
+template <int D, int HPB>
+constexpr int m32_occ() { return HPB == 1 ? 1 : (m32_pipe<D>() ? 2 : 4); }
+
 // q and k already rotated: the 32x32 matrix-op kernel, HPB heads per workgroup
 template <int D, int HPB>
 static hipError_t m32_go(const void* qkv, const int64_t* pos, void* o, void* kc, void* vc, int64_t ctx, int B,
@@ -1979,11 +1683,11 @@ static hipError_t m32_go(const void* qkv, const int64_t* pos, void* o, void* kc,
     // waves per SIMD (117 registers): in the 1B layer 0.108 ms pipelined at two, 0.095 at three (150
     // registers), 0.090 plain at four. 32-key tiles measured slower: 4% at d = 128 (pipelined, two waves
     // per SIMD, or plain at three), 2% at d = 64.
-    constexpr bool PIPE = D != 64;
-    constexpr int OCC = HPB == 2 ? (PIPE ? 2 : 4) : 1;
+    constexpr bool PIPE = m32_pipe<D>();
+    constexpr int OCC = m32_occ<D, HPB>();
     hipLaunchKernelGGL((attn_prefill_m32_kernel<D, HPB, OCC, PIPE>), dim3(blocks), dim3(128 * HPB), 0, st,
                        static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
-                       static_cast<bf16_t*>(vc), ctx, B, S_max, nh, nkv, scale_log2, cu, total);
+                       static_cast<bf16_t*>(vc), ctx, B, S_max, nh, nkv, scale_log2, cu, total, 1, nullptr);
     return hipGetLastError();
 }
 
@@ -2254,12 +1958,14 @@ static hipError_t chunk_go(const void* qkv, const int64_t* pos, void* o, void* k
     const int nqb = (S + 63) / 64;
     const unsigned blocks = static_cast<unsigned>(nqb) * B * nkv * (g / HPB) * nsplit;
     const float scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
+    constexpr bool PIPE = m32_pipe<D>();
+    constexpr int OCC = m32_occ<D, HPB>();
     if (nsplit > 1)
-        hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, true, true>), dim3(blocks), dim3(128 * HPB), 0, st,
-                           static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
+        hipLaunchKernelGGL((attn_prefill_m32_kernel<D, HPB, OCC, PIPE, true, true>), dim3(blocks), dim3(128 * HPB), 0,
+                           st, static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
                            static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2, nullptr, 0, nsplit, part);
     else
-        hipLaunchKernelGGL((attn_prefill_direct_kernel<D, HPB, true>), dim3(blocks), dim3(128 * HPB), 0, st,
+        hipLaunchKernelGGL((attn_prefill_m32_kernel<D, HPB, OCC, PIPE, true>), dim3(blocks), dim3(128 * HPB), 0, st,
                            static_cast<const bf16_t*>(qkv), pos, static_cast<bf16_t*>(o), static_cast<bf16_t*>(kc),
                            static_cast<bf16_t*>(vc), ctx, B, S, nh, nkv, scale_log2, nullptr, 0, 1, nullptr);
     hipError_t e = hipGetLastError();
