@@ -417,8 +417,8 @@ __device__ __forceinline__ int vt_phys(int r, int c) {
 // v_mfma_f32_32x32x16_bf16, which issues at full rate from one wave (the 16x16x32 form needs two
 // waves per SIMD to keep the matrix core fed).
 //  * K and V tiles (64 keys) go global -> LDS by buffer loads straight into LDS (no register staging),
-//    both row-major [key][dim] with 16-byte chunks XOR-swizzled by row; double-buffered, V one tile
-//    behind K; every wave of the group reads them.
+//    both row-major [key][dim] with 16-byte chunks XOR-swizzled by row; double-buffered (in the
+//    pipelined loop V runs one tile behind K); every wave of the group reads them.
 //  * S^T = K Q^T per 32-key block: A = 32 keys x 16 dims of K (one 16-byte LDS read), B = the wave's
 //    resident Q^T (16 dims x 32 queries). The accumulator gives lane l query l % 32 and keys
 //    8i + 4(l/32) + r in register 4i + r, so a query's scores sit in two lanes (l, l ^ 32): its row
@@ -431,13 +431,14 @@ __device__ __forceinline__ int vt_phys(int r, int c) {
 //    hand every lane 4 consecutive keys of one dim).
 //  * Online softmax in log2 units (q pre-scaled by log2(e)/sqrt(d)); score accumulators start at minus
 //    the running reference max, which moves only when a tile max exceeds it by more than kSlack (rare:
-//    corrected under a wave-uniform branch). Only the tiles crossing the diagonal are masked.
+//    corrected under a wave-uniform branch). Only tiles past the block's smallest visibility limit
+//    (the diagonal, over the call's own tokens) are masked.
 //  * OCC waves per SIMD (the register budget is 512 / OCC). With PIPE a wave overlaps tile j+1's scores
 //    with tile j's softmax (two score sets); without, it runs scores, softmax and P V of one tile in turn
 //    (one set, fewer registers), leaving the overlap to the other waves of its SIMD.
 //  * CACHED: chunked prefill over a cache prefix (keys are cache slots, query i sees slots
-//    0 .. position_ids[b, i], clamped to the cache); SPLIT: the block's key tiles shared out over nsplit workgroups,
-//    each writing a (max, sum, unnormalised o) record per query for the combine kernel.
+//    0 .. position_ids[b, i], clamped to the cache); SPLIT: the block's key tiles shared out over nsplit
+//    workgroups, each writing a (max, sum, unnormalised o) record per query for the combine kernel.
 template <int D, int HPB, int OCC, bool PIPE, bool CACHED = false, bool SPLIT = false>
 __global__ __launch_bounds__(128 * HPB, OCC) void attn_prefill_m32_kernel(
     const bf16_t* __restrict__ qkv, const int64_t* __restrict__ pos, bf16_t* __restrict__ out, bf16_t* __restrict__ kc,
