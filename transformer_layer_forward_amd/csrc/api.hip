@@ -551,10 +551,12 @@ ll_status swiglu_mlp(const void* x, const void* w_gate_up, const void* w_down, c
     void* gws = ws + round_up(static_cast<size_t>(M * intermediate) * elem_size(dtype));
     const size_t gbytes = workspace_bytes - round_up(static_cast<size_t>(M * intermediate) * elem_size(dtype));
     hipStream_t st = as_stream(stream);
-    hipError_t e = launch_gemm(dtype, EPI_SILU, x, w_gate_up, act, nullptr, M, intermediate, hidden, gws, gbytes, st);
+    const bool blk = gemm_act_blocked(dtype, M, intermediate, hidden);
+    hipError_t e = launch_gemm(dtype, EPI_SILU, x, w_gate_up, act, nullptr, M, intermediate, hidden, gws, gbytes, st,
+                               nullptr, blk);
     if (e != hipSuccess) return hip_fail(e, "gate_up launch");
     e = launch_gemm(dtype, residual ? EPI_RESIDUAL : EPI_STORE, act, w_down, out, residual, M, hidden, intermediate,
-                    gws, gbytes, st);
+                    gws, gbytes, st, nullptr, blk);
     if (e != hipSuccess) return hip_fail(e, "down launch");
     return LL_OK;
 }
@@ -724,12 +726,13 @@ static ll_status layer_forward_impl(const ll_layer_cfg* cfg, const ll_layer_weig
     e = launch_rmsnorm(dt, h, w->g_mlp, xn, s.M, s.H, eps, stream_h);
     if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
     LL_CHECK_HIP(mark(), "hipEventRecord");
-    // 6. gate_up + silu * up
-    e = launch_gemm(dt, EPI_SILU, xn, w->w_gate_up, act, nullptr, s.M, s.I, s.H, gws, gbytes, stream_h);
+    // 6. gate_up + silu * up (written K-blocked for the down projection where both take whole tiles)
+    const bool blk = gemm_act_blocked(dt, s.M, s.I, s.H);
+    e = launch_gemm(dt, EPI_SILU, xn, w->w_gate_up, act, nullptr, s.M, s.I, s.H, gws, gbytes, stream_h, nullptr, blk);
     if (e != hipSuccess) return hip_fail(e, "gate_up launch");
     LL_CHECK_HIP(mark(), "hipEventRecord");
     // 7. down + residual
-    e = launch_gemm(dt, EPI_RESIDUAL, act, w->w_down, out, h, s.M, s.H, s.I, gws, gbytes, stream_h);
+    e = launch_gemm(dt, EPI_RESIDUAL, act, w->w_down, out, h, s.M, s.H, s.I, gws, gbytes, stream_h, nullptr, blk);
     if (e != hipSuccess) return hip_fail(e, "down launch");
     LL_CHECK_HIP(mark(), "hipEventRecord");
     return LL_OK;

@@ -100,8 +100,12 @@ hipError_t launch_rope_apply(int dtype, void* qkv, const int64_t* pos, RopeTab t
                              int d, int interleaved, hipStream_t st);
 // C[M, ldc] (epi) = X[M, K] . W^T; W has N rows (EPI_SILU: 2*inter rows, N = inter output columns).
 size_t gemm_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K, int epi);
+// act_blocked: EPI_SILU writes C K-blocked ([N / 64][M][64]) and EPI_STORE / EPI_RESIDUAL read X K-blocked
+// ([K / 64][M][64]); only where gemm_act_blocked(dtype, M, inter, hidden) holds for the gate_up/down pair.
 hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C, const void* R, int64_t M,
-                       int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t st, const RopeEpi* re = nullptr);
+                       int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t st, const RopeEpi* re = nullptr,
+                       bool act_blocked = false);
+bool gemm_act_blocked(int dtype, int64_t M, int64_t inter, int64_t hidden);
 // whether EPI_ROPE can be fused for this projection (else the caller rotates with launch_rope_apply)
 bool gemm_rope_fusable(int dtype, int64_t M, int d);
 // whether a fused-RoPE projection of this shape ends in the partial-sum reduce that can also append the

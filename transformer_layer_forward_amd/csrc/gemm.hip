@@ -336,7 +336,7 @@ __device__ __forceinline__ int mf_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); 
 // TN = 128: the same kernel on a 256 x 128 tile (each wave 128 x 64: 4 x 2 accumulators, 12 loads per
 // wave per stage, 96 KiB of LDS) for shapes with few 256 x 256 tiles; no fused RoPE (a wave's 64
 // columns hold half a head), so RoPE goes through the split partials and the reduce.
-template <int EPI, int RD = 0, bool SPLIT = false, int TN = MF_N>
+template <int EPI, int RD = 0, bool SPLIT = false, int TN = MF_N, bool XBLK = false>
 __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, const bf16_t* __restrict__ R,
     int M, int N, int K, int tiles_m, int tiles_n, const int64_t* __restrict__ rpos, const float2* __restrict__ rcs,
@@ -344,6 +344,8 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     static_assert(EPI != EPI_ROPE || RD == 64 || RD == 128, "fused RoPE for head sizes 64 and 128");
     static_assert(!SPLIT || EPI == EPI_STORE || EPI == EPI_SILU, "split partials: plain or gate/up layout");
     static_assert((TN == 256 || TN == 128) && (TN == 256 || EPI != EPI_ROPE), "tile widths 256 and 128");
+    static_assert(!XBLK || (!SPLIT && TN == MF_N && (EPI == EPI_STORE || EPI == EPI_RESIDUAL)),
+                  "K-blocked X: whole-K 256-wide tiles with a plain or residual epilogue");
     constexpr int FA = TN / 64;                  // 32-row weight fragments per wave
     constexpr int STAGE = (MF_M + TN) * MF_K;    // elements per LDS stage
     constexpr int LPW = 8 + TN / 32;             // direct loads per wave per stage
@@ -384,8 +386,10 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
     // reads at once, lgkmcnt(0), where the buffer form lets it wait for just the oldest ones.)
     const int rsub = 8 * wave + (lane >> 3);
     const int cj = (lane & 7) ^ mf_swz(rsub);
-    const __amdgpu_buffer_rsrc_t rx =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(X + static_cast<int64_t>(m0) * K), (short)0, -1, 0x00020000);
+    // X row-major [M][K], or (XBLK) K-blocked [K / 64][M][64]: a stage's X slice is then 256 rows of 128
+    // contiguous bytes, where row-major rows lie K * 2 bytes apart
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(X + static_cast<int64_t>(m0) * (XBLK ? MF_K : K)), (short)0, -1, 0x00020000);
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(W + static_cast<int64_t>(n0) * K), (short)0, -1, 0x00020000);
     // sized for the widest tile: a lambda capturing an array whose size depends on a template
@@ -403,12 +407,15 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
         } else {
             row = min(n0 + r, N - 1) - n0;
         }
-        voff[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>(cj) * 16u;
+        const int ld = XBLK && j < 8 ? MF_K : K;
+        voff[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(ld) * 2u + static_cast<uint32_t>(cj) * 16u;
     }
     auto issue1 = [&](int slot, int k0, int j) {
+        const uint32_t kofs = XBLK && j < 8 ? static_cast<uint32_t>(k0 / MF_K) * static_cast<uint32_t>(M) * (MF_K * 2u)
+                                            : static_cast<uint32_t>(k0) * 2u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             j < 8 ? rx : rw, (__attribute__((address_space(3))) void*)(smem + slot * STAGE + (4 * j + wave) * 8 * MF_K),
-            16, voff[j], k0 * 2, 0, 0);
+            16, voff[j], kofs, 0, 0);
     };
     // operand fragment offsets within a stage (A: weight rows, B: tokens), one per 32-row block; k16
     // quarter q of a fragment sits at chunk (2q + lh) ^ swizzle = chunk(0) ^ 2q, i.e. offset(0) ^ 16q
@@ -712,6 +719,7 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_kernel(
 constexpr int MFP_EXTRA = 4 * 64 * (MF_N / 4) * 2;   // per wave: 64 rows x 64 output columns, bf16
 constexpr int mfp_lds_bytes() { return MF_NSLOT * (MF_M + MF_N) * MF_K * 2 + MFP_EXTRA; }   // 160 KiB
 
+template <bool CBLK>
 __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_silu_persist_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, int N, int K, int tiles_m,
     int tiles_n) {
@@ -877,7 +885,11 @@ __global__ __launch_bounds__(MF_THREADS, 1) void gemm_bf16_mfma32_silu_persist_k
             for (int e8 = 0; e8 < 64 * GPR / 64; ++e8) {
                 const int e = e8 * 64 + lane, m = e / GPR, gq = e % GPR;
                 const uint4 v = *reinterpret_cast<const uint4*>(lds_at(m, 8 * gq));
-                *reinterpret_cast<uint4*>(C + static_cast<int64_t>(mw + 64 * ps + m) * N + nw + 8 * gq) = v;
+                const int row = mw + 64 * ps + m, col = nw + 8 * gq;
+                // row-major [M][N], or (CBLK) K-blocked for the next projection: [N / 64][M][64]
+                const int64_t at = CBLK ? (static_cast<int64_t>(col >> 6) * (tiles_m * MF_M) + row) * 64 + (col & 63)
+                                        : static_cast<int64_t>(row) * N + col;
+                *reinterpret_cast<uint4*>(C + at) = v;
             }
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_sched_barrier(0);
@@ -1527,14 +1539,14 @@ static bool allow_lds(Fn* kernel, int bytes) {
                                bytes) == hipSuccess;
 }
 
-template <int EPI, int RD = 0, int TN = MF_N>
+template <int EPI, int RD = 0, int TN = MF_N, bool XBLK = false>
 static hipError_t mfma32_launch(const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N,
                                 int64_t K, hipStream_t st, const RopeEpi* re = nullptr) {
-    static const bool attr = allow_lds(&gemm_bf16_mfma32_kernel<EPI, RD, false, TN>, mf_lds_bytes<TN>());
+    static const bool attr = allow_lds(&gemm_bf16_mfma32_kernel<EPI, RD, false, TN, XBLK>, mf_lds_bytes<TN>());
     if (!attr) return hipErrorInvalidConfiguration;
     const int ncols = EPI == EPI_SILU ? TN / 2 : TN;
     const int tm = static_cast<int>((M + MF_M - 1) / MF_M), tn = static_cast<int>((N + ncols - 1) / ncols);
-    hipLaunchKernelGGL((gemm_bf16_mfma32_kernel<EPI, RD, false, TN>), dim3(tm * tn), dim3(MF_THREADS),
+    hipLaunchKernelGGL((gemm_bf16_mfma32_kernel<EPI, RD, false, TN, XBLK>), dim3(tm * tn), dim3(MF_THREADS),
                        mf_lds_bytes<TN>(), st, static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(W),
                        static_cast<bf16_t*>(C), static_cast<const bf16_t*>(R), static_cast<int>(M), static_cast<int>(N),
                        static_cast<int>(K), tm, tn, re ? re->pos : nullptr, re ? re->tab.cs : nullptr,
@@ -1562,10 +1574,11 @@ static bool mfp_usable(int64_t M, int64_t N, int64_t K) {
     return T % 8 == 0 && T >= 2 * static_cast<int64_t>(mfp_workgroups());
 }
 
+template <bool CBLK>
 static hipError_t mfp_launch(const void* X, const void* W, void* C, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-    static const bool attr = allow_lds(&gemm_bf16_mfma32_silu_persist_kernel, mfp_lds_bytes());
+    static const bool attr = allow_lds(&gemm_bf16_mfma32_silu_persist_kernel<CBLK>, mfp_lds_bytes());
     if (!attr) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(gemm_bf16_mfma32_silu_persist_kernel, dim3(static_cast<unsigned>(mfp_workgroups())),
+    hipLaunchKernelGGL(gemm_bf16_mfma32_silu_persist_kernel<CBLK>, dim3(static_cast<unsigned>(mfp_workgroups())),
                        dim3(MF_THREADS), mfp_lds_bytes(), st, static_cast<const bf16_t*>(X),
                        static_cast<const bf16_t*>(W), static_cast<bf16_t*>(C), static_cast<int>(N),
                        static_cast<int>(K), static_cast<int>(M / MF_M), static_cast<int>(N / (MF_N / 2)));
@@ -1664,9 +1677,28 @@ bool gemm_rope_fusable(int dtype, int64_t M, int d) {
     return d == 32 || d == 64 || d == 128;
 }
 
+// whether the gate_up output can be handed to the down projection K-blocked ([inter / 64][M][64]): both
+// projections run whole 256 x 256 tiles over all of K (gate_up the persistent kernel), and the blocked
+// offsets fit the down kernel's 32-bit byte offsets
+bool gemm_act_blocked(int dtype, int64_t M, int64_t inter, int64_t hidden) {
+    if (dtype != LL_BF16 || M == 0 || use_skinny(M) || inter % MF_K != 0) return false;
+    if (!mf_usable(EPI_SILU, inter, hidden, nullptr) || !mfp_usable(M, inter, hidden)) return false;
+    const MfPlan pu = mf_plan(EPI_SILU, M, inter, hidden);
+    if (pu.partial || pu.tn != MF_N) return false;
+    if (!mf_usable(EPI_RESIDUAL, hidden, inter, nullptr)) return false;
+    const MfPlan pd = mf_plan(EPI_RESIDUAL, M, hidden, inter);
+    return !pd.partial && pd.tn == MF_N && M * inter * 2 < (int64_t(1) << 32);
+}
+
 hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C, const void* R, int64_t M, int64_t N,
-                       int64_t K, void* ws, size_t ws_bytes, hipStream_t st, const RopeEpi* re) {
+                       int64_t K, void* ws, size_t ws_bytes, hipStream_t st, const RopeEpi* re, bool act_blocked) {
     if (M == 0 || N == 0) return hipSuccess;
+    if (act_blocked) {   // the caller checked gemm_act_blocked for this pair of projections
+        if (epi == EPI_SILU) return mfp_launch<true>(X, W, C, M, N, K, st);
+        if (epi == EPI_RESIDUAL) return mfma32_launch<EPI_RESIDUAL, 0, MF_N, true>(X, W, C, R, M, N, K, st);
+        if (epi == EPI_STORE) return mfma32_launch<EPI_STORE, 0, MF_N, true>(X, W, C, R, M, N, K, st);
+        return hipErrorInvalidValue;
+    }
     if (epi == EPI_ROPE && (!re || !gemm_rope_fusable(dtype, M, re->d))) return hipErrorInvalidValue;
     if (dtype == LL_F32) {
         switch (epi) {
@@ -1713,7 +1745,7 @@ hipError_t launch_gemm(int dtype, int epi, const void* X, const void* W, void* C
                 if (re->d == 128) return mfma32_launch<EPI_ROPE, 128>(X, W, C, R, M, N, K, st, re);
                 return mfma32_launch<EPI_ROPE, 64>(X, W, C, R, M, N, K, st, re);
             default:
-                if (mfp_usable(M, N, K)) return mfp_launch(X, W, C, M, N, K, st);
+                if (mfp_usable(M, N, K)) return mfp_launch<false>(X, W, C, M, N, K, st);
                 return mfma32_launch<EPI_SILU>(X, W, C, R, M, N, K, st);
         }
     }
