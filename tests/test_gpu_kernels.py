@@ -134,14 +134,17 @@ def test_swiglu_mlp_wide_tiles_sampled_rows(with_residual):
         assert ref.max_rel_err(got, want) <= tol(dtype)
 
 
-@pytest.mark.parametrize("M,H,I", [(2300, 4096, 14208), (2560, 2048, 8192), (4096, 128, 4096), (4096, 192, 4096)])
+@pytest.mark.parametrize("M,H,I", [(2300, 4096, 14208), (2560, 2048, 8192), (4096, 128, 4096), (4096, 192, 4096),
+                                   (4096, 4096, 4096)])
 def test_swiglu_mlp_many_tiles_sampled_rows(M, H, I):
     """Shapes with several 256 x 256 tiles per compute unit and a ragged last token tile.
     M = 2300, I = 14208: gate_up has 9 x 111 = 999 tiles (not a multiple of 8: the plain tile order instead of
     the per-XCD one); M = 2560, H = 2048, I = 8192: gate_up 10 x 64 = 640 tiles (per-XCD order; the persistent
     kernel, 2 or 3 tiles per workgroup), down 10 x 8 = 80 tiles (K split); M = 4096, H = 128 / 192: the
-    persistent gate_up kernel on 512 tiles whose K walk is two / three stages. 24 sampled rows (first, last,
-    the edges of the last token tile, seeded), with the residual."""
+    persistent gate_up kernel on 512 tiles whose K walk is two / three stages; M = H = I = 4096: both
+    projections on whole 256 x 256 tiles (gate_up 512 on the persistent kernel, down 256), so gate_up hands
+    its output to down K-blocked. 24 sampled rows (first, last, the edges of the last token tile, seeded),
+    with the residual."""
     require_gpu()
     dtype = "bf16"
     x = normal(6, 150, (M, H), dtype)
