@@ -647,8 +647,8 @@ def main():
         counter_summary(args.counter_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (each MI355X runs the whole "
-              "layer on its own sequences; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (data parallel, each MI355X "
+              "would run the whole layer on its own sequences). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
