@@ -171,6 +171,7 @@ PREFILL = [
     ("bf16", 1, 100, 16, 2, 128),
     ("bf16", 3, 1, 4, 1, 128),
     ("bf16", 1, 257, 6, 2, 64),      # g = 3 (one head per block)
+    ("bf16", 1, 150, 6, 2, 128),     # g = 3 at d = 128
     ("bf16", 1, 700, 8, 2, 128),     # 11 key tiles, ragged last tile
     ("bf16", 1, 50, 4, 2, 96),       # generic kernel
     ("f32", 1, 32, 4, 2, 16),
@@ -310,6 +311,7 @@ CHUNK = [
     ("bf16", 2, 1, 8, 2, 128, 600, (500, 37), "up"),          # one-token chunks
     ("bf16", 1, 200, 16, 2, 128, 1300, (1000,), "up"),        # long prefix, g = 8
     ("bf16", 1, 257, 6, 2, 64, 400, (33,), "up"),             # g = 3 (one head per block)
+    ("bf16", 1, 90, 6, 2, 128, 300, (120,), "up"),            # g = 3 at d = 128
     ("bf16", 1, 100, 8, 2, 128, 200, (60,), "down"),          # positions in reverse order
     ("bf16", 1, 64, 8, 2, 128, 2048, (500,), "up"),           # keys split over 16 workgroups, some of
     ("bf16", 1, 64, 8, 2, 128, 2048, (500,), "down"),         # them wholly masked for early queries
